@@ -1,0 +1,251 @@
+"""Benchmark: paged decode on one MI355X, GPT-style 64-sequence fp16 batch.
+
+A step is one decode iteration of the whole path over one batch:
+  host   pkv_prepare_decode (C++): append one token to each of the 64
+         sequences, take copy-on-write pairs, build block tables, lengths and
+         the split-K plan into a pinned staging buffer; one async upload;
+  device copy_blocks (if any pairs), write_kv of the 64 new tokens' K/V,
+         the paged-decode partition kernel, the split-K reduce kernel.
+Inputs (pools, q, the new tokens' K/V) are resident in HBM before timing.
+``--replicas`` independent copies of the batch (own pools, own allocators)
+are stepped in rotation so that every step reads K/V that the previous
+steps have pushed out of L2 and the 256 MiB Infinity Cache.
+
+Reported (one JSON line):
+  value        K/V bytes the steps attended / wall time of the K steps (GB/s);
+  roofline     the partition kernel alone, timed with HIP events on its
+               stream: algorithmic K/V bytes per launch / mean duration,
+               against the 8 TB/s HBM peak; ``traffic`` from rocprofv3
+               FETCH_SIZE + WRITE_SIZE counters when a counter summary for the
+               current kernel source is committed under profiles/;
+  cpu_baseline the fp64 CPU oracle on a bounded sample of the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "paged-decode achieved HBM GB/s (% of peak) + decode tokens/s, 64-seq fp16 batch"
+KERNEL_SOURCES = ("paged_kv_cache_257_amd/csrc/kernels/paged_decode.hip",
+                  "paged_kv_cache_257_amd/csrc/kernels/device_common.h")
+COUNTER_SUMMARY = "profiles/paged_decode_gpt_f16_counters.txt"
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """Per-launch HBM bytes from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, COUNTER_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="gpt_f16")
+    ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = library default)")
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    return ap.parse_args(argv)
+
+
+def calib_copy():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": n, "launches": 3}))
+
+
+def cpu_baseline(cfg, sh, vals, stride, budget_s):
+    """The fp64 oracle on a bounded sample of the same batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle.runs import DecodeRun
+
+    cores = os.cpu_count() or 1
+    with threadpool_limits(limits=cores):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        run = DecodeRun(cfg, sh.lens, sh.num_blocks, sh.free_order, stride)
+        run.write_context(vals["k"], vals["v"])
+        order = np.random.default_rng(cfg.seed + 7).permutation(len(sh.lens))
+        done, tokens, t0 = 0, 0, time.perf_counter()
+        for i in order:
+            run.attend(int(i), vals["q"][int(i)])
+            done += 1
+            tokens += int(sh.lens[int(i)])
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+    kv_bytes = tokens * 2 * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {len(sh.lens)} sequences ({tokens} context tokens) of the same batch, "
+                      f"fp64 numpy attention, {dt:.1f} s",
+            "decode_tokens_per_s": round(done / dt, 3)}
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path is not sharded across GPUs in this build)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    if args.calib_copy:
+        calib_copy()
+        return 0
+
+    from paged_kv_cache_257_amd import Pool
+    from paged_kv_cache_257_amd.step import DecodeIteration
+    from workloads import config_by_name, draw_decode_values, draw_normal_storage
+    from workloads.configs import draw_decode_shapes
+
+    cfg = config_by_name(args.workload)
+    sh = draw_decode_shapes(cfg)
+    vals = draw_decode_values(cfg, sh.lens)
+    B, Hq, H, d, dt = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.dtype
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    total = args.warmup + args.steps
+    grow = -(-total // args.replicas)  # tokens each replica appends
+    stride = -(-(int(sh.lens.max()) + grow) // 16)
+    # each replica's pool holds the batch plus its growth
+    grow_blocks = B * (-(-grow // 16) + 1)
+    nb = sh.num_blocks + grow_blocks
+    order = np.concatenate([sh.free_order, np.arange(sh.num_blocks, nb, dtype=np.int32)])
+
+    def dev_tensor(bits):
+        a = np.ascontiguousarray(bits)
+        t = torch.from_numpy(a.view(np.int16) if dt == "bf16" else a)
+        return (t.view(torch.bfloat16) if dt == "bf16" else t).to("cuda")
+
+    k_ctx, v_ctx, q_dev = dev_tensor(vals["k"]), dev_tensor(vals["v"]), dev_tensor(vals["q"])
+    new_k = dev_tensor(draw_normal_storage((cfg.seed, 50), (total, B, H, d), dt))
+    new_v = dev_tensor(draw_normal_storage((cfg.seed, 51), (total, B, H, d), dt))
+    reps = []
+    for r in range(args.replicas):
+        kc = torch.zeros((nb, H, 16, d), dtype=tdt, device="cuda")
+        vc = torch.zeros_like(kc)
+        pool = Pool(nb, H, d, dt, stride, 16, order, kc, vc)
+        slots = np.concatenate([pool.alloc(int(L))[1] for L in sh.lens])
+        pool.write_kv(k_ctx, v_ctx, torch.from_numpy(slots).cuda())
+        it = DecodeIteration(pool, B, stride, Hq, args.partition)
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+        reps.append((pool, it, out, kc, vc))
+    del k_ctx, v_ctx
+    torch.cuda.synchronize()
+    seqs = list(range(B))
+    per_tok = 2 * H * d * cfg.elem_bytes
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(total)]
+    step_bytes, infos = [], []
+
+    def step(s):
+        pool, it, out, _, _ = reps[s % args.replicas]
+        meta = it.prepare(seqs)
+        it.launch(meta, q_dev, out, new_k[s], new_v[s], cfg.scale, events=ev[s])
+        step_bytes.append(int(meta["host_lens"].astype(np.int64).sum()) * per_tok)
+        infos.append(meta["info"])
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, total):
+        step(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    timed = range(args.warmup, total)
+    kbytes = sum(step_bytes[s] for s in timed)
+    kern_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in timed]
+    mean_kern_s = float(np.mean(kern_ms)) / 1e3
+    mean_bytes = kbytes / args.steps
+    achieved = mean_bytes / mean_kern_s / 1e9
+    value = kbytes / wall / 1e9
+    info = infos[-1]
+    traffic = committed_traffic()
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": H,
+                   "head_dim": d, "block_size": 16, "mean_context": round(float(sh.lens.mean()), 1),
+                   "max_context": int(sh.lens.max()), "partition_tokens": info.partition_tokens,
+                   "work_items": info.n_work, "replicas": args.replicas,
+                   "accumulate": "f32", "output": "f32"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_tokens_per_s": round(B * args.steps / wall, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "paged_decode_kernel (partition kernel)",
+                     "kernel_ms_mean": round(float(np.mean(kern_ms)), 5),
+                     "kernel_ms_p10": round(float(np.percentile(kern_ms, 10)), 5),
+                     "kernel_ms_p90": round(float(np.percentile(kern_ms, 90)), 5),
+                     "algorithmic_bytes_per_launch": int(mean_bytes),
+                     "kernel_source_sha": kernel_source_sha()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, sh, vals, -(-int(sh.lens.max()) // 16), args.cpu_seconds)
+    for pool, *_ in reps:
+        pool.close()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,299 @@
+/*
+ * pkv.h -- C ABI of libpkv: a paged KV cache and PagedAttention decode for
+ * AMD MI355X (gfx950).
+ *
+ * Sources the operations follow (cited by page title and section):
+ *   [lesson]   "PagedAttention e continuous batching" (llmdeepdive lesson 7.8),
+ *              section "01 · Conceito", paragraphs 1-9;
+ *   [preview]  "04 — Hacia PagedAttention (vista previa)" (lynx-cortex,
+ *              phase 22 theory), section "La idea de PagedAttention", steps 1-5
+ *              and "Propiedades"; "Lo que deberías llevarte"; "Lo que la
+ *              Fase 22 construye";
+ *   [tutorial] "Paged Attention em Large Language Models LLMs" (acheiumaia),
+ *              "Configurando as Constantes".
+ *
+ * Two halves:
+ *   host    -- the block allocator.  A pool of fixed-size blocks with a free
+ *              list, per-block reference counts, per-sequence block tables
+ *              and copy-on-write.  Pure CPU code, no GPU calls.
+ *   device  -- HIP kernels that write new K/V rows at their slots, copy whole
+ *              blocks for copy-on-write, and run decode attention through the
+ *              block tables.  Asynchronous on the caller's stream.
+ *
+ * Conventions
+ *   - Every function returns a pkv_status.  On any error nothing changes
+ *     (admission is refused early with a clear error, [lesson] paragraph 8);
+ *     pkv_last_error() gives a message for the calling thread.
+ *   - The caller owns all device memory: the K/V pools, q, out, tables,
+ *     context lengths, plans and workspaces.  The library never allocates
+ *     device memory and never synchronises a stream.
+ *   - A pool object is not thread-safe; use one thread per pool.
+ *   - Slots: slot s of a pool is row s % block_size of block s / block_size.
+ *   - "stream" is a hipStream_t passed as void*; NULL is the null stream.
+ *   - Pool layout in device memory (a reading: the pages only say blocks may
+ *     live anywhere): K and V are two arrays shaped
+ *     [num_blocks][num_kv_heads][block_size][head_dim] of the pool dtype, so
+ *     one (block, head) tile is one contiguous block_size*head_dim span.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_E_NO_BLOCKS = 1,   /* not enough free blocks; nothing changed       */
+  PKV_E_BAD_SEQ = 2,     /* unknown or already freed sequence id          */
+  PKV_E_BAD_ARG = 3,     /* invalid argument (null, size, geometry, dtype) */
+  PKV_E_TABLE_FULL = 4,  /* a sequence would exceed max_blocks_per_seq    */
+  PKV_E_HIP = 5,         /* a HIP launch failed                           */
+  PKV_E_UNSUPPORTED = 6  /* valid, but not built (head_dim, dtype, ...)   */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/* Pool geometry.  block_size is the tokens per block ([preview] step 1;
+ * 16 in every workload here, and the only size the device kernels take). */
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq; /* block-table capacity per sequence       */
+  int32_t dtype;              /* pkv_dtype of the K/V pools and of q      */
+} pkv_pool_desc;
+
+/* Operational counters ([lesson] paragraph 9). */
+typedef struct {
+  int64_t free_blocks;
+  int64_t used_blocks;
+  int64_t alloc_failures;   /* calls refused for lack of free blocks      */
+  int64_t tail_waste_slots; /* unused rows of last blocks, all sequences  */
+  int64_t shared_blocks;    /* blocks with refcount > 1                   */
+  int64_t cow_copies;       /* copy-on-write block copies queued so far   */
+  int64_t forks;
+  int64_t live_seqs;
+} pkv_stats_t;
+
+typedef struct pkv_pool pkv_pool;
+
+/* Message describing the last error on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Host: pool and allocator
+ * ------------------------------------------------------------------------ */
+
+/* Create a pool.  k_cache / v_cache are device arrays of the layout above
+ * (may both be NULL for allocator-only use; device calls then fail with
+ * PKV_E_BAD_ARG).  free_order (host, num_blocks ids, a permutation; NULL =
+ * 0..num_blocks-1) is the free list's initial content: the first block handed
+ * out is free_order[0].  The free list is a stack: freed blocks are handed
+ * out again most-recent first ([preview] step 4). */
+pkv_status pkv_pool_create(const pkv_pool_desc* desc, void* k_cache, void* v_cache,
+                           const int32_t* free_order, pkv_pool** out);
+pkv_status pkv_pool_destroy(pkv_pool* pool);
+/* Drop every sequence and restore the initial free list (the "reset" of the
+ * cache API in [preview] "Lo que la Fase 22 construye").  Device contents are
+ * left as they are. */
+pkv_status pkv_pool_reset(pkv_pool* pool);
+pkv_status pkv_pool_get_desc(const pkv_pool* pool, pkv_pool_desc* out);
+
+/* New sequence holding n_tokens tokens (n_tokens >= 0).  Writes its id to
+ * *seq and, if slots != NULL, the slot of each token to slots[0..n_tokens).
+ * Needs ceil(n_tokens / block_size) free blocks; ids count up from 0 and are
+ * never reused. */
+pkv_status pkv_seq_alloc(pkv_pool* pool, int32_t n_tokens, int32_t* seq, int64_t* slots);
+
+/* Append n_tokens tokens to a sequence ([preview] step 3): a token goes into
+ * the last block if it has room, otherwise into a newly taken block; nothing
+ * already stored moves.  If the last block is partly filled and shared
+ * (refcount > 1), the first token copies it first ([lesson] paragraph 7):
+ * the appending sequence takes a fresh block, a (src, dst) copy is queued for
+ * pkv_take_cow, and the source loses one reference. */
+pkv_status pkv_seq_append(pkv_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots);
+
+/* Append n_tokens to each of seqs[0..n_seqs) in that order, all or nothing.
+ * slots (may be NULL) receives [n_seqs][n_tokens]. */
+pkv_status pkv_seq_append_batch(pkv_pool* pool, const int32_t* seqs, int32_t n_seqs,
+                                int32_t n_tokens, int64_t* slots);
+
+/* New sequence sharing every block of parent (prefix sharing, parallel
+ * samples; [lesson] paragraph 7, [preview] "Propiedades").  Takes no block:
+ * every block's refcount goes up by one. */
+pkv_status pkv_seq_fork(pkv_pool* pool, int32_t parent, int32_t* child);
+
+/* Release a sequence: each block of its table, front to back, loses one
+ * reference; blocks reaching zero go back on the free list. */
+pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq);
+
+pkv_status pkv_seq_length(const pkv_pool* pool, int32_t seq, int32_t* length);
+/* Copy the sequence's block table to table[0..cap); *n = its length. */
+pkv_status pkv_seq_table(const pkv_pool* pool, int32_t seq, int32_t* table, int32_t cap,
+                         int32_t* n);
+/* Live sequence ids in ascending order. */
+pkv_status pkv_live_seqs(const pkv_pool* pool, int32_t* ids, int32_t cap, int32_t* n);
+/* Free blocks in the order they will be handed out next. */
+pkv_status pkv_free_list(const pkv_pool* pool, int32_t* blocks, int32_t cap, int32_t* n);
+/* Reference count of every block, refcounts[0..num_blocks). */
+pkv_status pkv_refcounts(const pkv_pool* pool, int32_t* refcounts);
+pkv_status pkv_stats(const pkv_pool* pool, pkv_stats_t* out);
+
+/* Take the copy-on-write pairs queued since the last call, pairs[i][0] = src,
+ * pairs[i][1] = dst.  If more than cap are queued, fails with PKV_E_BAD_ARG,
+ * sets *n to the count and takes nothing.  Contract: enqueue pkv_copy_blocks
+ * for these pairs, then pkv_write_kv for the appended tokens, before the next
+ * append or fork; the pairs of one append batch never depend on each other. */
+pkv_status pkv_take_cow(pkv_pool* pool, int32_t* pairs, int32_t cap, int32_t* n);
+
+/* Block tables (row i = table of seqs[i], padded with -1 to table_stride) and
+ * context lengths of a batch, written to host arrays
+ * block_tables[n_seqs][table_stride] and context_lens[n_seqs]. */
+pkv_status pkv_build_batch(const pkv_pool* pool, const int32_t* seqs, int32_t n_seqs,
+                           int32_t* block_tables, int32_t table_stride, int32_t* context_lens);
+
+/* ---------------------------------------------------------------------------
+ * Host: decode plan
+ * ------------------------------------------------------------------------ */
+
+/* Split-K plan of a decode batch.  Each sequence's tokens are cut into
+ * partitions of partition_tokens (a multiple of block_size; 0 picks a size
+ * from the batch).  One work item per (sequence, partition); items are ordered
+ * longest first so that the GPU's in-order dispatch fills the tail with short
+ * ones.  Sequences with more than one partition write partial results that a
+ * second kernel combines.
+ *
+ * plan (host int32, cap >= pkv_decode_plan_ints(...)) receives
+ *   [0, 2*n_work)                     work items (seq index, partition index)
+ *   [2*n_work, 2*n_work + num_seqs)   first partial index of each sequence,
+ *                                     or -1 for single-partition sequences
+ *   [.., + n_reduce)                  indices of multi-partition sequences.
+ * Upload it unchanged and pass the device copy to pkv_paged_decode. */
+typedef struct {
+  int32_t num_seqs;
+  int32_t block_size;
+  int32_t partition_tokens;
+  int32_t n_work;
+  int32_t n_reduce;
+  int32_t n_partials;
+  int32_t plan_ints;
+  int32_t max_context_len;
+} pkv_decode_plan_info;
+
+/* Upper bound of the plan length for these lengths. */
+pkv_status pkv_decode_plan_ints(const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                                int32_t partition_tokens, int32_t* plan_ints);
+pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                           int32_t partition_tokens, int32_t* plan, int32_t cap,
+                           pkv_decode_plan_info* info);
+
+/* Device workspace bytes pkv_paged_decode needs for this plan. */
+size_t pkv_decode_workspace_bytes(const pkv_decode_plan_info* info, int32_t num_q_heads,
+                                  int32_t head_dim);
+
+/* ---------------------------------------------------------------------------
+ * Host: one decode iteration's metadata in one staging buffer
+ * ------------------------------------------------------------------------ */
+
+/* Where pkv_prepare_decode put each array inside the staging buffer (byte
+ * offsets from its start, each 256-byte aligned). */
+typedef struct {
+  int32_t n_seqs;
+  int32_t append_tokens;
+  int32_t n_pairs;       /* copy-on-write pairs taken by this call        */
+  int32_t table_stride;
+  int64_t off_slots;     /* int64 [n_seqs][append_tokens]                 */
+  int64_t off_pairs;     /* int32 [n_pairs][2]                            */
+  int64_t off_tables;    /* int32 [n_seqs][table_stride]                  */
+  int64_t off_lens;      /* int32 [n_seqs]                                */
+  int64_t off_plan;      /* int32 [plan.plan_ints]                        */
+  int64_t bytes;         /* bytes used from the start of the buffer       */
+  pkv_decode_plan_info plan;
+} pkv_batch_layout;
+
+/* Staging bytes pkv_prepare_decode needs at most for a batch of up to
+ * max_seqs sequences whose tables fit table_stride blocks. */
+size_t pkv_prepare_decode_bytes(int32_t max_seqs, int32_t append_tokens, int32_t table_stride,
+                                int32_t block_size, int32_t partition_tokens);
+
+/* The host half of a continuous-batching decode iteration ([lesson]
+ * paragraph 8: running sequences advance one token per iteration), in one
+ * call: append append_tokens (0 or more) to each of seqs[0..n_seqs) in that
+ * order (pkv_seq_append_batch), take the copy-on-write pairs, build block
+ * tables and context lengths (pkv_build_batch) and the split-K plan
+ * (pkv_decode_plan), all written into the host buffer `staging` (ideally
+ * pinned) at the offsets returned in *layout.  Upload the first
+ * layout->bytes bytes unchanged to a device buffer; the device arrays then
+ * sit at the same offsets.  All or nothing: on error the pool is unchanged. */
+pkv_status pkv_prepare_decode(pkv_pool* pool, const int32_t* seqs, int32_t n_seqs,
+                              int32_t append_tokens, int32_t table_stride,
+                              int32_t partition_tokens, void* staging, size_t staging_bytes,
+                              pkv_batch_layout* layout);
+
+/* ---------------------------------------------------------------------------
+ * Device (HIP, gfx950): asynchronous on `stream`
+ * ------------------------------------------------------------------------ */
+
+/* Copy-on-write copies ([lesson] paragraph 7): for each pair, K[dst] = K[src]
+ * and V[dst] = V[src] over all heads and rows.  pairs: device int32
+ * [n_pairs][2].  Pairs with an id outside the pool are skipped. */
+pkv_status pkv_copy_blocks(const pkv_pool* pool, const int32_t* pairs, int32_t n_pairs,
+                           void* stream);
+
+/* Store new tokens' K and V rows at their slots ([preview] step 3; the
+ * "reshape_and_cache" step of a decode iteration).  k_new, v_new: device
+ * [n_tokens][num_kv_heads][head_dim] of the pool dtype; slot_mapping: device
+ * int64 [n_tokens]; a negative slot skips the token, as does a slot outside
+ * the pool.  Bit-exact copy. */
+pkv_status pkv_write_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
+                        const int64_t* slot_mapping, int32_t n_tokens, void* stream);
+
+/* PagedAttention decode ([lesson] paragraph 5, [preview] step 5): for every
+ * sequence i and query head h,
+ *     out[i][h] = softmax_j(scale * q[i][h] . K_i[j][g]) . V_i[j][g]
+ * over the context_lens[i] tokens of sequence i, where K_i / V_i row j is read
+ * from the pool through block_tables[i][j / block_size] and
+ * g = h / (num_q_heads / num_kv_heads).  Paging does not change the result of
+ * dense attention ([preview] "Lo que deberías llevarte", item 2).
+ *   q:            device [num_seqs][num_q_heads][head_dim], pool dtype
+ *   out:          device float32 [num_seqs][num_q_heads][head_dim]
+ *   block_tables: device int32 [num_seqs][table_stride]
+ *   context_lens: device int32 [num_seqs]; every entry >= 1 and equal to the
+ *                 lengths given to pkv_decode_plan
+ *   plan, info:   device copy of the plan and its host-side info
+ *   workspace:    device, >= pkv_decode_workspace_bytes(info, ...) bytes
+ * Arithmetic: fp32 accumulation and an online (running max) softmax; the
+ * output is float32.  Table entries outside the pool read nothing. */
+pkv_status pkv_paged_decode(const pkv_pool* pool, const void* q, float* out, int32_t num_seqs,
+                            int32_t num_q_heads, const int32_t* block_tables,
+                            int32_t table_stride, const int32_t* context_lens, float scale,
+                            const int32_t* plan, const pkv_decode_plan_info* info,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two halves of pkv_paged_decode, same arguments, for callers that want
+ * to time or schedule them apart: the partition kernel (writes out for
+ * single-partition sequences, partials to the workspace otherwise), then the
+ * combine of the partials.  pkv_paged_decode = partitions + reduce. */
+pkv_status pkv_paged_decode_partitions(const pkv_pool* pool, const void* q, float* out,
+                                       int32_t num_seqs, int32_t num_q_heads,
+                                       const int32_t* block_tables, int32_t table_stride,
+                                       const int32_t* context_lens, float scale,
+                                       const int32_t* plan, const pkv_decode_plan_info* info,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+pkv_status pkv_paged_decode_reduce(const pkv_pool* pool, const void* q, float* out,
+                                   int32_t num_seqs, int32_t num_q_heads,
+                                   const int32_t* block_tables, int32_t table_stride,
+                                   const int32_t* context_lens, float scale,
+                                   const int32_t* plan, const pkv_decode_plan_info* info,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,20 @@
+"""paged_kv_cache_257_amd -- paged KV cache and PagedAttention decode on MI355X.
+
+The product is the C-ABI library ``lib/libpkv.so`` (include/pkv.h): a C++
+block allocator and HIP kernels for gfx950.  This package is its thin Python
+binding: ``Pool`` mirrors the pkv_* calls, ``DecodeIteration`` strings them
+into one decode iteration.  Importing it does not load the library; the
+first call does, and raises if it is not built (there is no fallback).
+"""
+
+from ._capi import PkvError, load  # noqa: F401
+from .pool import Pool, decode_plan, decode_workspace_bytes  # noqa: F401
+
+__all__ = ["Pool", "PkvError", "decode_plan", "decode_workspace_bytes", "load", "DecodeIteration"]
+
+
+def __getattr__(name):
+    if name == "DecodeIteration":
+        from .step import DecodeIteration
+        return DecodeIteration
+    raise AttributeError(name)

@@ -1,0 +1,490 @@
+// PagedAttention decode for gfx950.
+//
+// For every sequence i and query head h: out = softmax(scale * q . K^T) . V
+// over the sequence's logical tokens, with K/V rows read through the
+// sequence's block table ("PagedAttention e continuous batching",
+// 01 · Conceito, paragraph 5; "04 — Hacia PagedAttention", La idea de
+// PagedAttention, step 5).  Paging changes where rows live, not the result
+// or the FLOPs of dense attention ("Lo que deberías llevarte", item 2), so
+// the kernel is bound by HBM bandwidth: one pass over the K/V bytes.
+//
+// Work decomposition.  A host plan cuts every sequence into partitions of P
+// tokens (split-K); one workgroup takes one (partition, KV head, group of GW
+// query heads sharing that KV head).  Its NW waves stride over the
+// partition's blocks.  A (block, KV head) tile of K is 16 rows x R bytes,
+// contiguous (R = head_dim * element size); lane l of a wave loads bytes
+// [l*16, l*16+16) of each 1 KiB quarter, so every load instruction reads 1
+// KiB contiguous.  With R = 256 (fp16/bf16 x 128, fp32 x 64) a row spans 16
+// lanes, one DPP row: lanes of "row group" r = l/16 hold token rows r, r+4,
+// r+8, r+12 of every block, each lane 8 (or 4) elements of each row.
+//
+// Per block and query head a lane forms the partial dot products of its
+// chunk (v_dot2_f32_{f16,bf16} or fp32 FMA), sums them across the row's lanes
+// with DPP rotations (all lanes of the row get the score), and updates an
+// online softmax (running max m, running sum l, rescaled output o) that is
+// private to its row group, so no cross-row exchange is needed inside the
+// loop.  Scores are kept in base 2 (q . k * scale * log2 e) so that every
+// exponential is one v_exp_f32.  The next block's K and V are loaded while
+// the current one is processed.  At the end the row groups and waves of the
+// workgroup merge their (m, l, o) through LDS; a single-partition sequence
+// writes o / l, otherwise (m, l, o) go to the workspace and the reduce
+// kernel merges the partitions:  M = max m_p,
+//   out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+//
+// Rows past the sequence length in its last block are masked: their score
+// is -inf and their V row is replaced by zeros, so stale or NaN contents of
+// unused slots never reach the output.  Table entries outside the pool are
+// treated as fully masked blocks (nothing is read through them).
+#include <cstdlib>
+
+#include "device_common.h"
+
+namespace pkv {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeParams {
+  const char* q;
+  float* out;
+  const char* k_cache;
+  const char* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* work;         // [n_work][2] (sequence, partition)
+  const int32_t* part_offset;  // [num_seqs] first partial index or -1
+  float* part_o;               // [n_partials][H_q][D]
+  float* part_ml;              // [n_partials][H_q][2]
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;               // H_q / H_kv
+  int32_t hgroups_per_kv;      // group / GW
+  int32_t table_stride;
+  int32_t num_blocks;
+  int32_t partition_blocks;
+  int32_t n_partials;
+  float scale_log2;
+};
+
+template <int DT, int D, int GW, int NW>
+__global__ __launch_bounds__(kWave* NW) void paged_decode_kernel(const DecodeParams p) {
+  constexpr int E = ElemBytes<DT>::value;
+  constexpr int R = D * E;         // bytes per token row of one head
+  constexpr int LPR = R / 16;      // lanes per token row
+  constexpr int RPI = kWave / LPR; // token rows per load instruction
+  constexpr int NI = kBlockTokens / RPI;  // load instructions per tile
+  constexpr int EPL = 16 / E;      // elements per lane per row
+  constexpr int TILE = kBlockTokens * R;
+  static_assert(LPR >= 8 && LPR <= 64 && NI >= 1, "unsupported head_dim / dtype");
+
+  __shared__ float sm_m[NW * RPI * GW];
+  __shared__ float sm_l[NW * RPI * GW];
+  __shared__ float sm_o[NW * RPI * GW * D];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int hgroups = p.num_kv_heads * p.hgroups_per_kv;
+  const int wi = blockIdx.x / hgroups;
+  const int hg = blockIdx.x - wi * hgroups;
+  const int seq = p.work[2 * wi];
+  const int part = p.work[2 * wi + 1];
+  const int kvh = hg / p.hgroups_per_kv;
+  const int qh0 = kvh * p.group + (hg - kvh * p.hgroups_per_kv) * GW;
+  const int L = p.context_lens[seq];
+  const int nblk = min((L + kBlockTokens - 1) / kBlockTokens, p.table_stride);
+  const int n_parts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  const int b0 = part * p.partition_blocks;
+  const int b1 = min(b0 + p.partition_blocks, nblk);
+
+  const int rg = lane / LPR;  // row group
+  const int c = lane - rg * LPR;
+
+  u32x4 qv[GW];
+#pragma unroll
+  for (int g = 0; g < GW; ++g)
+    qv[g] = *reinterpret_cast<const u32x4*>(
+        p.q + (int64_t(seq) * p.num_q_heads + qh0 + g) * R + c * 16);
+
+  float m[GW], l[GW], o[GW][EPL];
+#pragma unroll
+  for (int g = 0; g < GW; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[g][e] = 0.f;
+  }
+
+  const int32_t* trow = p.block_tables + int64_t(seq) * p.table_stride;
+  const int64_t blk_stride = int64_t(p.num_kv_heads) * TILE;
+  const char* kbase = p.k_cache + int64_t(kvh) * TILE + lane * 16;
+  const char* vbase = p.v_cache + int64_t(kvh) * TILE + lane * 16;
+
+  // 64 table entries at a time, one per lane; block ids are then read with
+  // v_readlane (the block index is uniform across the wave).
+  int tbl = -1, tbl_base = -1;
+  auto block_id = [&](int j) -> int {
+    const int base = j & ~(kWave - 1);
+    if (base != tbl_base) {
+      tbl_base = base;
+      tbl = (base + lane < nblk) ? trow[base + lane] : -1;
+    }
+    return __builtin_amdgcn_readlane(tbl, j - base);
+  };
+
+  u32x4 kc[NI], vc[NI], kn[NI], vn[NI];
+  auto load = [&](int blk, u32x4* kk, u32x4* vv) {
+    const int b = (unsigned(blk) < unsigned(p.num_blocks)) ? blk : 0;
+    const char* kt = kbase + int64_t(b) * blk_stride;
+    const char* vt = vbase + int64_t(b) * blk_stride;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kk[i] = *reinterpret_cast<const u32x4*>(kt + i * 1024);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vv[i] = *reinterpret_cast<const u32x4*>(vt + i * 1024);
+  };
+
+  // Online-softmax update with one block; `valid` = rows of the block that
+  // hold tokens (16 except in the last block).
+  auto process = [&](const u32x4* kk, const u32x4* vv, int valid, bool masked) {
+    float ps[GW][NI];
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      float s[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float part_dot = dot16<DT>(qv[g], kk[i], 0.f);
+        s[i] = row_sum<LPR>(part_dot) * p.scale_log2;
+      }
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          if (i * RPI + rg >= valid) s[i] = -INFINITY;
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) mx = fmaxf(mx, s[i]);
+      const float m_new = fmaxf(m[g], mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - m_use);
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        ps[g][i] = __builtin_amdgcn_exp2f(s[i] - m_use);
+        sum += ps[g][i];
+      }
+      l[g] = l[g] * alpha + sum;
+      m[g] = m_new;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[g][e] *= alpha;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float vf[EPL];
+      to_f32<DT>(vv[i], vf);
+      if (masked && i * RPI + rg >= valid) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < GW; ++g)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[g][e] = __builtin_fmaf(ps[g][i], vf[e], o[g][e]);
+    }
+  };
+
+  int j = b0 + wave;
+  int blk = -1;
+  if (j < b1) {
+    blk = block_id(j);
+    load(blk, kc, vc);
+  }
+  while (j < b1) {
+    const int jn = j + NW;
+    int blk_n = -1;
+    if (jn < b1) {
+      blk_n = block_id(jn);
+      load(blk_n, kn, vn);
+    }
+    const bool in_pool = unsigned(blk) < unsigned(p.num_blocks);
+    if (in_pool && j != nblk - 1) {
+      process(kc, vc, kBlockTokens, false);
+    } else {
+      const int valid = in_pool ? min(kBlockTokens, L - j * kBlockTokens) : 0;
+      process(kc, vc, valid, true);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      kc[i] = kn[i];
+      vc[i] = vn[i];
+    }
+    blk = blk_n;
+    j = jn;
+  }
+
+  // merge the NW * RPI partial softmax states of this workgroup
+  const int sub = wave * RPI + rg;
+#pragma unroll
+  for (int g = 0; g < GW; ++g) {
+    if (c == 0) {
+      sm_m[sub * GW + g] = m[g];
+      sm_l[sub * GW + g] = l[g];
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sm_o[(sub * GW + g) * D + c * EPL + e] = o[g][e];
+  }
+  __syncthreads();
+
+  const bool single = (n_parts <= 1);
+  const int pidx = single ? -1 : p.part_offset[seq] + part;
+  if (!single && (pidx < 0 || pidx >= p.n_partials)) return;
+  for (int idx = threadIdx.x; idx < GW * D; idx += kWave * NW) {
+    const int g = idx / D;
+    const int dd = idx - g * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NW * RPI; ++s) M = fmaxf(M, sm_m[s * GW + g]);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int s = 0; s < NW * RPI; ++s) {
+      const float w = __builtin_amdgcn_exp2f(sm_m[s * GW + g] - M_use);
+      num = __builtin_fmaf(w, sm_o[(s * GW + g) * D + dd], num);
+      den = __builtin_fmaf(w, sm_l[s * GW + g], den);
+    }
+    const int qh = qh0 + g;
+    if (single) {
+      p.out[(int64_t(seq) * p.num_q_heads + qh) * D + dd] = num / den;
+    } else {
+      const int64_t row = int64_t(pidx) * p.num_q_heads + qh;
+      p.part_o[row * D + dd] = num;
+      if (dd == 0) {
+        p.part_ml[2 * row] = M;
+        p.part_ml[2 * row + 1] = den;
+      }
+    }
+  }
+}
+
+struct ReduceParams {
+  float* out;
+  const float* part_o;
+  const float* part_ml;
+  const int32_t* context_lens;
+  const int32_t* part_offset;
+  const int32_t* reduce_seqs;
+  int32_t num_q_heads;
+  int32_t table_stride;
+  int32_t partition_blocks;
+  int32_t n_partials;
+};
+
+// One workgroup of D threads per (multi-partition sequence, query head).
+template <int D>
+__global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const ReduceParams p) {
+  const int r = blockIdx.x / p.num_q_heads;
+  const int h = blockIdx.x - r * p.num_q_heads;
+  const int seq = p.reduce_seqs[r];
+  const int L = p.context_lens[seq];
+  const int nblk = min((L + kBlockTokens - 1) / kBlockTokens, p.table_stride);
+  const int n_parts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  const int base = p.part_offset[seq];
+  if (base < 0 || base + n_parts > p.n_partials) return;
+  const int dd = threadIdx.x;
+  float M = -INFINITY;
+  for (int q = 0; q < n_parts; ++q)
+    M = fmaxf(M, p.part_ml[2 * (int64_t(base + q) * p.num_q_heads + h)]);
+  const float M_use = (M == -INFINITY) ? 0.f : M;
+  float num = 0.f, den = 0.f;
+  for (int q = 0; q < n_parts; ++q) {
+    const int64_t row = int64_t(base + q) * p.num_q_heads + h;
+    const float w = __builtin_amdgcn_exp2f(p.part_ml[2 * row] - M_use);
+    num = __builtin_fmaf(w, p.part_o[row * D + dd], num);
+    den = __builtin_fmaf(w, p.part_ml[2 * row + 1], den);
+  }
+  p.out[(int64_t(seq) * p.num_q_heads + h) * D + dd] = num / den;
+}
+
+using DecodeFn = void (*)(const DecodeParams);
+
+template <int DT, int D, int GW>
+DecodeFn pick_waves(int nw) {
+  switch (nw) {
+    case 1: return paged_decode_kernel<DT, D, GW, 1>;
+    case 2: return paged_decode_kernel<DT, D, GW, 2>;
+    case 4: return paged_decode_kernel<DT, D, GW, 4>;
+    default: return nullptr;
+  }
+}
+
+template <int DT, int D>
+DecodeFn pick_gw(int gw, int nw) {
+  switch (gw) {
+    case 1: return pick_waves<DT, D, 1>(nw);
+    case 2: return pick_waves<DT, D, 2>(nw);
+    case 4: return pick_waves<DT, D, 4>(nw);
+    case 8: return pick_waves<DT, D, 8>(nw);
+    default: return nullptr;
+  }
+}
+
+template <int DT>
+DecodeFn pick_d(int d, int gw, int nw) {
+  switch (d) {
+    case 64: return pick_gw<DT, 64>(gw, nw);
+    case 128: return pick_gw<DT, 128>(gw, nw);
+    case 256: return pick_gw<DT, 256>(gw, nw);
+    default: return nullptr;
+  }
+}
+
+DecodeFn pick_decode(int dt, int d, int gw, int nw) {
+  switch (dt) {
+    case PKV_F32: return pick_d<PKV_F32>(d, gw, nw);
+    case PKV_F16: return pick_d<PKV_F16>(d, gw, nw);
+    case PKV_BF16: return pick_d<PKV_BF16>(d, gw, nw);
+    default: return nullptr;
+  }
+}
+
+// Waves per workgroup: an environment override for tuning sweeps, else 1.
+int waves_per_item() {
+  static const int nw = [] {
+    const char* s = std::getenv("PKV_DECODE_WAVES");
+    int v = s ? std::atoi(s) : 0;
+    return (v == 1 || v == 2 || v == 4) ? v : 1;
+  }();
+  return nw;
+}
+
+// Validate the arguments shared by the decode entry points and fill the
+// kernel parameters.  Returns PKV_OK with *empty set when there is no work.
+pkv_status setup_decode(const pkv_pool* pool, const void* q, float* out, int32_t num_seqs,
+                        int32_t num_q_heads, const int32_t* block_tables, int32_t table_stride,
+                        const int32_t* context_lens, float scale, const int32_t* plan,
+                        const pkv_decode_plan_info* info, void* workspace, size_t workspace_bytes,
+                        DecodeParams& prm, int& gw, bool& empty) {
+  empty = false;
+  if (!pool) return fail(PKV_E_BAD_ARG, "null pool");
+  const pkv_pool_desc& d = pool->desc;
+  if (!pool->k_cache || !pool->v_cache) return fail(PKV_E_BAD_ARG, "pool has no device K/V arrays");
+  if (d.block_size != kBlockTokens)
+    return fail(PKV_E_UNSUPPORTED, "device kernels take block_size 16 only");
+  if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256)
+    return fail(PKV_E_UNSUPPORTED, "head_dim must be 64, 128 or 256");
+  if (!info) return fail(PKV_E_BAD_ARG, "null plan info");
+  if (num_seqs < 0 || num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0)
+    return fail(PKV_E_BAD_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (info->num_seqs != num_seqs || info->block_size != d.block_size ||
+      info->partition_tokens < kBlockTokens || info->partition_tokens % kBlockTokens != 0 ||
+      info->n_work < 0 || info->n_partials < 0 || info->n_reduce < 0)
+    return fail(PKV_E_BAD_ARG, "plan info does not match this batch");
+  if (table_stride < 1) return fail(PKV_E_BAD_ARG, "table_stride must be >= 1");
+  if (int64_t(info->max_context_len) > int64_t(table_stride) * kBlockTokens)
+    return fail(PKV_E_BAD_ARG, "a context is longer than its table can address");
+  if (num_seqs == 0 || info->n_work == 0) {
+    empty = true;
+    return PKV_OK;
+  }
+  if (!q || !out || !block_tables || !context_lens || !plan)
+    return fail(PKV_E_BAD_ARG, "null device pointer");
+  const size_t need = pkv_decode_workspace_bytes(info, num_q_heads, d.head_dim);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_E_BAD_ARG, "workspace too small: need " + std::to_string(need) + " bytes");
+  const int group = num_q_heads / d.num_kv_heads;
+  gw = (group % 8 == 0) ? 8 : (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
+  prm.q = static_cast<const char*>(q);
+  prm.out = out;
+  prm.k_cache = static_cast<const char*>(pool->k_cache);
+  prm.v_cache = static_cast<const char*>(pool->v_cache);
+  prm.block_tables = block_tables;
+  prm.context_lens = context_lens;
+  prm.work = plan;
+  prm.part_offset = plan + 2 * int64_t(info->n_work);
+  prm.part_o = static_cast<float*>(workspace);
+  prm.part_ml = prm.part_o + int64_t(info->n_partials) * num_q_heads * d.head_dim;
+  prm.num_q_heads = num_q_heads;
+  prm.num_kv_heads = d.num_kv_heads;
+  prm.group = group;
+  prm.hgroups_per_kv = group / gw;
+  prm.table_stride = table_stride;
+  prm.num_blocks = d.num_blocks;
+  prm.partition_blocks = info->partition_tokens / kBlockTokens;
+  prm.n_partials = info->n_partials;
+  prm.scale_log2 = scale * kLog2e;
+  if (int64_t(info->n_work) * d.num_kv_heads * prm.hgroups_per_kv > INT32_MAX ||
+      int64_t(info->n_reduce) * num_q_heads > INT32_MAX)
+    return fail(PKV_E_BAD_ARG, "batch too large for one launch");
+  return PKV_OK;
+}
+
+pkv_status launch_partitions(const pkv_pool* pool, const DecodeParams& prm, int gw,
+                             const pkv_decode_plan_info* info, hipStream_t s) {
+  const int nw = waves_per_item();
+  DecodeFn fn = pick_decode(pool->desc.dtype, pool->desc.head_dim, gw, nw);
+  if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group");
+  const int64_t grid = int64_t(info->n_work) * prm.num_kv_heads * prm.hgroups_per_kv;
+  hipLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kWave * nw), 0, s, prm);
+  return launch_status("paged_decode launch");
+}
+
+pkv_status launch_reduce(const pkv_pool* pool, const DecodeParams& prm, int32_t num_seqs,
+                         const pkv_decode_plan_info* info, hipStream_t s) {
+  if (info->n_reduce == 0) return PKV_OK;
+  ReduceParams rp;
+  rp.out = prm.out;
+  rp.part_o = prm.part_o;
+  rp.part_ml = prm.part_ml;
+  rp.context_lens = prm.context_lens;
+  rp.part_offset = prm.part_offset;
+  rp.reduce_seqs = prm.part_offset + num_seqs;
+  rp.num_q_heads = prm.num_q_heads;
+  rp.table_stride = prm.table_stride;
+  rp.partition_blocks = prm.partition_blocks;
+  rp.n_partials = info->n_partials;
+  void (*rfn)(const ReduceParams) = nullptr;
+  switch (pool->desc.head_dim) {
+    case 64: rfn = paged_decode_reduce_kernel<64>; break;
+    case 128: rfn = paged_decode_reduce_kernel<128>; break;
+    case 256: rfn = paged_decode_reduce_kernel<256>; break;
+  }
+  const int64_t rgrid = int64_t(info->n_reduce) * prm.num_q_heads;
+  hipLaunchKernelGGL(rfn, dim3(uint32_t(rgrid)), dim3(pool->desc.head_dim), 0, s, rp);
+  return launch_status("paged_decode_reduce launch");
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+#define PKV_DECODE_ARGS                                                                          \
+  const pkv_pool *pool, const void *q, float *out, int32_t num_seqs, int32_t num_q_heads,       \
+      const int32_t *block_tables, int32_t table_stride, const int32_t *context_lens,           \
+      float scale, const int32_t *plan, const pkv_decode_plan_info *info, void *workspace,      \
+      size_t workspace_bytes, void *stream
+#define PKV_SETUP                                                                                \
+  DecodeParams prm;                                                                              \
+  int gw = 1;                                                                                    \
+  bool empty = false;                                                                            \
+  if (pkv_status st = setup_decode(pool, q, out, num_seqs, num_q_heads, block_tables,          \
+                                   table_stride, context_lens, scale, plan, info, workspace,    \
+                                   workspace_bytes, prm, gw, empty))                             \
+    return st;                                                                                   \
+  if (empty) return PKV_OK;                                                                      \
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+extern "C" pkv_status pkv_paged_decode(PKV_DECODE_ARGS) {
+  PKV_SETUP
+  if (pkv_status st = launch_partitions(pool, prm, gw, info, s)) return st;
+  return launch_reduce(pool, prm, num_seqs, info, s);
+}
+
+extern "C" pkv_status pkv_paged_decode_partitions(PKV_DECODE_ARGS) {
+  PKV_SETUP
+  return launch_partitions(pool, prm, gw, info, s);
+}
+
+extern "C" pkv_status pkv_paged_decode_reduce(PKV_DECODE_ARGS) {
+  PKV_SETUP
+  (void)gw;
+  return launch_reduce(pool, prm, num_seqs, info, s);
+}

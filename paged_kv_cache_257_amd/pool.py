@@ -1,0 +1,189 @@
+"""Python face of libpkv: the same calls as include/pkv.h, marshalled.
+
+Device memory and streams come from PyTorch; every computation runs in the
+library (host allocator in C++, kernels in HIP).  Host arrays are numpy.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _capi
+from ._capi import PlanInfo, PoolDesc, Stats, check, i32p, i64p
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class Pool:
+    """A paged K/V pool: host allocator state plus (optionally) device K/V.
+
+    ``k_cache`` / ``v_cache``: device tensors shaped
+    [num_blocks][num_kv_heads][block_size][head_dim] of the pool dtype, or
+    None for an allocator-only pool (``host_only=True`` loads the g++-built
+    allocator library, usable without a GPU).
+    """
+
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
+                 max_blocks_per_seq: int, block_size: int = 16, free_order=None,
+                 k_cache=None, v_cache=None, host_only: bool = False):
+        self.lib = _capi.load(host_only=host_only)
+        self.desc = PoolDesc(num_blocks, block_size, num_kv_heads, head_dim, max_blocks_per_seq,
+                             _capi.DTYPES[dtype])
+        self.dtype = dtype
+        self.k_cache, self.v_cache = k_cache, v_cache
+        order = None if free_order is None else np.ascontiguousarray(free_order, dtype=np.int32)
+        h = C.c_void_p()
+        check(self.lib, self.lib.pkv_pool_create(C.byref(self.desc), _dptr(k_cache), _dptr(v_cache),
+                                                 i32p(order), C.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            self.lib.pkv_pool_destroy(self.handle)
+            self.handle = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 -- interpreter shutdown
+            pass
+
+    # ---- allocator -----------------------------------------------------------
+    def reset(self):
+        check(self.lib, self.lib.pkv_pool_reset(self.handle))
+
+    def alloc(self, n_tokens: int) -> Tuple[int, np.ndarray]:
+        sid = C.c_int32()
+        slots = np.empty(max(n_tokens, 1), dtype=np.int64)
+        check(self.lib, self.lib.pkv_seq_alloc(self.handle, n_tokens, C.byref(sid), i64p(slots)))
+        return sid.value, slots[:n_tokens]
+
+    def append(self, seq: int, n_tokens: int = 1) -> np.ndarray:
+        slots = np.empty(max(n_tokens, 1), dtype=np.int64)
+        check(self.lib, self.lib.pkv_seq_append(self.handle, seq, n_tokens, i64p(slots)))
+        return slots[:n_tokens]
+
+    def append_batch(self, seqs: Sequence[int], n_tokens: int = 1) -> np.ndarray:
+        s = np.ascontiguousarray(seqs, dtype=np.int32)
+        slots = np.empty((max(len(s), 1), max(n_tokens, 1)), dtype=np.int64)
+        check(self.lib, self.lib.pkv_seq_append_batch(self.handle, i32p(s), len(s), n_tokens,
+                                                      i64p(slots)))
+        return slots[:len(s), :n_tokens]
+
+    def fork(self, parent: int) -> int:
+        c = C.c_int32()
+        check(self.lib, self.lib.pkv_seq_fork(self.handle, parent, C.byref(c)))
+        return c.value
+
+    def free(self, seq: int) -> None:
+        check(self.lib, self.lib.pkv_seq_free(self.handle, seq))
+
+    def length(self, seq: int) -> int:
+        n = C.c_int32()
+        check(self.lib, self.lib.pkv_seq_length(self.handle, seq, C.byref(n)))
+        return n.value
+
+    def table(self, seq: int) -> List[int]:
+        cap = self.desc.max_blocks_per_seq
+        buf = np.empty(cap, dtype=np.int32)
+        n = C.c_int32()
+        check(self.lib, self.lib.pkv_seq_table(self.handle, seq, i32p(buf), cap, C.byref(n)))
+        return buf[:n.value].tolist()
+
+    def live(self) -> List[int]:
+        n = C.c_int32()
+        self.lib.pkv_live_seqs(self.handle, None, 0, C.byref(n))
+        buf = np.empty(max(n.value, 1), dtype=np.int32)
+        check(self.lib, self.lib.pkv_live_seqs(self.handle, i32p(buf), len(buf), C.byref(n)))
+        return buf[:n.value].tolist()
+
+    def free_list(self) -> List[int]:
+        buf = np.empty(max(self.desc.num_blocks, 1), dtype=np.int32)
+        n = C.c_int32()
+        check(self.lib, self.lib.pkv_free_list(self.handle, i32p(buf), len(buf), C.byref(n)))
+        return buf[:n.value].tolist()
+
+    def refcounts(self) -> List[int]:
+        buf = np.empty(max(self.desc.num_blocks, 1), dtype=np.int32)
+        check(self.lib, self.lib.pkv_refcounts(self.handle, i32p(buf)))
+        return buf[:self.desc.num_blocks].tolist()
+
+    def stats(self) -> dict:
+        s = Stats()
+        check(self.lib, self.lib.pkv_stats(self.handle, C.byref(s)))
+        return s.as_dict()
+
+    def take_cow(self) -> np.ndarray:
+        n = C.c_int32()
+        self.lib.pkv_take_cow(self.handle, None, 0, C.byref(n))
+        buf = np.empty((max(n.value, 1), 2), dtype=np.int32)
+        check(self.lib, self.lib.pkv_take_cow(self.handle, i32p(buf), len(buf), C.byref(n)))
+        return buf[:n.value]
+
+    def build_batch(self, seqs: Sequence[int], table_stride: int,
+                    tables: Optional[np.ndarray] = None, lens: Optional[np.ndarray] = None):
+        s = np.ascontiguousarray(seqs, dtype=np.int32)
+        if tables is None:
+            tables = np.empty((len(s), table_stride), dtype=np.int32)
+        if lens is None:
+            lens = np.empty(len(s), dtype=np.int32)
+        check(self.lib, self.lib.pkv_build_batch(self.handle, i32p(s), len(s), i32p(tables),
+                                                 table_stride, i32p(lens)))
+        return tables, lens
+
+    # ---- device ----------------------------------------------------------------
+    def write_kv(self, k_new, v_new, slot_mapping, stream=None) -> None:
+        """k_new, v_new: device [T][H_kv][d]; slot_mapping: device int64 [T]."""
+        n = int(slot_mapping.shape[0])
+        check(self.lib, self.lib.pkv_write_kv(self.handle, _dptr(k_new), _dptr(v_new),
+                                              _dptr(slot_mapping), n, _stream_ptr(stream)))
+
+    def copy_blocks(self, pairs, stream=None) -> None:
+        """pairs: device int32 [n][2] (src, dst)."""
+        n = int(pairs.shape[0])
+        check(self.lib, self.lib.pkv_copy_blocks(self.handle, _dptr(pairs), n, _stream_ptr(stream)))
+
+    def paged_decode(self, q, out, block_tables, context_lens, scale: float, plan, info: PlanInfo,
+                     workspace, stream=None) -> None:
+        """Decode attention of every sequence of the batch through its table."""
+        B, Hq = int(q.shape[0]), int(q.shape[1])
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        check(self.lib, self.lib.pkv_paged_decode(
+            self.handle, _dptr(q), _dptr(out), B, Hq, _dptr(block_tables),
+            int(block_tables.shape[1]), _dptr(context_lens), float(scale), _dptr(plan),
+            C.byref(info), _dptr(workspace), ws_bytes, _stream_ptr(stream)))
+
+
+def decode_plan(context_lens: np.ndarray, partition_tokens: int = 0, block_size: int = 16,
+                host_only: bool = False) -> Tuple[np.ndarray, PlanInfo]:
+    """Host split-K plan (see pkv_decode_plan) for these context lengths."""
+    lib = _capi.load(host_only=host_only)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    n = C.c_int32()
+    check(lib, lib.pkv_decode_plan_ints(i32p(lens), len(lens), block_size, partition_tokens,
+                                        C.byref(n)))
+    plan = np.empty(max(n.value, 1), dtype=np.int32)
+    info = PlanInfo()
+    check(lib, lib.pkv_decode_plan(i32p(lens), len(lens), block_size, partition_tokens, i32p(plan),
+                                   len(plan), C.byref(info)))
+    return plan[:info.plan_ints], info
+
+
+def decode_workspace_bytes(info: PlanInfo, num_q_heads: int, head_dim: int,
+                           host_only: bool = False) -> int:
+    lib = _capi.load(host_only=host_only)
+    return int(lib.pkv_decode_workspace_bytes(C.byref(info), num_q_heads, head_dim))

@@ -1,0 +1,100 @@
+"""Helpers for the GPU parity tests: device tensors from storage bits, and
+one decode workload set up on both the HIP path and the oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle.runs import DecodeRun
+from paged_kv_cache_257_amd import Pool, decode_plan, decode_workspace_bytes
+from workloads import draw_decode_values
+from workloads.configs import draw_decode_shapes
+
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+
+
+def to_device(bits: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Storage bits (float32 / float16 / uint16-for-bf16) -> device tensor."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(bits))
+    return t.to(device)
+
+
+def device_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bits of a device tensor as a host integer array."""
+    if t.element_size() == 4:
+        return t.view(torch.int32).cpu().numpy()
+    return t.view(torch.int16).cpu().numpy()
+
+
+def host_bits(a: np.ndarray) -> np.ndarray:
+    return a.view(np.int32) if a.dtype.itemsize == 4 else a.view(np.int16)
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+class DecodeCase:
+    """A decode workload on the HIP path and on the oracle."""
+
+    def __init__(self, cfg, lens=None, num_blocks=None, free_order=None, table_stride=None,
+                 fill=0.0, values=None):
+        self.cfg = cfg
+        if lens is None:
+            sh = draw_decode_shapes(cfg)
+            lens, num_blocks, free_order = sh.lens, sh.num_blocks, sh.free_order
+        self.lens = np.asarray(lens, dtype=np.int64)
+        self.num_blocks = int(num_blocks)
+        self.free_order = np.asarray(free_order, dtype=np.int32)
+        self.stride = table_stride or max(1, max(-(-int(L) // 16) for L in self.lens))
+        self.vals = values if values is not None else draw_decode_values(cfg, self.lens)
+        H, d, dt = cfg.num_kv_heads, cfg.head_dim, cfg.dtype
+        shape = (self.num_blocks, H, 16, d)
+        tdt = TORCH_DTYPE[dt]
+        self.k_cache = torch.full(shape, fill, dtype=tdt, device="cuda")
+        self.v_cache = torch.full(shape, fill, dtype=tdt, device="cuda")
+        self.pool = Pool(self.num_blocks, H, d, dt, self.stride, 16, self.free_order,
+                         self.k_cache, self.v_cache)
+        self.oracle = DecodeRun(cfg, self.lens, self.num_blocks, self.free_order, self.stride)
+        self.oracle.write_context(self.vals["k"], self.vals["v"])
+        slots = []
+        for L in self.lens:
+            _, s = self.pool.alloc(int(L))
+            slots.append(s)
+        self.slots = np.concatenate(slots) if slots else np.zeros(0, np.int64)
+        self.seqs = list(range(len(self.lens)))
+
+    def write_context(self):
+        k = to_device(self.vals["k"], self.cfg.dtype)
+        v = to_device(self.vals["v"], self.cfg.dtype)
+        slots = torch.from_numpy(self.slots).cuda()
+        self.pool.write_kv(k, v, slots)
+        sync()
+        del k, v
+
+    def decode(self, partition_tokens=0):
+        cfg = self.cfg
+        tables, lens = self.pool.build_batch(self.seqs, self.stride)
+        plan, info = decode_plan(lens, partition_tokens)
+        q = to_device(self.vals["q"], cfg.dtype)
+        out = torch.full((len(self.lens), cfg.num_q_heads, cfg.head_dim), float("nan"),
+                         dtype=torch.float32, device="cuda")
+        ws = decode_workspace_bytes(info, cfg.num_q_heads, cfg.head_dim)
+        workspace = torch.empty(max(ws // 4, 1), dtype=torch.float32, device="cuda")
+        self.pool.paged_decode(q, out, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                               cfg.scale, torch.from_numpy(plan).cuda(), info, workspace)
+        sync()
+        return out.cpu().numpy().astype(np.float64), info
+
+    def oracle_out(self, i: int) -> np.ndarray:
+        return self.oracle.attend(i, self.vals["q"][i])
+
+    def close(self):
+        self.pool.close()
+        del self.k_cache, self.v_cache
+        torch.cuda.empty_cache()

@@ -1,0 +1,56 @@
+"""The host split-K plan (pkv_decode_plan), checked by enumeration (CPU)."""
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_257_amd import PkvError, decode_plan, decode_workspace_bytes
+from workloads import CONFIGS
+from workloads.configs import draw_decode_shapes
+
+
+def check_plan(lens, P):
+    plan, info = decode_plan(lens, P, host_only=True)
+    B = len(lens)
+    nw = info.n_work
+    work = plan[:2 * nw].reshape(nw, 2)
+    offs = plan[2 * nw:2 * nw + B]
+    red = plan[2 * nw + B:2 * nw + B + info.n_reduce]
+    parts = [-(-int(L) // P) for L in lens]
+    # every (seq, partition) exactly once
+    want = sorted((i, p) for i in range(B) for p in range(parts[i]))
+    assert sorted(map(tuple, work.tolist())) == want
+    # longest first
+    sizes = [min(P, int(lens[s]) - p * P) for s, p in work.tolist()]
+    nblk = [-(-x // 16) for x in sizes]
+    assert nblk == sorted(nblk, reverse=True)
+    # partial offsets: contiguous ranges for multi-partition sequences only
+    assert list(red) == [i for i in range(B) if parts[i] > 1]
+    pos = 0
+    for i in range(B):
+        if parts[i] > 1:
+            assert offs[i] == pos
+            pos += parts[i]
+        else:
+            assert offs[i] == -1
+    assert info.n_partials == pos and info.plan_ints == 2 * nw + B + info.n_reduce
+    assert info.max_context_len == max(lens)
+    return info
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+@pytest.mark.parametrize("P", [16, 256, 512])
+def test_plan_covers_every_partition_once(cfg, P):
+    sh = draw_decode_shapes(cfg)
+    check_plan(sh.lens, P)
+
+
+def test_plan_edge_cases():
+    info = check_plan(np.array([1, 16, 17, 512, 513]), 256)
+    assert info.n_reduce == 2
+    assert decode_workspace_bytes(info, 8, 128, host_only=True) == info.n_partials * 8 * 130 * 4
+    _, info0 = decode_plan(np.zeros(0, dtype=np.int32), 256, host_only=True)
+    assert info0.n_work == 0
+    with pytest.raises(PkvError):
+        decode_plan(np.array([0]), 256, host_only=True)
+    with pytest.raises(PkvError):
+        decode_plan(np.array([5]), 24, host_only=True)

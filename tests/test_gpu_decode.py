@@ -1,0 +1,149 @@
+"""GPU parity: write_kv, copy_blocks and paged_decode against the oracle.
+
+* every decode workload at its full size: block tables and slots bit-exact,
+  the whole written pool bit-exact, and attention outputs on a seeded sample
+  of sequences (all of them for the tiny workload) within the tolerance the
+  workload states: max |err| <= 1e-5 for fp32 inputs, <= 2e-3 for fp16/bf16
+  (fp32 accumulation, fp32 output);
+* each at the partition size the benchmark uses and at a second one, so both
+  the single-partition and the split-K + reduce paths are compared;
+* masking: pools pre-filled with NaN must not leak into outputs;
+* a sweep over dtypes, head dims 64/128/256, GQA groups 1-8 and ragged
+  lengths around block boundaries (1, 15, 16, 17, ...);
+* copy-on-write block copies bit-exact against the mirrored pool.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_helpers import TOL, DecodeCase, device_bits, host_bits, sync, to_device
+from workloads import CONFIGS, draw_normal_storage
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+# partition sizes: the one the benchmark times first, then another
+PARTITIONS = {"tiny_f32": (0, 16), "gpt_f16": (0, 2048), "ragged_bf16": (0, 512),
+              "gqa_long_bf16": (512, 0)}
+
+
+def sample_seqs(lens, k, seed):
+    lens = np.asarray(lens)
+    if len(lens) <= k:
+        return list(range(len(lens)))
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(len(lens), size=k, replace=False).tolist())
+    pick |= {int(np.argmax(lens)), int(np.argmin(lens))}
+    for v in (60, 200, 1500):
+        pick |= set(np.nonzero(lens == v)[0].tolist())
+    return sorted(pick)
+
+
+def max_err(case, out, seqs):
+    worst = 0.0
+    for i in seqs:
+        worst = max(worst, float(np.max(np.abs(out[i] - case.oracle_out(i)))))
+    return worst
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_workload_parity(cfg):
+    print(f"\n[gpu] workload {cfg.name}", flush=True)
+    case = DecodeCase(cfg)
+    try:
+        t_c, l_c = case.pool.build_batch(case.seqs, case.stride)
+        t_o, l_o = case.oracle.tables(case.stride)
+        assert np.array_equal(t_c, np.asarray(t_o, np.int32))
+        assert np.array_equal(l_c, np.asarray(l_o, np.int32))
+        assert np.array_equal(case.slots, case.oracle.slots)
+        case.write_context()
+        assert np.array_equal(device_bits(case.k_cache), host_bits(case.oracle.mirror.k))
+        assert np.array_equal(device_bits(case.v_cache), host_bits(case.oracle.mirror.v))
+        seqs = sample_seqs(case.lens, 12, cfg.seed)
+        ref = {i: case.oracle_out(i) for i in seqs}
+        for P in PARTITIONS[cfg.name]:
+            out, info = case.decode(P)
+            err = max(float(np.max(np.abs(out[i] - ref[i]))) for i in seqs)
+            print(f"[gpu] {cfg.name} P={info.partition_tokens} work={info.n_work} "
+                  f"reduce={info.n_reduce} max_err={err:.3e}", flush=True)
+            assert err <= TOL[cfg.dtype], (P, err)
+            assert np.isfinite(out).all()
+    finally:
+        case.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_nan_filled_pool_does_not_leak(dtype):
+    cfg = dataclasses.replace(CONFIGS[0], dtype=dtype, index=20, head_dim=128 if dtype != "f32" else 64)
+    lens = [1, 5, 16, 17, 31, 33, 60]
+    order = np.random.default_rng(7).permutation(40)
+    case = DecodeCase(cfg, lens=lens, num_blocks=40, free_order=order, fill=float("nan"))
+    try:
+        case.write_context()
+        for P in (16, 0):
+            out, _ = case.decode(P)
+            assert np.isfinite(out).all()
+            assert max_err(case, out, range(len(lens))) <= TOL[dtype]
+    finally:
+        case.close()
+
+
+SWEEP = [(dt, d, hkv, g) for dt in ("f32", "f16", "bf16") for d in (64, 128, 256)
+         for hkv, g in ((2, 1), (2, 2), (1, 4), (2, 8))]
+
+
+@pytest.mark.parametrize("dtype,head_dim,kv_heads,group", SWEEP)
+def test_shape_sweep(dtype, head_dim, kv_heads, group):
+    idx = 100 + SWEEP.index((dtype, head_dim, kv_heads, group))
+    cfg = dataclasses.replace(CONFIGS[0], name="sweep", index=idx, dtype=dtype, head_dim=head_dim,
+                              num_kv_heads=kv_heads, num_q_heads=kv_heads * group, num_seqs=9)
+    lens = [1, 15, 16, 17, 47, 64, 100, 129, 300]
+    nb = sum(-(-L // 16) for L in lens) + 5
+    order = np.random.default_rng(idx).permutation(nb)
+    case = DecodeCase(cfg, lens=lens, num_blocks=nb, free_order=order)
+    try:
+        case.write_context()
+        for P in (16, 64, 0):
+            out, _ = case.decode(P)
+            err = max_err(case, out, range(len(lens)))
+            assert err <= TOL[dtype], (P, err)
+    finally:
+        case.close()
+
+
+def test_copy_blocks_bit_exact():
+    cfg = dataclasses.replace(CONFIGS[1], index=30, num_seqs=1)
+    nb, H, d = 64, cfg.num_kv_heads, cfg.head_dim
+    case = DecodeCase(cfg, lens=[nb * 16], num_blocks=nb, free_order=np.arange(nb))
+    try:
+        case.write_context()
+        rng = np.random.default_rng(3)
+        blocks = rng.permutation(nb)
+        pairs = np.stack([blocks[:12], blocks[12:24]], axis=1).astype(np.int32)
+        case.pool.copy_blocks(torch.from_numpy(pairs).cuda())
+        sync()
+        case.oracle.mirror.copy_blocks([tuple(p) for p in pairs.tolist()])
+        assert np.array_equal(device_bits(case.k_cache), host_bits(case.oracle.mirror.k))
+        assert np.array_equal(device_bits(case.v_cache), host_bits(case.oracle.mirror.v))
+    finally:
+        case.close()
+
+
+def test_write_kv_skips_negative_and_out_of_pool_slots():
+    cfg = dataclasses.replace(CONFIGS[0], index=31)
+    case = DecodeCase(cfg, lens=[32], num_blocks=4, free_order=np.arange(4))
+    try:
+        case.write_context()
+        k = draw_normal_storage((5, 1), (4, cfg.num_kv_heads, cfg.head_dim), "f32")
+        slots = np.array([3, -1, 64, -7], dtype=np.int64)  # pool holds slots 0..63
+        case.pool.write_kv(to_device(k, "f32"), to_device(k, "f32"), torch.from_numpy(slots).cuda())
+        sync()
+        keep = (slots >= 0) & (slots < 64)
+        case.oracle.mirror.write_kv(k[keep], k[keep], slots[keep])
+        assert np.array_equal(device_bits(case.k_cache), host_bits(case.oracle.mirror.k))
+        assert np.array_equal(device_bits(case.v_cache), host_bits(case.oracle.mirror.v))
+    finally:
+        case.close()
