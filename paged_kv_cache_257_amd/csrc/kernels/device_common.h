@@ -78,21 +78,28 @@ __device__ __forceinline__ float dot16<PKV_F32>(const u32x4& q, const u32x4& k, 
   return acc;
 }
 
+// Vector elements are copied into scalars before __builtin_bit_cast: this
+// compiler mis-lowers a bit_cast whose operand is an element of an
+// ext_vector_type (`q.y`), reading element .x instead.
 template <>
 __device__ __forceinline__ float dot16<PKV_F16>(const u32x4& q, const u32x4& k, float acc) {
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q.x), __builtin_bit_cast(f16x2, k.x), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q.y), __builtin_bit_cast(f16x2, k.y), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q.z), __builtin_bit_cast(f16x2, k.z), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, q.w), __builtin_bit_cast(f16x2, k.w), acc, false);
+  const uint32_t qa[4] = {q.x, q.y, q.z, q.w};
+  const uint32_t ka[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qa[i]), __builtin_bit_cast(f16x2, ka[i]),
+                                 acc, false);
   return acc;
 }
 
 template <>
 __device__ __forceinline__ float dot16<PKV_BF16>(const u32x4& q, const u32x4& k, float acc) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.x), __builtin_bit_cast(bf16x2, k.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.y), __builtin_bit_cast(bf16x2, k.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.z), __builtin_bit_cast(bf16x2, k.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w), __builtin_bit_cast(bf16x2, k.w), acc, false);
+  const uint32_t qa[4] = {q.x, q.y, q.z, q.w};
+  const uint32_t ka[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qa[i]),
+                                          __builtin_bit_cast(bf16x2, ka[i]), acc, false);
   return acc;
 }
 

@@ -3,6 +3,8 @@ one decode workload set up on both the HIP path and the oracle."""
 
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import torch
 
@@ -44,6 +46,8 @@ class DecodeCase:
 
     def __init__(self, cfg, lens=None, num_blocks=None, free_order=None, table_stride=None,
                  fill=0.0, values=None):
+        if lens is not None and cfg.num_seqs != len(lens):
+            cfg = dataclasses.replace(cfg, num_seqs=len(lens))
         self.cfg = cfg
         if lens is None:
             sh = draw_decode_shapes(cfg)
