@@ -14,7 +14,7 @@ using pkv::fail;
 
 namespace {
 
-constexpr int32_t kDefaultPartitionTokens = 256;
+constexpr int32_t kDefaultPartitionTokens = 512;
 
 pkv_status check_lens(const int32_t* lens, int32_t n, int32_t bs, int32_t& P, int32_t& max_len) {
   if (n < 0 || (n > 0 && !lens)) return fail(PKV_E_BAD_ARG, "bad context_lens");

@@ -11,7 +11,7 @@ using pkv::fail;
 namespace {
 
 constexpr int64_t kAlign = 256;
-constexpr int32_t kDefaultPartitionTokens = 256;
+constexpr int32_t kDefaultPartitionTokens = 512;
 
 int64_t align_up(int64_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 

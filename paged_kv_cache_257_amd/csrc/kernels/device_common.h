@@ -31,6 +31,12 @@ inline pkv_status launch_status(const char* what) {
 __device__ __forceinline__ float bits_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t f_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
 
+// 16-byte load of data read once (K/V tiles): the nontemporal hint ("nt")
+// keeps it from displacing reusable lines and streams at a higher rate.
+__device__ __forceinline__ u32x4 load_stream(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // DPP lane move within a row of 16 lanes (all lanes read a valid source for
 // the controls used here, so bound_ctrl and the masks do not matter).
 template <int CTRL>

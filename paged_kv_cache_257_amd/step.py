@@ -41,7 +41,7 @@ class DecodeIteration:
         self.dev = [torch.empty(self.nbytes, dtype=torch.uint8, device=device) for _ in range(2)]
         self.events = [None, None]
         self.turn = 0
-        P_eff = partition_tokens or 256
+        P_eff = partition_tokens or 512
         max_parts = -(-table_stride * bs // P_eff)
         worst = PlanInfo(max_batch, bs, P_eff, 0, 0, max_batch * max_parts, 0, 0)
         ws = decode_workspace_bytes(worst, num_q_heads, pool.desc.head_dim)
