@@ -4,8 +4,12 @@ A step is one decode iteration of the whole path over one batch:
   host   pkv_prepare_decode (C++): append one token to each of the 64
          sequences, take copy-on-write pairs, build block tables, lengths and
          the split-K plan into a pinned staging buffer; one async upload;
-  device copy_blocks (if any pairs), write_kv of the 64 new tokens' K/V,
-         the paged-decode partition kernel, the split-K reduce kernel.
+  device copy_blocks (if any pairs), then one paged-decode launch that stores
+         the 64 new tokens' K/V and attends (split-K partials combined in the
+         same launch); the step's metadata uploads on a side stream while the
+         previous step computes.  The whole step is one native call
+         (pkv_stepper_step); --two-launch / --separate-write / --no-overlap
+         switch fusions off for comparison.
 Inputs (pools, q, the new tokens' K/V) are resident in HBM before timing.
 ``--replicas`` independent copies of the batch (own pools, own allocators)
 are stepped in rotation so that every step reads K/V that the previous
@@ -13,7 +17,7 @@ steps have pushed out of L2 and the 256 MiB Infinity Cache.
 
 Reported (one JSON line):
   value        K/V bytes the steps attended / wall time of the K steps (GB/s);
-  roofline     the partition kernel alone, timed with HIP events on its
+  roofline     the decode launch alone, timed with HIP events on its
                stream: algorithmic K/V bytes per launch / mean duration,
                against the 8 TB/s HBM peak; ``traffic`` from rocprofv3
                FETCH_SIZE + WRITE_SIZE counters when a counter summary for the
@@ -80,6 +84,14 @@ def parse_args(argv=None):
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--two-launch", action="store_true",
+                    help="decode as partition kernel + separate combine kernel (comparison)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="store the new tokens with write_kv instead of inside the decode (comparison)")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="upload each step's metadata on the compute stream (comparison)")
+    ap.add_argument("--time-every", type=int, default=8,
+                    help="record the HIP timing events around every N-th decode launch (events cost GPU time)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args(argv)
@@ -172,7 +184,7 @@ def main(argv=None):
         pool = Pool(nb, H, d, dt, stride, 16, order, kc, vc)
         slots = np.concatenate([pool.alloc(int(L))[1] for L in sh.lens])
         pool.write_kv(k_ctx, v_ctx, torch.from_numpy(slots).cuda())
-        it = DecodeIteration(pool, B, stride, Hq, args.partition)
+        it = DecodeIteration(pool, B, stride, Hq, args.partition, pipelined=not args.no_overlap)
         out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
         reps.append((pool, it, out, kc, vc))
     del k_ctx, v_ctx
@@ -184,12 +196,27 @@ def main(argv=None):
           for _ in range(total)]
     step_bytes, infos = [], []
 
+    native = not (args.two_launch or args.separate_write or args.no_overlap)
+    seqs_np = np.arange(B, dtype=np.int32)
+    ctx_tokens = [int(sh.lens.sum())] * args.replicas  # tokens in each replica before a step
+
     def step(s):
-        pool, it, out, _, _ = reps[s % args.replicas]
-        meta = it.prepare(seqs)
-        it.launch(meta, q_dev, out, new_k[s], new_v[s], cfg.scale, events=ev[s])
-        step_bytes.append(int(meta["host_lens"].astype(np.int64).sum()) * per_tok)
-        infos.append(meta["info"])
+        r = s % args.replicas
+        pool, it, out, _, _ = reps[r]
+        timed_launch = (s % args.time_every) == 0
+        evs = ev[s] if timed_launch else None
+        if native:
+            lay = it.step(seqs_np, q_dev, out, new_k[s], new_v[s], cfg.scale, events=evs)
+            info = lay.plan
+        else:
+            meta = it.prepare(seqs)
+            it.launch(meta, q_dev, out, new_k[s], new_v[s], cfg.scale, events=evs,
+                      fused=not (args.two_launch or args.separate_write),
+                      fused_append=not args.separate_write)
+            info = meta["info"]
+        ctx_tokens[r] += B  # every sequence appended one token and attends over it
+        step_bytes.append(ctx_tokens[r] * per_tok)
+        infos.append(info)
 
     for s in range(args.warmup):
         step(s)
@@ -202,9 +229,10 @@ def main(argv=None):
 
     timed = range(args.warmup, total)
     kbytes = sum(step_bytes[s] for s in timed)
-    kern_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in timed]
+    sampled = [s for s in timed if s % args.time_every == 0]
+    kern_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in sampled]
     mean_kern_s = float(np.mean(kern_ms)) / 1e3
-    mean_bytes = kbytes / args.steps
+    mean_bytes = float(np.mean([step_bytes[s] for s in sampled]))
     achieved = mean_bytes / mean_kern_s / 1e9
     value = kbytes / wall / 1e9
     info = infos[-1]
@@ -226,16 +254,21 @@ def main(argv=None):
                    "head_dim": d, "block_size": 16, "mean_context": round(float(sh.lens.mean()), 1),
                    "max_context": int(sh.lens.max()), "partition_tokens": info.partition_tokens,
                    "work_items": info.n_work, "replicas": args.replicas,
+                   "decode_launches": 2 if args.two_launch else 1,
+                   "new_kv_store": "write_kv" if args.separate_write else "in decode",
+                   "upload": "compute stream" if args.no_overlap else "side stream",
                    "accumulate": "f32", "output": "f32"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(B * args.steps / wall, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "paged_decode_kernel (partition kernel)",
+                     "kernel": "paged_decode_kernel" + (" (partition kernel of two launches)"
+                                                        if args.two_launch else ""),
                      "kernel_ms_mean": round(float(np.mean(kern_ms)), 5),
                      "kernel_ms_p10": round(float(np.percentile(kern_ms, 10)), 5),
                      "kernel_ms_p90": round(float(np.percentile(kern_ms, 90)), 5),
+                     "timed_launches": len(sampled),
                      "algorithmic_bytes_per_launch": int(mean_bytes),
                      "kernel_source_sha": kernel_source_sha()},
     }

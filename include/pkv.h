@@ -192,7 +192,8 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
                            int32_t partition_tokens, int32_t* plan, int32_t cap,
                            pkv_decode_plan_info* info);
 
-/* Device workspace bytes pkv_paged_decode needs for this plan. */
+/* Device workspace bytes pkv_paged_decode needs for this plan: completion
+ * tickets for num_seqs x num_q_heads, then the split-K partials. */
 size_t pkv_decode_workspace_bytes(const pkv_decode_plan_info* info, int32_t num_q_heads,
                                   int32_t head_dim);
 
@@ -236,6 +237,51 @@ pkv_status pkv_prepare_decode(pkv_pool* pool, const int32_t* seqs, int32_t n_seq
                               pkv_batch_layout* layout);
 
 /* ---------------------------------------------------------------------------
+ * One decode iteration in one call (host + device)
+ * ------------------------------------------------------------------------ */
+
+/* A stepper runs continuous-batching decode iterations ([lesson] paragraph 8:
+ * at every iteration the running sequences advance one token) over a pool.
+ * The caller provides PKV_STEPPER_SLOTS staging slots of slot_bytes each, in
+ * pinned host memory (staging_host) and in device memory (staging_dev), the
+ * decode workspace (zeroed before first use, pkv_decode_workspace_bytes for
+ * the largest batch) and a copy stream (NULL: uploads go on the compute
+ * stream).  The stepper creates PKV_STEPPER_SLOTS + 2 HIP events and nothing
+ * else.  The compute stream never waits on another stream; the host waits
+ * for each upload before launching, and for the iterations that last used a
+ * slot before rewriting it (one completion event per group of four slots).
+ * All calls on one stepper must use the same compute stream. */
+#define PKV_STEPPER_SLOTS 8
+typedef struct pkv_stepper pkv_stepper;
+
+size_t pkv_stepper_slot_bytes(int32_t max_seqs, int32_t table_stride, int32_t block_size,
+                              int32_t partition_tokens);
+pkv_status pkv_stepper_create(pkv_pool* pool, int32_t max_seqs, int32_t table_stride,
+                              int32_t num_q_heads, int32_t partition_tokens, void* staging_host,
+                              void* staging_dev, size_t slot_bytes, void* workspace,
+                              size_t workspace_bytes, void* copy_stream, pkv_stepper** out);
+/* Waits for the stepper's own uploads and launches to finish, then frees it. */
+pkv_status pkv_stepper_destroy(pkv_stepper* stepper);
+
+/* One iteration over seqs[0..n_seqs):
+ *   host    pkv_prepare_decode (append one token to each sequence, take the
+ *           copy-on-write pairs, tables, lengths, split-K plan) into the next
+ *           staging slot; all or nothing, the pool is unchanged on error;
+ *   upload  one async copy of the slot on the copy stream;
+ *   stream  wait for that upload, pkv_copy_blocks for the pairs, then
+ *           pkv_paged_decode with k_new/v_new (the appended tokens' rows,
+ *           [n_seqs][num_kv_heads][head_dim]) stored and attended.
+ * The host may run up to PKV_STEPPER_SLOTS iterations ahead of the device.
+ * ev_before / ev_after: optional hipEvent_t recorded on `stream` around the
+ * decode launch.  layout_out / slot_out (optional) receive the iteration's
+ * staging layout and slot index (the host slot stays readable until the slot
+ * comes round again, PKV_STEPPER_SLOTS iterations later). */
+pkv_status pkv_stepper_step(pkv_stepper* stepper, const int32_t* seqs, int32_t n_seqs,
+                            const void* q, const void* k_new, const void* v_new, float* out,
+                            float scale, void* stream, void* ev_before, void* ev_after,
+                            pkv_batch_layout* layout_out, int32_t* slot_out);
+
+/* ---------------------------------------------------------------------------
  * Device (HIP, gfx950): asynchronous on `stream`
  * ------------------------------------------------------------------------ */
 
@@ -261,34 +307,50 @@ pkv_status pkv_write_kv(const pkv_pool* pool, const void* k_new, const void* v_n
  * g = h / (num_q_heads / num_kv_heads).  Paging does not change the result of
  * dense attention ([preview] "Lo que deberías llevarte", item 2).
  *   q:            device [num_seqs][num_q_heads][head_dim], pool dtype
+ *   k_new, v_new: device [num_seqs][num_kv_heads][head_dim], pool dtype, or
+ *                 both NULL.  When given, they are the K/V rows of each
+ *                 sequence's newest token (position context_lens[i] - 1, the
+ *                 token just appended, [preview] step 3): the kernel stores
+ *                 them into the pool at that position and attends over them,
+ *                 i.e. pkv_write_kv and decode in one launch.  Copy-on-write
+ *                 copies of the same iteration must be enqueued before.
  *   out:          device float32 [num_seqs][num_q_heads][head_dim]
  *   block_tables: device int32 [num_seqs][table_stride]
  *   context_lens: device int32 [num_seqs]; every entry >= 1 and equal to the
  *                 lengths given to pkv_decode_plan
  *   plan, info:   device copy of the plan and its host-side info
- *   workspace:    device, >= pkv_decode_workspace_bytes(info, ...) bytes
+ *   workspace:    device, >= pkv_decode_workspace_bytes(info, ...) bytes.  Its
+ *                 first bytes hold completion tickets: they must be zero
+ *                 before the first call (allocate it zeroed) and every call
+ *                 leaves them zero.  Calls that share a workspace must not
+ *                 overlap in time.
+ * One kernel launch: multi-partition sequences are combined by the last
+ * workgroup of each sequence and head group to finish.
  * Arithmetic: fp32 accumulation and an online (running max) softmax; the
  * output is float32.  Table entries outside the pool read nothing. */
-pkv_status pkv_paged_decode(const pkv_pool* pool, const void* q, float* out, int32_t num_seqs,
-                            int32_t num_q_heads, const int32_t* block_tables,
-                            int32_t table_stride, const int32_t* context_lens, float scale,
-                            const int32_t* plan, const pkv_decode_plan_info* info,
-                            void* workspace, size_t workspace_bytes, void* stream);
+pkv_status pkv_paged_decode(const pkv_pool* pool, const void* q, const void* k_new,
+                            const void* v_new, float* out, int32_t num_seqs, int32_t num_q_heads,
+                            const int32_t* block_tables, int32_t table_stride,
+                            const int32_t* context_lens, float scale, const int32_t* plan,
+                            const pkv_decode_plan_info* info, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
-/* The two halves of pkv_paged_decode, same arguments, for callers that want
- * to time or schedule them apart: the partition kernel (writes out for
- * single-partition sequences, partials to the workspace otherwise), then the
- * combine of the partials.  pkv_paged_decode = partitions + reduce. */
-pkv_status pkv_paged_decode_partitions(const pkv_pool* pool, const void* q, float* out,
-                                       int32_t num_seqs, int32_t num_q_heads,
-                                       const int32_t* block_tables, int32_t table_stride,
-                                       const int32_t* context_lens, float scale,
-                                       const int32_t* plan, const pkv_decode_plan_info* info,
-                                       void* workspace, size_t workspace_bytes, void* stream);
-pkv_status pkv_paged_decode_reduce(const pkv_pool* pool, const void* q, float* out,
-                                   int32_t num_seqs, int32_t num_q_heads,
-                                   const int32_t* block_tables, int32_t table_stride,
-                                   const int32_t* context_lens, float scale,
+/* The same decode as two launches, same arguments: the partition kernel
+ * (writes out for single-partition sequences, partials to the workspace
+ * otherwise; stores k_new/v_new like pkv_paged_decode), then a separate kernel
+ * that combines the partials.  Kept for comparison and for callers that want
+ * to schedule the combine apart. */
+pkv_status pkv_paged_decode_partitions(const pkv_pool* pool, const void* q, const void* k_new,
+                                       const void* v_new, float* out, int32_t num_seqs,
+                                       int32_t num_q_heads, const int32_t* block_tables,
+                                       int32_t table_stride, const int32_t* context_lens,
+                                       float scale, const int32_t* plan,
+                                       const pkv_decode_plan_info* info, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+pkv_status pkv_paged_decode_reduce(const pkv_pool* pool, const void* q, const void* k_new,
+                                   const void* v_new, float* out, int32_t num_seqs,
+                                   int32_t num_q_heads, const int32_t* block_tables,
+                                   int32_t table_stride, const int32_t* context_lens, float scale,
                                    const int32_t* plan, const pkv_decode_plan_info* info,
                                    void* workspace, size_t workspace_bytes, void* stream);
 

@@ -56,6 +56,11 @@ I32 = C.c_int32
 PI32 = C.POINTER(C.c_int32)
 PI64 = C.POINTER(C.c_int64)
 
+# pool, q, k_new, v_new, out, num_seqs, num_q_heads, tables, stride, lens, scale,
+# plan, info, workspace, workspace_bytes, stream
+DECODE_ARGS = [P, P, P, P, P, I32, I32, P, I32, P, C.c_float, P, C.POINTER(PlanInfo), P,
+               C.c_size_t, P]
+
 # name -> (argtypes); every function returns pkv_status (int) unless listed
 SIGNATURES = {
     "pkv_pool_create": [C.POINTER(PoolDesc), P, P, PI32, C.POINTER(P)],
@@ -80,20 +85,23 @@ SIGNATURES = {
     "pkv_decode_workspace_bytes": [C.POINTER(PlanInfo), I32, I32],
     "pkv_prepare_decode_bytes": [I32, I32, I32, I32, I32],
     "pkv_prepare_decode": [P, PI32, I32, I32, I32, I32, P, C.c_size_t, C.POINTER(BatchLayout)],
+    "pkv_stepper_slot_bytes": [I32, I32, I32, I32],
+    "pkv_stepper_create": [P, I32, I32, I32, I32, P, P, C.c_size_t, P, C.c_size_t, P, C.POINTER(P)],
+    "pkv_stepper_destroy": [P],
+    "pkv_stepper_step": [P, PI32, I32, P, P, P, P, C.c_float, P, P, P, C.POINTER(BatchLayout),
+                         PI32],
     "pkv_copy_blocks": [P, P, I32, P],
     "pkv_write_kv": [P, P, P, P, I32, P],
-    "pkv_paged_decode": [P, P, P, I32, I32, P, I32, P, C.c_float, P, C.POINTER(PlanInfo), P,
-                         C.c_size_t, P],
-    "pkv_paged_decode_partitions": [P, P, P, I32, I32, P, I32, P, C.c_float, P,
-                                    C.POINTER(PlanInfo), P, C.c_size_t, P],
-    "pkv_paged_decode_reduce": [P, P, P, I32, I32, P, I32, P, C.c_float, P, C.POINTER(PlanInfo),
-                                P, C.c_size_t, P],
+    "pkv_paged_decode": DECODE_ARGS,
+    "pkv_paged_decode_partitions": DECODE_ARGS,
+    "pkv_paged_decode_reduce": DECODE_ARGS,
     "pkv_last_error": [],
 }
 RESTYPES = {"pkv_last_error": C.c_char_p, "pkv_decode_workspace_bytes": C.c_size_t,
-            "pkv_prepare_decode_bytes": C.c_size_t}
+            "pkv_prepare_decode_bytes": C.c_size_t, "pkv_stepper_slot_bytes": C.c_size_t}
 DEVICE_FUNCS = ("pkv_copy_blocks", "pkv_write_kv", "pkv_paged_decode", "pkv_paged_decode_partitions",
-                "pkv_paged_decode_reduce")
+                "pkv_paged_decode_reduce", "pkv_stepper_slot_bytes", "pkv_stepper_create",
+                "pkv_stepper_destroy", "pkv_stepper_step")
 
 _LIBS = {}
 

@@ -28,7 +28,7 @@ CXX = os.environ.get("CXX", "g++")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["host/pool.cpp", "host/plan.cpp", "host/prepare.cpp"]
-HIP_SOURCES = ["kernels/kv_write.hip", "kernels/paged_decode.hip"]
+HIP_SOURCES = ["kernels/kv_write.hip", "kernels/paged_decode.hip", "kernels/stepper.cpp"]
 
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

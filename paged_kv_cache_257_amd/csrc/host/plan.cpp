@@ -14,7 +14,7 @@ using pkv::fail;
 
 namespace {
 
-constexpr int32_t kDefaultPartitionTokens = 512;
+constexpr int32_t kDefaultPartitionTokens = 1024;
 
 pkv_status check_lens(const int32_t* lens, int32_t n, int32_t bs, int32_t& P, int32_t& max_len) {
   if (n < 0 || (n > 0 && !lens)) return fail(PKV_E_BAD_ARG, "bad context_lens");
@@ -32,6 +32,27 @@ pkv_status check_lens(const int32_t* lens, int32_t n, int32_t bs, int32_t& P, in
 
 }  // namespace
 
+namespace {
+
+struct PlanCounts {
+  int64_t work = 0, reduce = 0, partials = 0;
+};
+
+PlanCounts count_plan(const int32_t* lens, int32_t n, int32_t P) {
+  PlanCounts c;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t parts = (int64_t(lens[i]) + P - 1) / P;
+    c.work += parts;
+    if (parts > 1) {
+      c.reduce++;
+      c.partials += parts;
+    }
+  }
+  return c;
+}
+
+}  // namespace
+
 extern "C" {
 
 pkv_status pkv_decode_plan_ints(const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
@@ -39,13 +60,8 @@ pkv_status pkv_decode_plan_ints(const int32_t* context_lens, int32_t num_seqs, i
   if (!plan_ints) return fail(PKV_E_BAD_ARG, "null plan_ints");
   int32_t P = partition_tokens, max_len = 0;
   if (pkv_status st = check_lens(context_lens, num_seqs, block_size, P, max_len)) return st;
-  int64_t work = 0, reduce = 0;
-  for (int32_t i = 0; i < num_seqs; ++i) {
-    int64_t parts = (int64_t(context_lens[i]) + P - 1) / P;
-    work += parts;
-    reduce += parts > 1;
-  }
-  int64_t total = 2 * work + num_seqs + reduce;
+  const PlanCounts c = count_plan(context_lens, num_seqs, P);
+  const int64_t total = 2 * c.work + num_seqs + c.reduce;
   if (total > INT32_MAX) return fail(PKV_E_BAD_ARG, "plan too large");
   *plan_ints = int32_t(total);
   return PKV_OK;
@@ -55,46 +71,53 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
                            int32_t partition_tokens, int32_t* plan, int32_t cap,
                            pkv_decode_plan_info* info) {
   if (!info) return fail(PKV_E_BAD_ARG, "null info");
-  int32_t need = 0;
-  if (pkv_status st = pkv_decode_plan_ints(context_lens, num_seqs, block_size, partition_tokens, &need))
-    return st;
-  if (cap < need || (need > 0 && !plan)) return fail(PKV_E_BAD_ARG, "plan buffer too small");
   int32_t P = partition_tokens, max_len = 0;
-  check_lens(context_lens, num_seqs, block_size, P, max_len);
+  if (pkv_status st = check_lens(context_lens, num_seqs, block_size, P, max_len)) return st;
+  const PlanCounts c = count_plan(context_lens, num_seqs, P);
+  const int64_t need = 2 * c.work + num_seqs + c.reduce;
+  if (need > INT32_MAX) return fail(PKV_E_BAD_ARG, "plan too large");
+  if (cap < need || (need > 0 && !plan)) return fail(PKV_E_BAD_ARG, "plan buffer too small");
   const int32_t pblocks = P / block_size;
+  const int32_t n_work = int32_t(c.work);
+  int32_t* part_offset = plan + 2 * int64_t(n_work);
+  int32_t* reduce = part_offset + num_seqs;
 
-  // work items bucketed by their block count (counting sort, longest first,
-  // ties in (sequence, partition) order)
-  std::vector<std::vector<std::pair<int32_t, int32_t>>> by_len(pblocks + 1);
-  int32_t n_work = 0, n_reduce = 0, n_partials = 0;
-  int32_t* part_offset = plan;  // filled after the work list is laid out
-  std::vector<int32_t> offsets(num_seqs, -1), reduce;
+  // Counting sort of the work items by their block count, longest first;
+  // ties keep (sequence, partition) order.  Scratch is reused across calls.
+  thread_local std::vector<int32_t> start;
+  start.assign(size_t(pblocks) + 2, 0);
+  int32_t n_reduce = 0, n_partials = 0;
   for (int32_t i = 0; i < num_seqs; ++i) {
-    const int32_t L = context_lens[i];
-    const int32_t nblk = (L + block_size - 1) / block_size;
-    const int32_t parts = (L + P - 1) / P;
-    for (int32_t p = 0; p < parts; ++p) {
-      int32_t blocks = std::min(pblocks, nblk - p * pblocks);
-      by_len[blocks].emplace_back(i, p);
-    }
-    n_work += parts;
+    const int32_t nblk = (context_lens[i] + block_size - 1) / block_size;
+    const int32_t parts = (nblk + pblocks - 1) / pblocks;
+    const int32_t last = nblk - (parts - 1) * pblocks;  // blocks of the last partition
+    start[pblocks] += parts - 1;
+    start[last] += 1;
     if (parts > 1) {
-      offsets[i] = n_partials;
+      part_offset[i] = n_partials;
       n_partials += parts;
-      reduce.push_back(i);
-      n_reduce++;
+      reduce[n_reduce++] = i;
+    } else {
+      part_offset[i] = -1;
     }
   }
-  int32_t w = 0;
-  for (int32_t b = pblocks; b >= 1; --b)
-    for (const auto& it : by_len[b]) {
-      plan[2 * w] = it.first;
-      plan[2 * w + 1] = it.second;
-      w++;
+  // bucket b starts after all buckets with more blocks
+  int32_t pos = 0;
+  for (int32_t b = pblocks; b >= 1; --b) {
+    const int32_t cnt = start[b];
+    start[b] = pos;
+    pos += cnt;
+  }
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t nblk = (context_lens[i] + block_size - 1) / block_size;
+    const int32_t parts = (nblk + pblocks - 1) / pblocks;
+    for (int32_t q = 0; q < parts; ++q) {
+      const int32_t b = q + 1 < parts ? pblocks : nblk - q * pblocks;
+      const int32_t w = start[b]++;
+      plan[2 * w] = i;
+      plan[2 * w + 1] = q;
     }
-  part_offset = plan + 2 * n_work;
-  std::copy(offsets.begin(), offsets.end(), part_offset);
-  std::copy(reduce.begin(), reduce.end(), part_offset + num_seqs);
+  }
 
   info->num_seqs = num_seqs;
   info->block_size = block_size;
@@ -102,7 +125,7 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
   info->n_work = n_work;
   info->n_reduce = n_reduce;
   info->n_partials = n_partials;
-  info->plan_ints = need;
+  info->plan_ints = int32_t(need);
   info->max_context_len = max_len;
   return PKV_OK;
 }
@@ -110,8 +133,12 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
 size_t pkv_decode_workspace_bytes(const pkv_decode_plan_info* info, int32_t num_q_heads,
                                   int32_t head_dim) {
   if (!info || num_q_heads < 1 || head_dim < 1) return 0;
-  // partial o (head_dim floats) + (m, l) per (partial, query head)
-  return size_t(info->n_partials) * size_t(num_q_heads) * (size_t(head_dim) + 2) * sizeof(float);
+  // completion tickets [num_seqs][H_q] int32 (256-byte aligned), then one
+  // record per (partial, query head): o[head_dim], m, l, padded to whole
+  // 128-byte cache lines so that no two workgroups write the same line
+  const size_t tickets = (size_t(info->num_seqs) * size_t(num_q_heads) * 4 + 255) / 256 * 256;
+  const size_t record = ((size_t(head_dim) + 2) * sizeof(float) + 127) / 128 * 128;
+  return tickets + size_t(info->n_partials) * size_t(num_q_heads) * record;
 }
 
 }  // extern "C"

@@ -20,7 +20,6 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
-#include <unordered_map>
 
 #include "pool_internal.h"
 
@@ -44,6 +43,8 @@ using pkv::fail;
 extern "C" const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
 namespace {
+
+using pkv::find_seq;
 
 int64_t blocks_for(int64_t tokens, int32_t bs) { return (tokens + bs - 1) / bs; }
 
@@ -80,43 +81,68 @@ int64_t append_token(pkv_pool* p, pkv_seq_state& s) {
 
 // Dry run of appending n tokens to a sequence of (table size, length, last
 // block) as the current state would do it.  `avail` is the free-block count
-// still available to this call; `cow_taken` counts references of shared last
-// blocks already given up earlier in the same call.
-pkv_status dry_append(const pkv_pool* p, size_t table_size, int32_t length, int32_t last_block,
-                      int32_t n, int64_t& avail,
-                      std::unordered_map<int32_t, int32_t>& cow_taken) {
+// still available to this call; p->rc_taken counts references of shared last
+// blocks already given up earlier in the same call (p->rc_touched lists the
+// entries to clear afterwards).
+pkv_status dry_append(pkv_pool* p, size_t table_size, int32_t length, int32_t last_block, int32_t n,
+                      int64_t& avail) {
   const int32_t bs = p->desc.block_size;
   if (n == 0) return PKV_OK;
   if (length % bs != 0) {
-    int32_t eff = p->rc[last_block] - cow_taken[last_block];
-    if (eff > 1) {
+    int32_t& taken = p->rc_taken[last_block];
+    if (p->rc[last_block] - taken > 1) {
       if (avail == 0) return fail(PKV_E_NO_BLOCKS, "no free block for copy-on-write");
       avail--;
-      cow_taken[last_block]++;
+      if (taken++ == 0) p->rc_touched.push_back(last_block);
     }
   }
-  // new blocks opened at positions that start a block
-  int64_t opened = blocks_for(int64_t(length) + n, bs) - blocks_for(length, bs);
-  int64_t table_after = int64_t(table_size) + opened;
-  // The token-by-token order matters for which error is reported first: a
-  // boundary checks table capacity, then free blocks.
+  // new blocks opened at positions that start a block; the token-by-token
+  // order decides which error comes first: a boundary checks table capacity,
+  // then free blocks
+  const int64_t opened = blocks_for(int64_t(length) + n, bs) - blocks_for(length, bs);
   if (opened > 0) {
-    int64_t room = p->desc.max_blocks_per_seq - int64_t(table_size);
-    int64_t can = std::min<int64_t>(room, avail);
+    const int64_t room = p->desc.max_blocks_per_seq - int64_t(table_size);
+    const int64_t can = std::min<int64_t>(room, avail);
     if (can < opened) {
       if (room <= avail) return fail(PKV_E_TABLE_FULL, "block table is full");
       return fail(PKV_E_NO_BLOCKS, "no free block");
     }
     avail -= opened;
   }
-  (void)table_after;
   return PKV_OK;
+}
+
+void clear_dry_run(pkv_pool* p) {
+  for (int32_t b : p->rc_touched) p->rc_taken[b] = 0;
+  p->rc_touched.clear();
 }
 
 pkv_status check_pool(const pkv_pool* p) {
   if (!p) return fail(PKV_E_BAD_ARG, "null pool");
   return PKV_OK;
 }
+
+// A new live sequence with the next id; returns its state.
+pkv_seq_state& new_seq(pkv_pool* p) {
+  int32_t slot;
+  if (!p->free_slots.empty()) {
+    slot = p->free_slots.back();
+    p->free_slots.pop_back();
+  } else {
+    slot = int32_t(p->slots.size());
+    p->slots.emplace_back();
+  }
+  pkv_seq_state& s = p->slots[slot];
+  s.id = p->next_id++;
+  s.length = 0;
+  s.table.clear();
+  s.mark = 0;
+  p->index.insert(s.id, slot);
+  p->live++;
+  return s;
+}
+
+std::string unknown(int32_t id) { return "unknown sequence " + std::to_string(id); }
 
 }  // namespace
 
@@ -152,6 +178,7 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, void* k_cache, void* v_cac
   p->k_cache = k_cache;
   p->v_cache = v_cache;
   p->initial_order = std::move(order);
+  p->rc_taken.assign(d.num_blocks, 0);
   pkv_pool_reset(p);
   *out = p;
   return PKV_OK;
@@ -166,7 +193,10 @@ pkv_status pkv_pool_reset(pkv_pool* p) {
   if (pkv_status st = check_pool(p)) return st;
   p->free_stack.assign(p->initial_order.rbegin(), p->initial_order.rend());
   p->rc.assign(p->desc.num_blocks, 0);
-  p->seqs.clear();
+  p->slots.clear();
+  p->free_slots.clear();
+  p->index.clear();
+  p->live = 0;
   p->next_id = 0;
   p->cow_pending.clear();
   p->alloc_failures = p->cow_copies = p->forks = 0;
@@ -184,19 +214,19 @@ pkv_status pkv_seq_alloc(pkv_pool* p, int32_t n_tokens, int32_t* seq, int64_t* s
   if (pkv_status st = check_pool(p)) return st;
   if (!seq || n_tokens < 0) return fail(PKV_E_BAD_ARG, "null seq or negative token count");
   int64_t avail = int64_t(p->free_stack.size());
-  std::unordered_map<int32_t, int32_t> taken;
-  pkv_status st = dry_append(p, 0, 0, -1, n_tokens, avail, taken);
+  pkv_status st = dry_append(p, 0, 0, -1, n_tokens, avail);
+  clear_dry_run(p);
   if (st != PKV_OK) {
     if (st == PKV_E_NO_BLOCKS) p->alloc_failures++;
     return st;
   }
-  int32_t id = p->next_id++;
-  pkv_seq_state& s = p->seqs[id];
+  pkv_seq_state& s = new_seq(p);
+  s.table.reserve(size_t(blocks_for(n_tokens, p->desc.block_size)));
   for (int32_t t = 0; t < n_tokens; ++t) {
     int64_t slot = append_token(p, s);
     if (slots) slots[t] = slot;
   }
-  *seq = id;
+  *seq = s.id;
   return PKV_OK;
 }
 
@@ -205,27 +235,42 @@ pkv_status pkv_seq_append_batch(pkv_pool* p, const int32_t* seqs, int32_t n_seqs
   if (pkv_status st = check_pool(p)) return st;
   if (n_seqs < 0 || n_tokens < 0 || (n_seqs > 0 && !seqs))
     return fail(PKV_E_BAD_ARG, "bad batch arguments");
-  {
+  // duplicates: mark every live sequence with this call's epoch; ids that
+  // are not live (the call fails anyway) are checked by sorting
+  const uint64_t epoch = ++p->epoch;
+  bool any_unknown = false;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    pkv_seq_state* s = find_seq(p, seqs[i]);
+    if (!s) {
+      any_unknown = true;
+    } else {
+      if (s->mark == epoch) return fail(PKV_E_BAD_ARG, "duplicate sequence in batch");
+      s->mark = epoch;
+    }
+  }
+  if (any_unknown) {
     std::vector<int32_t> sorted(seqs, seqs + n_seqs);
     std::sort(sorted.begin(), sorted.end());
     if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
       return fail(PKV_E_BAD_ARG, "duplicate sequence in batch");
   }
   int64_t avail = int64_t(p->free_stack.size());
-  std::unordered_map<int32_t, int32_t> taken;
   for (int32_t i = 0; i < n_seqs; ++i) {
-    auto it = p->seqs.find(seqs[i]);
-    if (it == p->seqs.end()) return fail(PKV_E_BAD_SEQ, "unknown sequence " + std::to_string(seqs[i]));
-    const pkv_seq_state& s = it->second;
-    int32_t last = s.table.empty() ? -1 : s.table.back();
-    pkv_status st = dry_append(p, s.table.size(), s.length, last, n_tokens, avail, taken);
+    const pkv_seq_state* s = find_seq(p, seqs[i]);
+    pkv_status st = s ? PKV_OK : fail(PKV_E_BAD_SEQ, unknown(seqs[i]));
+    if (st == PKV_OK) {
+      const int32_t last = s->table.empty() ? -1 : s->table.back();
+      st = dry_append(p, s->table.size(), s->length, last, n_tokens, avail);
+    }
     if (st != PKV_OK) {
+      clear_dry_run(p);
       if (st == PKV_E_NO_BLOCKS) p->alloc_failures++;
       return st;
     }
   }
+  clear_dry_run(p);
   for (int32_t i = 0; i < n_seqs; ++i) {
-    pkv_seq_state& s = p->seqs[seqs[i]];
+    pkv_seq_state& s = *find_seq(p, seqs[i]);
     for (int32_t t = 0; t < n_tokens; ++t) {
       int64_t slot = append_token(p, s);
       if (slots) slots[int64_t(i) * n_tokens + t] = slot;
@@ -241,42 +286,46 @@ pkv_status pkv_seq_append(pkv_pool* p, int32_t seq, int32_t n_tokens, int64_t* s
 pkv_status pkv_seq_fork(pkv_pool* p, int32_t parent, int32_t* child) {
   if (pkv_status st = check_pool(p)) return st;
   if (!child) return fail(PKV_E_BAD_ARG, "null child");
-  auto it = p->seqs.find(parent);
-  if (it == p->seqs.end()) return fail(PKV_E_BAD_SEQ, "unknown sequence " + std::to_string(parent));
-  pkv_seq_state copy = it->second;
-  for (int32_t b : copy.table) p->rc[b]++;
-  int32_t id = p->next_id++;
-  p->seqs.emplace(id, std::move(copy));
+  if (!find_seq(p, parent)) return fail(PKV_E_BAD_SEQ, unknown(parent));
+  pkv_seq_state& c = new_seq(p);  // may move `slots`: look the parent up again
+  const pkv_seq_state& par = *find_seq(p, parent);
+  c.table = par.table;
+  c.length = par.length;
+  for (int32_t b : c.table) p->rc[b]++;
   p->forks++;
-  *child = id;
+  *child = c.id;
   return PKV_OK;
 }
 
 pkv_status pkv_seq_free(pkv_pool* p, int32_t seq) {
   if (pkv_status st = check_pool(p)) return st;
-  auto it = p->seqs.find(seq);
-  if (it == p->seqs.end()) return fail(PKV_E_BAD_SEQ, "unknown sequence " + std::to_string(seq));
-  std::vector<int32_t> table = std::move(it->second.table);
-  p->seqs.erase(it);
-  for (int32_t b : table) release_block(p, b);
+  const int32_t slot = p->index.find(seq);
+  if (slot < 0) return fail(PKV_E_BAD_SEQ, unknown(seq));
+  pkv_seq_state& s = p->slots[slot];
+  for (int32_t b : s.table) release_block(p, b);
+  s.table.clear();
+  s.id = -1;
+  p->index.erase(seq);
+  p->free_slots.push_back(slot);
+  p->live--;
   return PKV_OK;
 }
 
 pkv_status pkv_seq_length(const pkv_pool* p, int32_t seq, int32_t* length) {
   if (pkv_status st = check_pool(p)) return st;
   if (!length) return fail(PKV_E_BAD_ARG, "null length");
-  auto it = p->seqs.find(seq);
-  if (it == p->seqs.end()) return fail(PKV_E_BAD_SEQ, "unknown sequence " + std::to_string(seq));
-  *length = it->second.length;
+  const pkv_seq_state* s = find_seq(p, seq);
+  if (!s) return fail(PKV_E_BAD_SEQ, unknown(seq));
+  *length = s->length;
   return PKV_OK;
 }
 
 pkv_status pkv_seq_table(const pkv_pool* p, int32_t seq, int32_t* table, int32_t cap, int32_t* n) {
   if (pkv_status st = check_pool(p)) return st;
   if (!n || cap < 0 || (cap > 0 && !table)) return fail(PKV_E_BAD_ARG, "bad table buffer");
-  auto it = p->seqs.find(seq);
-  if (it == p->seqs.end()) return fail(PKV_E_BAD_SEQ, "unknown sequence " + std::to_string(seq));
-  const auto& t = it->second.table;
+  const pkv_seq_state* s = find_seq(p, seq);
+  if (!s) return fail(PKV_E_BAD_SEQ, unknown(seq));
+  const auto& t = s->table;
   *n = int32_t(t.size());
   if (int64_t(t.size()) > cap) return fail(PKV_E_BAD_ARG, "table buffer too small");
   std::copy(t.begin(), t.end(), table);
@@ -286,10 +335,12 @@ pkv_status pkv_seq_table(const pkv_pool* p, int32_t seq, int32_t* table, int32_t
 pkv_status pkv_live_seqs(const pkv_pool* p, int32_t* ids, int32_t cap, int32_t* n) {
   if (pkv_status st = check_pool(p)) return st;
   if (!n || cap < 0 || (cap > 0 && !ids)) return fail(PKV_E_BAD_ARG, "bad id buffer");
-  *n = int32_t(p->seqs.size());
-  if (int64_t(p->seqs.size()) > cap) return fail(PKV_E_BAD_ARG, "id buffer too small");
+  *n = p->live;
+  if (p->live > cap) return fail(PKV_E_BAD_ARG, "id buffer too small");
   int32_t i = 0;
-  for (const auto& kv : p->seqs) ids[i++] = kv.first;
+  for (const pkv_seq_state& s : p->slots)
+    if (s.id >= 0) ids[i++] = s.id;
+  std::sort(ids, ids + i);
   return PKV_OK;
 }
 
@@ -317,12 +368,12 @@ pkv_status pkv_stats(const pkv_pool* p, pkv_stats_t* out) {
   s.used_blocks = p->desc.num_blocks - s.free_blocks;
   s.alloc_failures = p->alloc_failures;
   const int32_t bs = p->desc.block_size;
-  for (const auto& kv : p->seqs)
-    s.tail_waste_slots += int64_t(bs) * int64_t(kv.second.table.size()) - kv.second.length;
+  for (const pkv_seq_state& q : p->slots)
+    if (q.id >= 0) s.tail_waste_slots += int64_t(bs) * int64_t(q.table.size()) - q.length;
   for (int32_t r : p->rc) s.shared_blocks += (r > 1);
   s.cow_copies = p->cow_copies;
   s.forks = p->forks;
-  s.live_seqs = int64_t(p->seqs.size());
+  s.live_seqs = p->live;
   *out = s;
   return PKV_OK;
 }
@@ -346,13 +397,13 @@ pkv_status pkv_build_batch(const pkv_pool* p, const int32_t* seqs, int32_t n_seq
   if (n_seqs < 0 || table_stride < 1 || (n_seqs > 0 && (!seqs || !block_tables || !context_lens)))
     return fail(PKV_E_BAD_ARG, "bad batch arguments");
   for (int32_t i = 0; i < n_seqs; ++i) {
-    auto it = p->seqs.find(seqs[i]);
-    if (it == p->seqs.end()) return fail(PKV_E_BAD_SEQ, "unknown sequence " + std::to_string(seqs[i]));
-    if (int64_t(it->second.table.size()) > table_stride)
+    const pkv_seq_state* s = find_seq(p, seqs[i]);
+    if (!s) return fail(PKV_E_BAD_SEQ, unknown(seqs[i]));
+    if (int64_t(s->table.size()) > table_stride)
       return fail(PKV_E_BAD_ARG, "a table is wider than table_stride");
   }
   for (int32_t i = 0; i < n_seqs; ++i) {
-    const pkv_seq_state& s = p->seqs.find(seqs[i])->second;
+    const pkv_seq_state& s = *find_seq(p, seqs[i]);
     int32_t* row = block_tables + int64_t(i) * table_stride;
     std::copy(s.table.begin(), s.table.end(), row);
     std::fill(row + s.table.size(), row + table_stride, -1);

@@ -3,7 +3,6 @@
 #pragma once
 
 #include <cstdint>
-#include <map>
 #include <string>
 #include <utility>
 #include <vector>
@@ -13,7 +12,68 @@
 struct pkv_seq_state {
   std::vector<int32_t> table;  // physical block of each logical block
   int32_t length = 0;          // tokens stored
+  int32_t id = -1;             // -1: the slot is free
+  uint64_t mark = 0;           // batch epoch that last touched the sequence
 };
+
+namespace pkv {
+
+// Open-addressing map from sequence id to slot index (linear probing,
+// power-of-two capacity, tombstones on erase).  Lookups touch one or two
+// cache lines; no allocation except when the table grows.
+class SeqIndex {
+ public:
+  int32_t find(int32_t id) const {
+    if (cap_ == 0) return -1;
+    for (uint32_t i = hash(id);; i = (i + 1) & (cap_ - 1)) {
+      const Entry& e = e_[i];
+      if (e.key == id) return e.val;
+      if (e.key == kEmpty) return -1;
+    }
+  }
+  void insert(int32_t id, int32_t slot) {
+    if ((size_ + tombs_ + 1) * 2 > cap_) rehash(cap_ == 0 ? 64 : (size_ + 1) * 4 > cap_ ? cap_ * 2 : cap_);
+    uint32_t i = hash(id);
+    while (e_[i].key != kEmpty && e_[i].key != kTomb) i = (i + 1) & (cap_ - 1);
+    if (e_[i].key == kTomb) tombs_--;
+    e_[i] = {id, slot};
+    size_++;
+  }
+  void erase(int32_t id) {
+    for (uint32_t i = hash(id);; i = (i + 1) & (cap_ - 1)) {
+      if (e_[i].key == id) {
+        e_[i].key = kTomb;
+        size_--;
+        tombs_++;
+        return;
+      }
+      if (e_[i].key == kEmpty) return;
+    }
+  }
+  void clear() {
+    e_.assign(e_.size(), Entry{kEmpty, 0});
+    size_ = tombs_ = 0;
+  }
+
+ private:
+  static constexpr int32_t kEmpty = -1, kTomb = -2;
+  struct Entry {
+    int32_t key, val;
+  };
+  uint32_t hash(int32_t id) const { return (uint32_t(id) * 2654435761u) & (cap_ - 1); }
+  void rehash(uint32_t cap) {
+    std::vector<Entry> old(std::move(e_));
+    e_.assign(cap, Entry{kEmpty, 0});
+    cap_ = cap;
+    size_ = tombs_ = 0;
+    for (const Entry& e : old)
+      if (e.key >= 0) insert(e.key, e.val);
+  }
+  std::vector<Entry> e_;
+  uint32_t cap_ = 0, size_ = 0, tombs_ = 0;
+};
+
+}  // namespace pkv
 
 struct pkv_pool {
   pkv_pool_desc desc{};
@@ -22,9 +82,15 @@ struct pkv_pool {
   std::vector<int32_t> initial_order;        // free_order as given
   std::vector<int32_t> free_stack;           // back() is handed out next
   std::vector<int32_t> rc;                   // reference count per block
-  std::map<int32_t, pkv_seq_state> seqs;     // ordered by id
+  std::vector<pkv_seq_state> slots;          // sequence states, recycled
+  std::vector<int32_t> free_slots;           // unused entries of `slots`
+  pkv::SeqIndex index;                       // live sequence id -> slot
+  int32_t live = 0;                          // live sequences
   int32_t next_id = 0;
+  uint64_t epoch = 0;                        // batch calls, for duplicate marks
   std::vector<std::pair<int32_t, int32_t>> cow_pending;  // (src, dst)
+  std::vector<int32_t> rc_taken;             // dry-run scratch, all zero between calls
+  std::vector<int32_t> rc_touched;
   int64_t alloc_failures = 0;
   int64_t cow_copies = 0;
   int64_t forks = 0;
@@ -37,5 +103,15 @@ pkv_status fail(pkv_status st, const std::string& msg);
 pkv_status ok();
 
 inline int dtype_bytes(int32_t dt) { return dt == PKV_F32 ? 4 : 2; }
+
+// Live sequence with this id, or null.
+inline pkv_seq_state* find_seq(pkv_pool* p, int32_t id) {
+  const int32_t s = p->index.find(id);
+  return s < 0 ? nullptr : &p->slots[s];
+}
+inline const pkv_seq_state* find_seq(const pkv_pool* p, int32_t id) {
+  const int32_t s = p->index.find(id);
+  return s < 0 ? nullptr : &p->slots[s];
+}
 
 }  // namespace pkv

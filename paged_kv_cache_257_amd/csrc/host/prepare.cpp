@@ -11,7 +11,7 @@ using pkv::fail;
 namespace {
 
 constexpr int64_t kAlign = 256;
-constexpr int32_t kDefaultPartitionTokens = 512;
+constexpr int32_t kDefaultPartitionTokens = 1024;
 
 int64_t align_up(int64_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
@@ -64,9 +64,9 @@ pkv_status pkv_prepare_decode(pkv_pool* p, const int32_t* seqs, int32_t n_seqs,
     return fail(PKV_E_BAD_ARG, "staging buffer must be 8-byte aligned");
   // every check that could fail comes before the pool changes
   for (int32_t i = 0; i < n_seqs; ++i) {
-    auto it = p->seqs.find(seqs[i]);
-    if (it == p->seqs.end()) return fail(PKV_E_BAD_SEQ, "unknown sequence " + std::to_string(seqs[i]));
-    const int64_t after = int64_t(it->second.length) + append_tokens;
+    const pkv_seq_state* s = pkv::find_seq(p, seqs[i]);
+    if (!s) return fail(PKV_E_BAD_SEQ, "unknown sequence " + std::to_string(seqs[i]));
+    const int64_t after = int64_t(s->length) + append_tokens;
     if (after < 1) return fail(PKV_E_BAD_ARG, "a sequence in the batch has no tokens to attend");
     if ((after + bs - 1) / bs > table_stride)
       return fail(PKV_E_BAD_ARG, "a table would be wider than table_stride");

@@ -48,15 +48,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeParams {
   const char* q;
+  const char* k_new;           // [B][H_kv][D] newest token's K, or null
+  const char* v_new;
   float* out;
-  const char* k_cache;
-  const char* v_cache;
+  char* k_cache;
+  char* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* work;         // [n_work][2] (sequence, partition)
   const int32_t* part_offset;  // [num_seqs] first partial index or -1
-  float* part_o;               // [n_partials][H_q][D]
-  float* part_ml;              // [n_partials][H_q][2]
+  float* part;                 // [n_partials][H_q] records of rec_floats
+  int32_t* counters;           // [num_seqs][H_q] completion tickets, or null
+  int32_t rec_floats;          // record: o[D], m, l, padded to whole 128-byte lines
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;               // H_q / H_kv
@@ -100,6 +103,7 @@ __global__ __launch_bounds__(kWave* NW) void paged_decode_kernel(const DecodePar
 
   const int rg = lane / LPR;  // row group
   const int c = lane - rg * LPR;
+  const bool writes_new = (hg - kvh * p.hgroups_per_kv) == 0;
 
   u32x4 qv[GW];
 #pragma unroll
@@ -118,35 +122,30 @@ __global__ __launch_bounds__(kWave* NW) void paged_decode_kernel(const DecodePar
 
   const int32_t* trow = p.block_tables + int64_t(seq) * p.table_stride;
   const int64_t blk_stride = int64_t(p.num_kv_heads) * TILE;
-  const char* kbase = p.k_cache + int64_t(kvh) * TILE + lane * 16;
-  const char* vbase = p.v_cache + int64_t(kvh) * TILE + lane * 16;
 
-  // 64 table entries at a time, one per lane; block ids are then read with
-  // v_readlane (the block index is uniform across the wave).
-  int tbl = -1, tbl_base = -1;
-  auto block_id = [&](int j) -> int {
-    const int base = j & ~(kWave - 1);
-    if (base != tbl_base) {
-      tbl_base = base;
-      tbl = (base + lane < nblk) ? trow[base + lane] : -1;
-    }
-    return __builtin_amdgcn_readlane(tbl, j - base);
-  };
-
-  u32x4 kc[NI], vc[NI], kn[NI], vn[NI];
-  auto load = [&](int blk, u32x4* kk, u32x4* vv) {
-    const int b = (unsigned(blk) < unsigned(p.num_blocks)) ? blk : 0;
-    const char* kt = kbase + int64_t(b) * blk_stride;
-    const char* vt = vbase + int64_t(b) * blk_stride;
+  // Issue the K/V loads of block j of the current chunk (see below).  The
+  // loads are always issued, so every path through the loop has the same
+  // loads in flight and each wait covers exactly the buffer about to be used;
+  // past the chunk's end, or for a table entry outside the pool, the buffer
+  // resource has no records and the loads return zeros without touching
+  // memory.  Returns the block id.
+  int cb = 0, ce = 0, tbl = -1;
+  auto issue = [&](int j, u32x4* kk, u32x4* vv) __attribute__((always_inline)) -> int {
+    const int blk = __builtin_amdgcn_readlane(tbl, min(j - cb, kWave - 1));
+    const bool ok = j < ce && unsigned(blk) < unsigned(p.num_blocks);
+    const int64_t tile = int64_t(ok ? blk : 0) * blk_stride + int64_t(kvh) * TILE;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_cache + tile, ok ? TILE : 0);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_cache + tile, ok ? TILE : 0);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kk[i] = load_stream(kt + i * 1024);
+    for (int i = 0; i < NI; ++i) kk[i] = load_stream(rk, lane * 16 + i * 1024);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vv[i] = load_stream(vt + i * 1024);
+    for (int i = 0; i < NI; ++i) vv[i] = load_stream(rv, lane * 16 + i * 1024);
+    return j < ce ? blk : -1;
   };
 
   // Online-softmax update with one block; `valid` = rows of the block that
   // hold tokens (16 except in the last block).
-  auto process = [&](const u32x4* kk, const u32x4* vv, int valid, bool masked) {
+  auto process = [&](const u32x4* kk, const u32x4* vv, int valid, bool masked) __attribute__((always_inline)) {
     float ps[GW][NI];
 #pragma unroll
     for (int g = 0; g < GW; ++g) {
@@ -193,33 +192,78 @@ __global__ __launch_bounds__(kWave* NW) void paged_decode_kernel(const DecodePar
     }
   };
 
-  int j = b0 + wave;
-  int blk = -1;
-  if (j < b1) {
-    blk = block_id(j);
-    load(blk, kc, vc);
-  }
-  while (j < b1) {
-    const int jn = j + NW;
-    int blk_n = -1;
-    if (jn < b1) {
-      blk_n = block_id(jn);
-      load(blk_n, kn, vn);
+  // The sequence's newest token, held in registers (nk, nv: this lane's
+  // chunk of its K and V rows), as one more online-softmax update.  Every
+  // row group computes the score; only row group 0 counts the token.
+  auto process_one = [&](const u32x4& nk, const u32x4& nv) __attribute__((always_inline)) {
+    float vf[EPL];
+    to_f32<DT>(nv, vf);
+#pragma unroll
+    for (int g = 0; g < GW; ++g) {
+      float sc = row_sum<LPR>(dot16<DT>(qv[g], nk, 0.f)) * p.scale_log2;
+      if (rg != 0) sc = -INFINITY;
+      const float m_new = fmaxf(m[g], sc);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - m_use);
+      const float pn = __builtin_amdgcn_exp2f(sc - m_use);
+      l[g] = l[g] * alpha + pn;
+      m[g] = m_new;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[g][e] = __builtin_fmaf(pn, vf[e], o[g][e] * alpha);
     }
+  };
+
+  // One block.  The last block of the sequence is masked past its length.
+  // With k_new given, the newest token (position L-1, row r_new of the last
+  // block) comes from k_new/v_new instead of the pool: the block is processed
+  // without that row, the row as process_one, and the first head group of
+  // the KV head stores it into the pool.
+  auto consume = [&](const u32x4* kk, const u32x4* vv, int j, int blk) __attribute__((always_inline)) {
     const bool in_pool = unsigned(blk) < unsigned(p.num_blocks);
     if (in_pool && j != nblk - 1) {
-      process(kc, vc, kBlockTokens, false);
-    } else {
-      const int valid = in_pool ? min(kBlockTokens, L - j * kBlockTokens) : 0;
-      process(kc, vc, valid, true);
+      process(kk, vv, kBlockTokens, false);
+      return;
     }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      kc[i] = kn[i];
-      vc[i] = vn[i];
+    const int r_new = L - 1 - j * kBlockTokens;
+    if (p.k_new != nullptr && in_pool && r_new >= 0 && r_new < kBlockTokens) {
+      const int64_t src = (int64_t(seq) * p.num_kv_heads + kvh) * R + c * 16;
+      const u32x4 nk = *reinterpret_cast<const u32x4*>(p.k_new + src);
+      const u32x4 nv = *reinterpret_cast<const u32x4*>(p.v_new + src);
+      if (writes_new && rg == r_new % RPI) {
+        const int64_t dst = int64_t(blk) * blk_stride + int64_t(kvh) * TILE + int64_t(r_new) * R + c * 16;
+        *reinterpret_cast<u32x4*>(p.k_cache + dst) = nk;
+        *reinterpret_cast<u32x4*>(p.v_cache + dst) = nv;
+      }
+      process(kk, vv, r_new, true);
+      process_one(nk, nv);
+      return;
     }
-    blk = blk_n;
-    j = jn;
+    const int valid = in_pool ? min(kBlockTokens, L - j * kBlockTokens) : 0;
+    process(kk, vv, valid, true);
+  };
+
+  // Wave `wave` takes blocks b0 + wave, b0 + wave + NW, ...  The partition's
+  // table entries come in chunks of 64, one entry per lane, loaded once per
+  // chunk; inside a chunk a block id is a v_readlane, so the only memory
+  // operations in the inner loop are the K/V loads.  Two register buffers
+  // alternate: the next block loads while the current one computes.
+  u32x4 ka[NI], va[NI], kb[NI], vb[NI];
+  for (cb = b0; cb < b1; cb += kWave) {
+    ce = min(cb + kWave, b1);
+    tbl = (cb + lane < ce) ? trow[cb + lane] : -1;
+    int j = cb + wave;
+    if (j >= ce) break;  // uniform: no block of this chunk (nor later ones) for this wave
+    int blk_a = issue(j, ka, va), blk_b;
+    while (true) {
+      blk_b = issue(j + NW, kb, vb);
+      consume(ka, va, j, blk_a);
+      j += NW;
+      if (j >= ce) break;
+      blk_a = issue(j + NW, ka, va);
+      consume(kb, vb, j, blk_b);
+      j += NW;
+      if (j >= ce) break;
+    }
   }
 
   // merge the NW * RPI partial softmax states of this workgroup
@@ -256,20 +300,61 @@ __global__ __launch_bounds__(kWave* NW) void paged_decode_kernel(const DecodePar
     if (single) {
       p.out[(int64_t(seq) * p.num_q_heads + qh) * D + dd] = num / den;
     } else {
-      const int64_t row = int64_t(pidx) * p.num_q_heads + qh;
-      p.part_o[row * D + dd] = num;
+      // partial record of (partition, query head): agent-scope stores, so
+      // the combining workgroup on any XCD reads them without cache flushes
+      float* rec = p.part + (int64_t(pidx) * p.num_q_heads + qh) * p.rec_floats;
+      __hip_atomic_store(rec + dd, num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (dd == 0) {
-        p.part_ml[2 * row] = M;
-        p.part_ml[2 * row + 1] = den;
+        __hip_atomic_store(rec + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(rec + D + 1, den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
+  if (single || p.counters == nullptr) return;
+
+  // Split-K combine in the same launch.  Each workgroup of a (sequence, head
+  // group) waits until its partial stores have completed, takes a ticket, and
+  // the one taking the last ticket combines every partition's record and
+  // resets the ticket for the next launch.  Records and tickets are only
+  // touched through agent-scope atomics and every record owns whole cache
+  // lines, so no cache writeback or invalidate is needed.
+  __shared__ int sm_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int32_t* ticket = p.counters + int64_t(seq) * hgroups + hg;
+  if (threadIdx.x == 0)
+    sm_last = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               n_parts - 1);
+  __syncthreads();
+  if (!sm_last) return;
+  const int base = p.part_offset[seq];
+  if (base < 0 || base + n_parts > p.n_partials) return;
+  for (int idx = threadIdx.x; idx < GW * D; idx += kWave * NW) {
+    const int g = idx / D;
+    const int dd = idx - g * D;
+    const int qh = qh0 + g;
+    const float* rec0 = p.part + (int64_t(base) * p.num_q_heads + qh) * p.rec_floats;
+    const int64_t step = int64_t(p.num_q_heads) * p.rec_floats;
+    float M = -INFINITY;
+    for (int q = 0; q < n_parts; ++q)
+      M = fmaxf(M, __hip_atomic_load(rec0 + q * step + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    float num = 0.f, den = 0.f;
+    for (int q = 0; q < n_parts; ++q) {
+      const float* rec = rec0 + q * step;
+      const float w = __builtin_amdgcn_exp2f(
+          __hip_atomic_load(rec + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M_use);
+      num = __builtin_fmaf(w, __hip_atomic_load(rec + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), num);
+      den = __builtin_fmaf(w, __hip_atomic_load(rec + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), den);
+    }
+    p.out[(int64_t(seq) * p.num_q_heads + qh) * D + dd] = num / den;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 struct ReduceParams {
   float* out;
-  const float* part_o;
-  const float* part_ml;
+  const float* part;
   const int32_t* context_lens;
   const int32_t* part_offset;
   const int32_t* reduce_seqs;
@@ -277,9 +362,11 @@ struct ReduceParams {
   int32_t table_stride;
   int32_t partition_blocks;
   int32_t n_partials;
+  int32_t rec_floats;
 };
 
-// One workgroup of D threads per (multi-partition sequence, query head).
+// Separate combine kernel (two-launch variant): one workgroup of D threads
+// per (multi-partition sequence, query head).
 template <int D>
 __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const ReduceParams p) {
   const int r = blockIdx.x / p.num_q_heads;
@@ -291,16 +378,17 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const ReducePara
   const int base = p.part_offset[seq];
   if (base < 0 || base + n_parts > p.n_partials) return;
   const int dd = threadIdx.x;
+  const float* rec0 = p.part + (int64_t(base) * p.num_q_heads + h) * p.rec_floats;
+  const int64_t step = int64_t(p.num_q_heads) * p.rec_floats;
   float M = -INFINITY;
-  for (int q = 0; q < n_parts; ++q)
-    M = fmaxf(M, p.part_ml[2 * (int64_t(base + q) * p.num_q_heads + h)]);
+  for (int q = 0; q < n_parts; ++q) M = fmaxf(M, rec0[q * step + D]);
   const float M_use = (M == -INFINITY) ? 0.f : M;
   float num = 0.f, den = 0.f;
   for (int q = 0; q < n_parts; ++q) {
-    const int64_t row = int64_t(base + q) * p.num_q_heads + h;
-    const float w = __builtin_amdgcn_exp2f(p.part_ml[2 * row] - M_use);
-    num = __builtin_fmaf(w, p.part_o[row * D + dd], num);
-    den = __builtin_fmaf(w, p.part_ml[2 * row + 1], den);
+    const float* rec = rec0 + q * step;
+    const float w = __builtin_amdgcn_exp2f(rec[D] - M_use);
+    num = __builtin_fmaf(w, rec[dd], num);
+    den = __builtin_fmaf(w, rec[D + 1], den);
   }
   p.out[(int64_t(seq) * p.num_q_heads + h) * D + dd] = num / den;
 }
@@ -313,6 +401,9 @@ DecodeFn pick_waves(int nw) {
     case 1: return paged_decode_kernel<DT, D, GW, 1>;
     case 2: return paged_decode_kernel<DT, D, GW, 2>;
     case 4: return paged_decode_kernel<DT, D, GW, 4>;
+    case 8:  // 512 threads; its LDS merge area fits 64 KiB for GW <= 2 only
+      if constexpr (GW <= 2) return paged_decode_kernel<DT, D, GW, 8>;
+      return paged_decode_kernel<DT, D, GW, 4>;
     default: return nullptr;
   }
 }
@@ -354,15 +445,16 @@ int waves_per_item() {
   static const int nw = [] {
     const char* s = std::getenv("PKV_DECODE_WAVES");
     int v = s ? std::atoi(s) : 0;
-    return (v == 1 || v == 2 || v == 4) ? v : 4;
+    return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 4;
   }();
   return nw;
 }
 
 // Validate the arguments shared by the decode entry points and fill the
 // kernel parameters.  Returns PKV_OK with *empty set when there is no work.
-pkv_status setup_decode(const pkv_pool* pool, const void* q, float* out, int32_t num_seqs,
-                        int32_t num_q_heads, const int32_t* block_tables, int32_t table_stride,
+pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, const void* v_new,
+                        float* out, int32_t num_seqs, int32_t num_q_heads,
+                        const int32_t* block_tables, int32_t table_stride,
                         const int32_t* context_lens, float scale, const int32_t* plan,
                         const pkv_decode_plan_info* info, void* workspace, size_t workspace_bytes,
                         DecodeParams& prm, int& gw, bool& empty) {
@@ -384,6 +476,10 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, float* out, int32_t
   if (table_stride < 1) return fail(PKV_E_BAD_ARG, "table_stride must be >= 1");
   if (int64_t(info->max_context_len) > int64_t(table_stride) * kBlockTokens)
     return fail(PKV_E_BAD_ARG, "a context is longer than its table can address");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(PKV_E_BAD_ARG, "k_new and v_new must both be given or both be NULL");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return fail(PKV_E_BAD_ARG, "k_new and v_new must be 16-byte aligned");
   if (num_seqs == 0 || info->n_work == 0) {
     empty = true;
     return PKV_OK;
@@ -396,15 +492,22 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, float* out, int32_t
   const int group = num_q_heads / d.num_kv_heads;
   gw = (group % 8 == 0) ? 8 : (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
   prm.q = static_cast<const char*>(q);
+  prm.k_new = static_cast<const char*>(k_new);
+  prm.v_new = static_cast<const char*>(v_new);
   prm.out = out;
-  prm.k_cache = static_cast<const char*>(pool->k_cache);
-  prm.v_cache = static_cast<const char*>(pool->v_cache);
+  prm.k_cache = static_cast<char*>(pool->k_cache);
+  prm.v_cache = static_cast<char*>(pool->v_cache);
   prm.block_tables = block_tables;
   prm.context_lens = context_lens;
   prm.work = plan;
   prm.part_offset = plan + 2 * int64_t(info->n_work);
-  prm.part_o = static_cast<float*>(workspace);
-  prm.part_ml = prm.part_o + int64_t(info->n_partials) * num_q_heads * d.head_dim;
+  // workspace: completion tickets [num_seqs][H_q] (256-byte aligned), then
+  // one record per (partial, query head): o[D], m, l, padded to 128 bytes
+  char* ws = static_cast<char*>(workspace);
+  const int64_t ticket_bytes = (int64_t(num_seqs) * num_q_heads * 4 + 255) / 256 * 256;
+  prm.counters = reinterpret_cast<int32_t*>(ws);
+  prm.part = reinterpret_cast<float*>(ws + ticket_bytes);
+  prm.rec_floats = int32_t(((int64_t(d.head_dim) + 2) * 4 + 127) / 128 * 32);
   prm.num_q_heads = num_q_heads;
   prm.num_kv_heads = d.num_kv_heads;
   prm.group = group;
@@ -435,8 +538,8 @@ pkv_status launch_reduce(const pkv_pool* pool, const DecodeParams& prm, int32_t 
   if (info->n_reduce == 0) return PKV_OK;
   ReduceParams rp;
   rp.out = prm.out;
-  rp.part_o = prm.part_o;
-  rp.part_ml = prm.part_ml;
+  rp.part = prm.part;
+  rp.rec_floats = prm.rec_floats;
   rp.context_lens = prm.context_lens;
   rp.part_offset = prm.part_offset;
   rp.reduce_seqs = prm.part_offset + num_seqs;
@@ -461,29 +564,29 @@ pkv_status launch_reduce(const pkv_pool* pool, const DecodeParams& prm, int32_t 
 using namespace pkv;
 
 #define PKV_DECODE_ARGS                                                                          \
-  const pkv_pool *pool, const void *q, float *out, int32_t num_seqs, int32_t num_q_heads,       \
-      const int32_t *block_tables, int32_t table_stride, const int32_t *context_lens,           \
-      float scale, const int32_t *plan, const pkv_decode_plan_info *info, void *workspace,      \
-      size_t workspace_bytes, void *stream
+  const pkv_pool *pool, const void *q, const void *k_new, const void *v_new, float *out,        \
+      int32_t num_seqs, int32_t num_q_heads, const int32_t *block_tables, int32_t table_stride, \
+      const int32_t *context_lens, float scale, const int32_t *plan,                            \
+      const pkv_decode_plan_info *info, void *workspace, size_t workspace_bytes, void *stream
 #define PKV_SETUP                                                                                \
   DecodeParams prm;                                                                              \
   int gw = 1;                                                                                    \
   bool empty = false;                                                                            \
-  if (pkv_status st = setup_decode(pool, q, out, num_seqs, num_q_heads, block_tables,          \
-                                   table_stride, context_lens, scale, plan, info, workspace,    \
-                                   workspace_bytes, prm, gw, empty))                             \
+  if (pkv_status st = setup_decode(pool, q, k_new, v_new, out, num_seqs, num_q_heads,           \
+                                   block_tables, table_stride, context_lens, scale, plan, info, \
+                                   workspace, workspace_bytes, prm, gw, empty))                 \
     return st;                                                                                   \
   if (empty) return PKV_OK;                                                                      \
   hipStream_t s = static_cast<hipStream_t>(stream);
 
 extern "C" pkv_status pkv_paged_decode(PKV_DECODE_ARGS) {
   PKV_SETUP
-  if (pkv_status st = launch_partitions(pool, prm, gw, info, s)) return st;
-  return launch_reduce(pool, prm, num_seqs, info, s);
+  return launch_partitions(pool, prm, gw, info, s);  // combine fused in
 }
 
 extern "C" pkv_status pkv_paged_decode_partitions(PKV_DECODE_ARGS) {
   PKV_SETUP
+  prm.counters = nullptr;  // partials only; pkv_paged_decode_reduce combines
   return launch_partitions(pool, prm, gw, info, s);
 }
 

@@ -158,14 +158,23 @@ class Pool:
         check(self.lib, self.lib.pkv_copy_blocks(self.handle, _dptr(pairs), n, _stream_ptr(stream)))
 
     def paged_decode(self, q, out, block_tables, context_lens, scale: float, plan, info: PlanInfo,
-                     workspace, stream=None) -> None:
-        """Decode attention of every sequence of the batch through its table."""
+                     workspace, stream=None, k_new=None, v_new=None, split: bool = False) -> None:
+        """Decode attention of every sequence of the batch through its table.
+
+        ``k_new``/``v_new`` (device [B][H_kv][d]) are the newest token's rows:
+        stored into the pool and attended in the same launch.  ``workspace``
+        must be zeroed before its first use.  ``split`` runs the two-launch
+        variant (partition kernel, then the separate combine kernel)."""
         B, Hq = int(q.shape[0]), int(q.shape[1])
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-        check(self.lib, self.lib.pkv_paged_decode(
-            self.handle, _dptr(q), _dptr(out), B, Hq, _dptr(block_tables),
-            int(block_tables.shape[1]), _dptr(context_lens), float(scale), _dptr(plan),
-            C.byref(info), _dptr(workspace), ws_bytes, _stream_ptr(stream)))
+        args = (self.handle, _dptr(q), _dptr(k_new), _dptr(v_new), _dptr(out), B, Hq,
+                _dptr(block_tables), int(block_tables.shape[1]), _dptr(context_lens), float(scale),
+                _dptr(plan), C.byref(info), _dptr(workspace), ws_bytes, _stream_ptr(stream))
+        if split:
+            check(self.lib, self.lib.pkv_paged_decode_partitions(*args))
+            check(self.lib, self.lib.pkv_paged_decode_reduce(*args))
+        else:
+            check(self.lib, self.lib.pkv_paged_decode(*args))
 
 
 def decode_plan(context_lens: np.ndarray, partition_tokens: int = 0, block_size: int = 16,

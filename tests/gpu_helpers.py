@@ -73,15 +73,26 @@ class DecodeCase:
         self.slots = np.concatenate(slots) if slots else np.zeros(0, np.int64)
         self.seqs = list(range(len(self.lens)))
 
-    def write_context(self):
-        k = to_device(self.vals["k"], self.cfg.dtype)
-        v = to_device(self.vals["v"], self.cfg.dtype)
-        slots = torch.from_numpy(self.slots).cuda()
+    def last_rows(self):
+        """Index of each sequence's newest token in the context K/V rows."""
+        return np.cumsum(self.lens) - 1
+
+    def write_context(self, skip_last: bool = False):
+        """Write the context rows; ``skip_last`` leaves each sequence's newest
+        token out (the fused append-decode stores it)."""
+        keep = np.ones(len(self.slots), dtype=bool)
+        if skip_last:
+            keep[self.last_rows()] = False
+        k = to_device(np.ascontiguousarray(self.vals["k"][keep]), self.cfg.dtype)
+        v = to_device(np.ascontiguousarray(self.vals["v"][keep]), self.cfg.dtype)
+        slots = torch.from_numpy(np.ascontiguousarray(self.slots[keep])).cuda()
         self.pool.write_kv(k, v, slots)
         sync()
         del k, v
 
-    def decode(self, partition_tokens=0):
+    def decode(self, partition_tokens=0, split=False, append=False):
+        """Decode the batch; ``append`` passes each sequence's newest token as
+        k_new/v_new (fused store + decode)."""
         cfg = self.cfg
         tables, lens = self.pool.build_batch(self.seqs, self.stride)
         plan, info = decode_plan(lens, partition_tokens)
@@ -89,10 +100,19 @@ class DecodeCase:
         out = torch.full((len(self.lens), cfg.num_q_heads, cfg.head_dim), float("nan"),
                          dtype=torch.float32, device="cuda")
         ws = decode_workspace_bytes(info, cfg.num_q_heads, cfg.head_dim)
-        workspace = torch.empty(max(ws // 4, 1), dtype=torch.float32, device="cuda")
+        workspace = torch.zeros(max(ws // 4, 1), dtype=torch.float32, device="cuda")
+        k_new = v_new = None
+        if append:
+            rows = self.last_rows()
+            k_new = to_device(np.ascontiguousarray(self.vals["k"][rows]), cfg.dtype)
+            v_new = to_device(np.ascontiguousarray(self.vals["v"][rows]), cfg.dtype)
         self.pool.paged_decode(q, out, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
-                               cfg.scale, torch.from_numpy(plan).cuda(), info, workspace)
+                               cfg.scale, torch.from_numpy(plan).cuda(), info, workspace,
+                               k_new=k_new, v_new=v_new, split=split)
         sync()
+        ntickets = -(-len(self.lens) * cfg.num_q_heads * 4 // 256) * 64
+        tickets_zero = bool((workspace[:ntickets].view(torch.int32) == 0).all().item())
+        self.last_tickets_zero = tickets_zero
         return out.cpu().numpy().astype(np.float64), info
 
     def oracle_out(self, i: int) -> np.ndarray:

@@ -47,7 +47,9 @@ def test_plan_covers_every_partition_once(cfg, P):
 def test_plan_edge_cases():
     info = check_plan(np.array([1, 16, 17, 512, 513]), 256)
     assert info.n_reduce == 2
-    assert decode_workspace_bytes(info, 8, 128, host_only=True) == info.n_partials * 8 * 130 * 4
+    tickets = -(-5 * 8 * 4 // 256) * 256  # one int32 per (sequence, query head), 256-byte aligned
+    record = 640  # 128 + 2 floats, padded to whole 128-byte lines
+    assert decode_workspace_bytes(info, 8, 128, host_only=True) == tickets + info.n_partials * 8 * record
     _, info0 = decode_plan(np.zeros(0, dtype=np.int32), 256, host_only=True)
     assert info0.n_work == 0
     with pytest.raises(PkvError):

@@ -65,12 +65,14 @@ def test_workload_parity(cfg):
         seqs = sample_seqs(case.lens, 12, cfg.seed)
         ref = {i: case.oracle_out(i) for i in seqs}
         for P in PARTITIONS[cfg.name]:
-            out, info = case.decode(P)
-            err = max(float(np.max(np.abs(out[i] - ref[i]))) for i in seqs)
-            print(f"[gpu] {cfg.name} P={info.partition_tokens} work={info.n_work} "
-                  f"reduce={info.n_reduce} max_err={err:.3e}", flush=True)
-            assert err <= TOL[cfg.dtype], (P, err)
-            assert np.isfinite(out).all()
+            for split in (False, True):
+                out, info = case.decode(P, split=split)
+                err = max(float(np.max(np.abs(out[i] - ref[i]))) for i in seqs)
+                print(f"[gpu] {cfg.name} P={info.partition_tokens} split={split} work={info.n_work} "
+                      f"reduce={info.n_reduce} max_err={err:.3e}", flush=True)
+                assert err <= TOL[cfg.dtype], (P, split, err)
+                assert np.isfinite(out).all()
+                assert case.last_tickets_zero
     finally:
         case.close()
 
@@ -91,6 +93,56 @@ def test_nan_filled_pool_does_not_leak(dtype):
         case.close()
 
 
+@pytest.mark.parametrize("cfg", CONFIGS[:3], ids=lambda c: c.name)
+def test_fused_append_decode(cfg):
+    """k_new/v_new path: the pool holds every token but each sequence's newest;
+    one launch stores the newest rows and attends over all of them."""
+    print(f"\n[gpu] append-decode {cfg.name}", flush=True)
+    case = DecodeCase(cfg, fill=float("nan"))
+    try:
+        case.write_context(skip_last=True)
+        seqs = sample_seqs(case.lens, 12, cfg.seed)
+        ref = {i: case.oracle_out(i) for i in seqs}
+        out, info = case.decode(PARTITIONS[cfg.name][0], append=True)
+        err = max(float(np.max(np.abs(out[i] - ref[i]))) for i in seqs)
+        print(f"[gpu] append-decode {cfg.name} max_err={err:.3e}", flush=True)
+        assert err <= TOL[cfg.dtype] and np.isfinite(out).all()
+        # the newest rows landed in the pool: bit-exact everywhere a token lives
+        kd, vd = device_bits(case.k_cache), device_bits(case.v_cache)
+        km, vm = host_bits(case.oracle.mirror.k), host_bits(case.oracle.mirror.v)
+        s = case.slots
+        blk, row = s // 16, s % 16
+        assert np.array_equal(kd[blk, :, row, :], km[blk, :, row, :])
+        assert np.array_equal(vd[blk, :, row, :], vm[blk, :, row, :])
+    finally:
+        case.close()
+
+
+@pytest.mark.parametrize("group,q_heads", [(1, 4), (6, 6), (12, 24), (16, 16)])
+def test_fused_append_decode_gqa_groups(group, q_heads):
+    """Several workgroups (query-head groups) read the same new row; one stores it."""
+    kv = q_heads // group
+    cfg = dataclasses.replace(CONFIGS[2], name="append_gqa", index=40 + group, num_kv_heads=kv,
+                              num_q_heads=kv * group, dtype="bf16")
+    lens = [1, 2, 16, 17, 31, 100, 513, 700]
+    nb = sum(-(-L // 16) for L in lens) + 2
+    case = DecodeCase(cfg, lens=lens, num_blocks=nb, free_order=np.random.default_rng(group).permutation(nb),
+                      fill=float("nan"))
+    try:
+        case.write_context(skip_last=True)
+        for P in (16, 0):
+            for split in (False, True):
+                out, _ = case.decode(P, split=split, append=True)
+                err = max_err(case, out, range(len(lens)))
+                assert err <= TOL["bf16"], (P, split, err)
+        kd = device_bits(case.k_cache)
+        km = host_bits(case.oracle.mirror.k)
+        blk, row = case.slots // 16, case.slots % 16
+        assert np.array_equal(kd[blk, :, row, :], km[blk, :, row, :])
+    finally:
+        case.close()
+
+
 SWEEP = [(dt, d, hkv, g) for dt in ("f32", "f16", "bf16") for d in (64, 128, 256)
          for hkv, g in ((2, 1), (2, 2), (1, 4), (2, 8))]
 
@@ -107,9 +159,11 @@ def test_shape_sweep(dtype, head_dim, kv_heads, group):
     try:
         case.write_context()
         for P in (16, 64, 0):
-            out, _ = case.decode(P)
-            err = max_err(case, out, range(len(lens)))
-            assert err <= TOL[dtype], (P, err)
+            for split in (False, True):
+                out, _ = case.decode(P, split=split)
+                err = max_err(case, out, range(len(lens)))
+                assert err <= TOL[dtype], (P, split, err)
+                assert case.last_tickets_zero
     finally:
         case.close()
 
