@@ -77,12 +77,12 @@ def committed_traffic():
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="gpt_f16")
     ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = library default)")
-    ap.add_argument("--replicas", type=int, default=4)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--two-launch", action="store_true",
                     help="decode as partition kernel + separate combine kernel (comparison)")
@@ -122,20 +122,201 @@ def cpu_baseline(cfg, sh, vals, stride, budget_s):
         run = DecodeRun(cfg, sh.lens, sh.num_blocks, sh.free_order, stride)
         run.write_context(vals["k"], vals["v"])
         order = np.random.default_rng(cfg.seed + 7).permutation(len(sh.lens))
+        # whole passes over the batch in a fixed random order until the
+        # budget is spent (the last pass may be partial)
         done, tokens, t0 = 0, 0, time.perf_counter()
-        for i in order:
-            run.attend(int(i), vals["q"][int(i)])
+        while time.perf_counter() - t0 <= budget_s:
+            i = int(order[done % len(order)])
+            run.attend(i, vals["q"][i])
             done += 1
-            tokens += int(sh.lens[int(i)])
-            if time.perf_counter() - t0 > budget_s:
-                break
+            tokens += int(sh.lens[i])
         dt = time.perf_counter() - t0
     kv_bytes = tokens * 2 * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{done} of {len(sh.lens)} sequences ({tokens} context tokens) of the same batch, "
-                      f"fp64 numpy attention, {dt:.1f} s",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{done / len(sh.lens):.2f} passes over the {len(sh.lens)}-sequence batch "
+                      f"({done} sequence decodes, {tokens} context tokens), fp64 numpy attention, "
+                      f"{dt:.1f} s",
             "decode_tokens_per_s": round(done / dt, 3)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_probe():
+    """A plain 1 GiB device-to-device copy timed with HIP events: the GB/s
+    (read + write) a streaming kernel reaches on this GPU, for context."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = []
+    for _ in range(5):
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    best = min(ms)
+    return {"bytes_moved": 2 * n, "ms_best": round(best, 4), "GBps": round(2 * n / best / 1e6, 1)}
+
+
+def prefix_shared_schedule(cfg, plan, width, iterations):
+    """Replay the prefix-shared loop on a host-only allocator (the same C++
+    allocator, no GPU) to count each iteration's bytes: logical = every
+    decoded sequence's context, physical = the distinct filled slots those
+    contexts map to (shared prefix blocks counted once)."""
+    import numpy as np
+
+    from paged_kv_cache_257_amd import Pool
+    from workloads.churn import choose_churn
+
+    pool = Pool(plan.num_blocks, cfg.num_kv_heads, cfg.head_dim, cfg.dtype, width, 16,
+                plan.free_order, host_only=True)
+    try:
+        root, _ = pool.alloc(cfg.prefix_len)
+        for t in plan.tails:
+            pool.append(pool.fork(root), int(t))
+        rows, col = [], np.arange(width)
+        for it in range(iterations):
+            seqs = [x for x in pool.live() if x != root]
+            pool.append_batch(seqs, 1)
+            pool.take_cow()
+            tables, lens = pool.build_batch(seqs, width)
+            fill = np.clip(lens[:, None] - 16 * col[None, :], 0, 16)
+            used = fill > 0
+            blocks, fills = tables[used], fill[used]
+            best = np.zeros(plan.num_blocks, dtype=np.int64)
+            np.maximum.at(best, blocks, fills)
+            rows.append((len(seqs), int(lens.sum()), int(best.sum())))
+            retire, parents = choose_churn(cfg, it, seqs)
+            for x in retire:
+                pool.free(x)
+            for x in parents:
+                pool.fork(x)
+        return rows
+    finally:
+        pool.close()
+
+
+def bench_prefix_shared(args, cfg):
+    """The prefix-shared continuous-batching loop: every iteration appends one
+    token to each of the 256 decoding sequences (copy-on-write where a
+    partly filled block is shared), decodes them all, retires 13 and admits
+    13 forks.  The timed region is whole iterations, CPU scheduler work
+    included."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_257_amd import Pool
+    from paged_kv_cache_257_amd.step import DecodeIteration
+    from workloads import draw_normal_storage
+    from workloads.churn import choose_churn, draw_prefix_shared_plan
+
+    warm = min(args.warmup, 8)
+    steps = min(args.steps, cfg.iterations - warm)
+    total = warm + steps
+    plan = draw_prefix_shared_plan(cfg)
+    width = -(-(cfg.prefix_len + cfg.tail_max + cfg.iterations) // 16)
+    H, Hq, d, dt = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.dtype
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    per_tok = 2 * H * d * (4 if dt == "f32" else 2)
+    sched = prefix_shared_schedule(cfg, plan, width, total)
+
+    def dev(bits):
+        a = np.ascontiguousarray(bits)
+        t = torch.from_numpy(a.view(np.int16) if dt == "bf16" else a)
+        return (t.view(torch.bfloat16) if dt == "bf16" else t).to("cuda")
+
+    kc = torch.zeros((plan.num_blocks, H, 16, d), dtype=tdt, device="cuda")
+    vc = torch.zeros_like(kc)
+    pool = Pool(plan.num_blocks, H, d, dt, width, 16, plan.free_order, kc, vc)
+    # context K/V: a seeded 8192-token chunk written over and over (values do
+    # not change the traffic)
+    chunk = 8192
+    ck = dev(draw_normal_storage((cfg.seed, 60), (chunk, H, d), dt))
+    cv = dev(draw_normal_storage((cfg.seed, 61), (chunk, H, d), dt))
+    root, slots = pool.alloc(cfg.prefix_len)
+    all_slots = [slots] + [pool.append(pool.fork(root), int(t)) for t in plan.tails]
+    all_slots = torch.from_numpy(np.concatenate(all_slots)).cuda()
+    for o in range(0, all_slots.numel(), chunk):
+        sl = all_slots[o:o + chunk]
+        pool.write_kv(ck[:sl.numel()], cv[:sl.numel()], sl)
+    del ck, cv
+    n_max = cfg.num_seqs
+    vals = [(dev(draw_normal_storage((cfg.seed, 70 + j), (n_max, Hq, d), dt)),
+             dev(draw_normal_storage((cfg.seed, 80 + j), (n_max, H, d), dt)),
+             dev(draw_normal_storage((cfg.seed, 90 + j), (n_max, H, d), dt))) for j in range(4)]
+    out = torch.empty((n_max, Hq, d), dtype=torch.float32, device="cuda")
+    step = DecodeIteration(pool, n_max, width, Hq, args.partition)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(total)]
+    torch.cuda.synchronize()
+
+    def iteration(it):
+        seqs = np.asarray([x for x in pool.live() if x != root], dtype=np.int32)
+        q, k, v = vals[it % 4]
+        step.step(seqs, q, out, k, v, cfg.scale, events=ev[it] if it % args.time_every == 0 else None)
+        retire, parents = choose_churn(cfg, it, seqs.tolist())
+        for x in retire:
+            pool.free(x)
+        for x in parents:
+            pool.fork(x)
+        return len(seqs)
+
+    for it in range(warm):
+        iteration(it)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    decoded = sum(iteration(it) for it in range(warm, total))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stats = pool.stats()
+    step.close()
+    pool.close()
+    timed = range(warm, total)
+    assert decoded == sum(sched[i][0] for i in timed)
+    logical = sum(sched[i][1] for i in timed) * per_tok
+    physical = sum(sched[i][2] for i in timed) * per_tok
+    sampled = [i for i in timed if i % args.time_every == 0]
+    kern_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in sampled]
+    s_log = float(np.mean([sched[i][1] for i in sampled])) * per_tok
+    s_phy = float(np.mean([sched[i][2] for i in sampled])) * per_tok
+    km = float(np.mean(kern_ms)) / 1e3 if kern_ms else float("nan")
+    res = {
+        "metric": "prefix-shared decode loop: logical K/V GB/s + iteration tokens/s",
+        "value": round(logical / wall / 1e9, 2),
+        "unit": "GB/s (logical)",
+        "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "num_seqs": cfg.num_seqs, "num_q_heads": Hq, "num_kv_heads": H,
+                   "head_dim": d, "block_size": 16, "prefix_len": cfg.prefix_len,
+                   "tail_max": cfg.tail_max, "churn_per_iteration": cfg.churn,
+                   "step": "append + copy-on-write + decode (new K/V stored inside) + retire/admit"},
+        "physical_GBps": round(physical / wall / 1e9, 2),
+        "pct_of_hbm_peak_physical": round(100 * physical / wall / 1e9 / HBM_PEAK_GBPS, 2),
+        "iteration_tokens_per_s": round(decoded / wall, 1),
+        "cow_copies": stats["cow_copies"],
+        "kernel": {"ms_mean": round(km * 1e3, 4), "launches_timed": len(kern_ms),
+                   "logical_GBps": round(s_log / km / 1e9, 1),
+                   "physical_GBps": round(s_phy / km / 1e9, 1)},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
 
 
 def main(argv=None):
@@ -154,9 +335,11 @@ def main(argv=None):
     from paged_kv_cache_257_amd import Pool
     from paged_kv_cache_257_amd.step import DecodeIteration
     from workloads import config_by_name, draw_decode_values, draw_normal_storage
-    from workloads.configs import draw_decode_shapes
+    from workloads.configs import PrefixSharedConfig, draw_decode_shapes
 
     cfg = config_by_name(args.workload)
+    if isinstance(cfg, PrefixSharedConfig):
+        return bench_prefix_shared(args, cfg)
     sh = draw_decode_shapes(cfg)
     vals = draw_decode_values(cfg, sh.lens)
     B, Hq, H, d, dt = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.dtype
@@ -230,10 +413,14 @@ def main(argv=None):
     timed = range(args.warmup, total)
     kbytes = sum(step_bytes[s] for s in timed)
     sampled = [s for s in timed if s % args.time_every == 0]
+    if not sampled:
+        print("bench.py: --time-every leaves no timed launch in the measured steps", file=sys.stderr)
+        return 2
     kern_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in sampled]
     mean_kern_s = float(np.mean(kern_ms)) / 1e3
     mean_bytes = float(np.mean([step_bytes[s] for s in sampled]))
     achieved = mean_bytes / mean_kern_s / 1e9
+    timed_ctx = float(np.mean([step_bytes[s] for s in timed])) / per_tok / B
     value = kbytes / wall / 1e9
     info = infos[-1]
     traffic = committed_traffic()
@@ -252,6 +439,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": cfg.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": H,
                    "head_dim": d, "block_size": 16, "mean_context": round(float(sh.lens.mean()), 1),
+                   "mean_context_timed": round(timed_ctx, 1),
                    "max_context": int(sh.lens.max()), "partition_tokens": info.partition_tokens,
                    "work_items": info.n_work, "replicas": args.replicas,
                    "decode_launches": 2 if args.two_launch else 1,
@@ -260,22 +448,30 @@ def main(argv=None):
                    "accumulate": "f32", "output": "f32"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(B * args.steps / wall, 1),
+        # one attention layer per step; a 32-layer model of this shape would
+        # decode about 1/32 as many tokens per second (a projection)
+        "decode_tokens_per_s_32_layer_projection": round(B * args.steps / wall / 32, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
                      "kernel": "paged_decode_kernel" + (" (partition kernel of two launches)"
                                                         if args.two_launch else ""),
                      "kernel_ms_mean": round(float(np.mean(kern_ms)), 5),
+                     "kernel_ms_median": round(float(np.median(kern_ms)), 5),
                      "kernel_ms_p10": round(float(np.percentile(kern_ms, 10)), 5),
                      "kernel_ms_p90": round(float(np.percentile(kern_ms, 90)), 5),
                      "timed_launches": len(sampled),
                      "algorithmic_bytes_per_launch": int(mean_bytes),
                      "kernel_source_sha": kernel_source_sha()},
     }
+    for pool, it, *_ in reps:
+        it.close()
+        pool.close()
+    del reps
+    torch.cuda.empty_cache()
+    res["copy_probe"] = copy_probe()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, sh, vals, -(-int(sh.lens.max()) // 16), args.cpu_seconds)
-    for pool, *_ in reps:
-        pool.close()
     print(json.dumps(res), flush=True)
     return 0
 

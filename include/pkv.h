@@ -162,8 +162,8 @@ pkv_status pkv_build_batch(const pkv_pool* pool, const int32_t* seqs, int32_t n_
  * ------------------------------------------------------------------------ */
 
 /* Split-K plan of a decode batch.  Each sequence's tokens are cut into
- * partitions of partition_tokens (a multiple of block_size; 0 picks a size
- * from the batch).  One work item per (sequence, partition); items are ordered
+ * partitions of partition_tokens (a multiple of block_size; 0 selects
+ * pkv_default_partition_tokens()).  One work item per (sequence, partition); items are ordered
  * longest first so that the GPU's in-order dispatch fills the tail with short
  * ones.  Sequences with more than one partition write partial results that a
  * second kernel combines.
@@ -196,6 +196,15 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
  * tickets for num_seqs x num_q_heads, then the split-K partials. */
 size_t pkv_decode_workspace_bytes(const pkv_decode_plan_info* info, int32_t num_q_heads,
                                   int32_t head_dim);
+
+/* Workspace bytes that suffice for every plan of at most max_seqs sequences
+ * no longer than max_context_len tokens (0 on bad arguments); for callers
+ * that size the workspace once. */
+size_t pkv_decode_workspace_bound(int32_t max_seqs, int32_t max_context_len, int32_t block_size,
+                                  int32_t partition_tokens, int32_t num_q_heads, int32_t head_dim);
+
+/* Partition length that partition_tokens = 0 selects. */
+int32_t pkv_default_partition_tokens(void);
 
 /* ---------------------------------------------------------------------------
  * Host: one decode iteration's metadata in one staging buffer
@@ -272,8 +281,9 @@ pkv_status pkv_stepper_destroy(pkv_stepper* stepper);
  *           pkv_paged_decode with k_new/v_new (the appended tokens' rows,
  *           [n_seqs][num_kv_heads][head_dim]) stored and attended.
  * The host may run up to PKV_STEPPER_SLOTS iterations ahead of the device.
- * ev_before / ev_after: optional hipEvent_t recorded on `stream` around the
- * decode launch.  layout_out / slot_out (optional) receive the iteration's
+ * ev_before / ev_after: optional hipEvent_t attached to the decode dispatch
+ * (start and end of the kernel's execution on `stream`); when the batch is
+ * empty no kernel runs and they are not recorded.  layout_out / slot_out (optional) receive the iteration's
  * staging layout and slot index (the host slot stays readable until the slot
  * comes round again, PKV_STEPPER_SLOTS iterations later). */
 pkv_status pkv_stepper_step(pkv_stepper* stepper, const int32_t* seqs, int32_t n_seqs,

@@ -83,6 +83,8 @@ SIGNATURES = {
     "pkv_decode_plan_ints": [PI32, I32, I32, I32, PI32],
     "pkv_decode_plan": [PI32, I32, I32, I32, PI32, I32, C.POINTER(PlanInfo)],
     "pkv_decode_workspace_bytes": [C.POINTER(PlanInfo), I32, I32],
+    "pkv_decode_workspace_bound": [I32, I32, I32, I32, I32, I32],
+    "pkv_default_partition_tokens": [],
     "pkv_prepare_decode_bytes": [I32, I32, I32, I32, I32],
     "pkv_prepare_decode": [P, PI32, I32, I32, I32, I32, P, C.c_size_t, C.POINTER(BatchLayout)],
     "pkv_stepper_slot_bytes": [I32, I32, I32, I32],
@@ -98,6 +100,7 @@ SIGNATURES = {
     "pkv_last_error": [],
 }
 RESTYPES = {"pkv_last_error": C.c_char_p, "pkv_decode_workspace_bytes": C.c_size_t,
+            "pkv_decode_workspace_bound": C.c_size_t, "pkv_default_partition_tokens": C.c_int32,
             "pkv_prepare_decode_bytes": C.c_size_t, "pkv_stepper_slot_bytes": C.c_size_t}
 DEVICE_FUNCS = ("pkv_copy_blocks", "pkv_write_kv", "pkv_paged_decode", "pkv_paged_decode_partitions",
                 "pkv_paged_decode_reduce", "pkv_stepper_slot_bytes", "pkv_stepper_create",

@@ -14,12 +14,11 @@ using pkv::fail;
 
 namespace {
 
-constexpr int32_t kDefaultPartitionTokens = 1024;
 
 pkv_status check_lens(const int32_t* lens, int32_t n, int32_t bs, int32_t& P, int32_t& max_len) {
   if (n < 0 || (n > 0 && !lens)) return fail(PKV_E_BAD_ARG, "bad context_lens");
   if (bs < 1) return fail(PKV_E_BAD_ARG, "bad block_size");
-  if (P == 0) P = kDefaultPartitionTokens;
+  if (P == 0) P = pkv::kDefaultPartitionTokens;
   if (P < bs || P % bs != 0)
     return fail(PKV_E_BAD_ARG, "partition_tokens must be a positive multiple of block_size");
   max_len = 0;
@@ -128,6 +127,24 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
   info->plan_ints = int32_t(need);
   info->max_context_len = max_len;
   return PKV_OK;
+}
+
+int32_t pkv_default_partition_tokens(void) { return pkv::kDefaultPartitionTokens; }
+
+size_t pkv_decode_workspace_bound(int32_t max_seqs, int32_t max_context_len, int32_t block_size,
+                                  int32_t partition_tokens, int32_t num_q_heads, int32_t head_dim) {
+  if (max_seqs < 0 || max_context_len < 1 || block_size < 1) return 0;
+  const int32_t P = partition_tokens ? partition_tokens : pkv::kDefaultPartitionTokens;
+  if (P < block_size || P % block_size != 0) return 0;
+  const int64_t parts = (int64_t(max_context_len) + P - 1) / P;
+  pkv_decode_plan_info worst{};
+  worst.num_seqs = max_seqs;
+  worst.block_size = block_size;
+  worst.partition_tokens = P;
+  const int64_t partials = parts > 1 ? int64_t(max_seqs) * parts : 0;
+  if (partials > INT32_MAX) return 0;
+  worst.n_partials = int32_t(partials);
+  return pkv_decode_workspace_bytes(&worst, num_q_heads, head_dim);
 }
 
 size_t pkv_decode_workspace_bytes(const pkv_decode_plan_info* info, int32_t num_q_heads,

@@ -11,7 +11,6 @@ using pkv::fail;
 namespace {
 
 constexpr int64_t kAlign = 256;
-constexpr int32_t kDefaultPartitionTokens = 1024;
 
 int64_t align_up(int64_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
@@ -42,7 +41,7 @@ extern "C" {
 size_t pkv_prepare_decode_bytes(int32_t max_seqs, int32_t append_tokens, int32_t table_stride,
                                 int32_t block_size, int32_t partition_tokens) {
   if (max_seqs < 0 || append_tokens < 0 || table_stride < 1 || block_size < 1) return 0;
-  const int32_t P = partition_tokens ? partition_tokens : kDefaultPartitionTokens;
+  const int32_t P = partition_tokens ? partition_tokens : pkv::kDefaultPartitionTokens;
   if (P < block_size) return 0;
   const Offsets o = layout_for(max_seqs, append_tokens, max_seqs, table_stride,
                                plan_cap_for(max_seqs, table_stride, block_size, P));
@@ -57,7 +56,7 @@ pkv_status pkv_prepare_decode(pkv_pool* p, const int32_t* seqs, int32_t n_seqs,
   if (n_seqs < 0 || append_tokens < 0 || table_stride < 1 || (n_seqs > 0 && !seqs))
     return fail(PKV_E_BAD_ARG, "bad batch arguments");
   const int32_t bs = p->desc.block_size;
-  const int32_t P = partition_tokens ? partition_tokens : kDefaultPartitionTokens;
+  const int32_t P = partition_tokens ? partition_tokens : pkv::kDefaultPartitionTokens;
   if (P < bs || P % bs != 0)
     return fail(PKV_E_BAD_ARG, "partition_tokens must be a positive multiple of block_size");
   if (reinterpret_cast<uintptr_t>(staging) % 8 != 0)

@@ -29,16 +29,30 @@
 // carry the nontemporal hint: on MI355X that lifts a random 4 KiB-tile gather
 // from ~5.0 TB/s to ~6.4 TB/s.  At the end the row groups and waves of the
 // workgroup merge their (m, l, o) through LDS; a single-partition sequence
-// writes o / l, otherwise (m, l, o) go to the workspace and the reduce
-// kernel merges the partitions:  M = max m_p,
+// writes o / l, otherwise (m, l, o) go to the workspace and the partitions
+// are merged:  M = max m_p,
 //   out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// The merge runs in the same launch: each partial record is written with
+// device-scope atomic stores, the workgroup waits for its stores, then takes
+// a ticket from a per-(sequence, head) counter; the workgroup that takes the
+// last ticket reads the records with device-scope loads, merges them and
+// resets the counter to zero for the next launch.  pkv_paged_decode_reduce
+// is the same merge as a kernel of its own.
+//
+// With k_new / v_new given, the sequence's newest token (position L-1) is
+// taken from those arrays instead of the pool, and the workgroup of the first
+// query-head group of its KV head stores it into its slot, so the decode and
+// the append of that token are one launch.
 //
 // Rows past the sequence length in its last block are masked: their score
 // is -inf and their V row is replaced by zeros, so stale or NaN contents of
 // unused slots never reach the output.  Table entries outside the pool are
 // treated as fully masked blocks (nothing is read through them).
+#include <hip/hip_ext.h>
+
 #include <cstdlib>
 
+#include "decode_launch.h"
 #include "device_common.h"
 
 namespace pkv {
@@ -523,13 +537,20 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
   return PKV_OK;
 }
 
+// ev_start / ev_stop (optional) are attached to the dispatch itself
+// (hipExtLaunchKernel), so their interval is the kernel's execution, without
+// the queueing of separate marker packets.
 pkv_status launch_partitions(const pkv_pool* pool, const DecodeParams& prm, int gw,
-                             const pkv_decode_plan_info* info, hipStream_t s) {
+                             const pkv_decode_plan_info* info, hipStream_t s,
+                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
   const int nw = waves_per_item();
   DecodeFn fn = pick_decode(pool->desc.dtype, pool->desc.head_dim, gw, nw);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group");
   const int64_t grid = int64_t(info->n_work) * prm.num_kv_heads * prm.hgroups_per_kv;
-  hipLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kWave * nw), 0, s, prm);
+  if (ev_start || ev_stop)
+    hipExtLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kWave * nw), 0, s, ev_start, ev_stop, 0, prm);
+  else
+    hipLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kWave * nw), 0, s, prm);
   return launch_status("paged_decode launch");
 }
 
@@ -563,11 +584,6 @@ pkv_status launch_reduce(const pkv_pool* pool, const DecodeParams& prm, int32_t 
 
 using namespace pkv;
 
-#define PKV_DECODE_ARGS                                                                          \
-  const pkv_pool *pool, const void *q, const void *k_new, const void *v_new, float *out,        \
-      int32_t num_seqs, int32_t num_q_heads, const int32_t *block_tables, int32_t table_stride, \
-      const int32_t *context_lens, float scale, const int32_t *plan,                            \
-      const pkv_decode_plan_info *info, void *workspace, size_t workspace_bytes, void *stream
 #define PKV_SETUP                                                                                \
   DecodeParams prm;                                                                              \
   int gw = 1;                                                                                    \
@@ -582,6 +598,11 @@ using namespace pkv;
 extern "C" pkv_status pkv_paged_decode(PKV_DECODE_ARGS) {
   PKV_SETUP
   return launch_partitions(pool, prm, gw, info, s);  // combine fused in
+}
+
+pkv_status pkv::paged_decode_timed(PKV_DECODE_ARGS, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  PKV_SETUP
+  return launch_partitions(pool, prm, gw, info, s, ev_start, ev_stop);
 }
 
 extern "C" pkv_status pkv_paged_decode_partitions(PKV_DECODE_ARGS) {

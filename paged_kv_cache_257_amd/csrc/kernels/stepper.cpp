@@ -19,6 +19,7 @@
 #include <string>
 
 #include "../host/pool_internal.h"
+#include "decode_launch.h"
 
 using pkv::fail;
 
@@ -154,21 +155,13 @@ pkv_status pkv_stepper_step(pkv_stepper* s, const int32_t* seqs, int32_t n_seqs,
                                         lay.n_pairs, cs))
       return st;
   }
-  if (ev_before) {
-    if (pkv_status st = hip_status(hipEventRecord(static_cast<hipEvent_t>(ev_before), cs), "hipEventRecord"))
-      return st;
-  }
-  if (pkv_status st = pkv_paged_decode(
+  if (pkv_status st = pkv::paged_decode_timed(
           s->pool, q, k_new, v_new, out, n_seqs, s->num_q_heads,
           reinterpret_cast<const int32_t*>(dev + lay.off_tables), s->stride,
           reinterpret_cast<const int32_t*>(dev + lay.off_lens), scale,
           reinterpret_cast<const int32_t*>(dev + lay.off_plan), &lay.plan, s->workspace,
-          s->workspace_bytes, cs))
+          s->workspace_bytes, cs, static_cast<hipEvent_t>(ev_before), static_cast<hipEvent_t>(ev_after)))
     return st;
-  if (ev_after) {
-    if (pkv_status st = hip_status(hipEventRecord(static_cast<hipEvent_t>(ev_after), cs), "hipEventRecord"))
-      return st;
-  }
   s->used[k] = true;
   s->last_stream = cs;
   s->pending = true;

@@ -196,3 +196,19 @@ def decode_workspace_bytes(info: PlanInfo, num_q_heads: int, head_dim: int,
                            host_only: bool = False) -> int:
     lib = _capi.load(host_only=host_only)
     return int(lib.pkv_decode_workspace_bytes(C.byref(info), num_q_heads, head_dim))
+
+
+def decode_workspace_bound(max_seqs: int, max_context_len: int, num_q_heads: int, head_dim: int,
+                           partition_tokens: int = 0, block_size: int = 16,
+                           host_only: bool = False) -> int:
+    """Workspace bytes enough for any batch within these limits."""
+    lib = _capi.load(host_only=host_only)
+    n = int(lib.pkv_decode_workspace_bound(max_seqs, max_context_len, block_size, partition_tokens,
+                                           num_q_heads, head_dim))
+    if n == 0:
+        raise ValueError("bad decode geometry")
+    return n
+
+
+def default_partition_tokens(host_only: bool = False) -> int:
+    return int(_capi.load(host_only=host_only).pkv_default_partition_tokens())

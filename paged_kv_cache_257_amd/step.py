@@ -27,8 +27,8 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from ._capi import BatchLayout, PlanInfo, check, i32p
-from .pool import Pool, _dptr, _stream_ptr, decode_workspace_bytes
+from ._capi import BatchLayout, check, i32p
+from .pool import Pool, _dptr, _stream_ptr
 
 NBUF = 3
 STEPPER_SLOTS = 8  # PKV_STEPPER_SLOTS in include/pkv.h
@@ -56,10 +56,10 @@ class DecodeIteration:
         self.compute_done = [None] * NBUF
         self.turn = 0
         self.copy_stream = torch.cuda.Stream(device=device) if pipelined else None
-        P_eff = partition_tokens or 1024
-        max_parts = -(-table_stride * bs // P_eff)
-        worst = PlanInfo(max_batch, bs, P_eff, 0, 0, max_batch * max_parts, 0, 0)
-        ws = decode_workspace_bytes(worst, num_q_heads, pool.desc.head_dim)
+        ws = int(self.lib.pkv_decode_workspace_bound(max_batch, table_stride * bs, bs, partition_tokens,
+                                                     num_q_heads, pool.desc.head_dim))
+        if ws == 0:
+            raise ValueError("bad decode geometry")
         # zeroed once: the decode's completion tickets start at zero and
         # every launch leaves them at zero
         self.workspace = torch.zeros(max(ws // 4, 1), dtype=torch.float32, device=device)
@@ -91,8 +91,8 @@ class DecodeIteration:
     def step(self, seqs, q, out, k_new, v_new, scale: float, stream=None, events=None,
              host_meta: bool = False) -> BatchLayout:
         """One whole iteration in one native call.  ``seqs``: int32 numpy
-        array (or sequence); ``events``: optional (before, after) torch events
-        recorded around the decode launch.  With ``host_meta`` the returned
+        array (or sequence); ``events``: optional (start, stop) torch events
+        attached to the decode dispatch (they time the kernel itself).  With ``host_meta`` the returned
         dict also holds host copies of the iteration's slots, pairs, tables
         and lengths."""
         seqs_np = seqs if isinstance(seqs, np.ndarray) and seqs.dtype == np.int32 else \

@@ -3,7 +3,8 @@
 import numpy as np
 import pytest
 
-from paged_kv_cache_257_amd import PkvError, decode_plan, decode_workspace_bytes
+from paged_kv_cache_257_amd import (PkvError, decode_plan, decode_workspace_bound,
+                                    decode_workspace_bytes, default_partition_tokens)
 from workloads import CONFIGS
 from workloads.configs import draw_decode_shapes
 
@@ -56,3 +57,26 @@ def test_plan_edge_cases():
         decode_plan(np.array([0]), 256, host_only=True)
     with pytest.raises(PkvError):
         decode_plan(np.array([5]), 24, host_only=True)
+
+
+def test_default_partition_and_workspace_bound():
+    P0 = default_partition_tokens(host_only=True)
+    assert P0 > 0 and P0 % 16 == 0
+    rng = np.random.default_rng(7)
+    for trial in range(200):
+        B = int(rng.integers(1, 40))
+        Lmax = int(rng.integers(1, 20000))
+        P = int(rng.choice([0, 16, 256, 2048]))
+        lens = rng.integers(1, Lmax + 1, size=B)
+        _, info = decode_plan(lens, P, host_only=True)
+        assert info.partition_tokens == (P or P0)
+        need = decode_workspace_bytes(info, 12, 64, host_only=True)
+        for nb in (B, B + 3):
+            assert decode_workspace_bound(nb, Lmax, 12, 64, P, host_only=True) >= need
+    # tight when every sequence has the maximum length
+    lens = np.full(9, 5000)
+    _, info = decode_plan(lens, 0, host_only=True)
+    assert decode_workspace_bound(9, 5000, 8, 128, 0, host_only=True) == \
+        decode_workspace_bytes(info, 8, 128, host_only=True)
+    with pytest.raises(ValueError):
+        decode_workspace_bound(4, 100, 8, 128, 24, host_only=True)
