@@ -14,6 +14,15 @@ computed here in float64:
 with scale = 1/sqrt(d) and, reading for grouped-query attention,
 g(h) = h // (H_q / H_kv) (contiguous groups of query heads share a KV head).
 
+Chunked prefill: a chunk of T new tokens appended after C cached ones
+(L = C + T) brings T queries; the query of chunk token t sits at position
+C + t and attends to positions 0 .. C + t of the same sequence, its own
+key included.  The lesson names the slicing of long prefills into chunks
+("PagedAttention e continuous batching", 01 · Conceito, the paragraph on
+the scheduler) without printing a mask; the causal reading is the plain
+one (a prompt token never sees later tokens, so slicing a prompt does not
+change any output).
+
 Split-K: a sequence's tokens cut into partitions of P tokens give per-
 partition (m_p, l_p, o~_p) = (max s, sum exp(s - m_p), sum exp(s - m_p) v);
 the exact combine is  o = sum_p e^{m_p - M} o~_p / sum_p e^{m_p - M} l_p
@@ -62,6 +71,24 @@ def decode_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) 
         m = np.max(s)
         p = np.exp(s - m)
         out[h] = (p @ V[:, g, :]) / np.sum(p)
+    return out
+
+
+def prefill_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """The queries of the last T tokens of a sequence, causally.
+
+    q: [T][H_q][d] float64 (the chunk's queries, in token order);
+    K, V: [L][H_kv][d] float64, the whole context including the chunk
+    (L >= T)  ->  [T][H_q][d].  Query t attends to K/V rows 0 .. L - T + t.
+    """
+    T = q.shape[0]
+    L = K.shape[0]
+    if T > L:
+        raise ValueError("the chunk is longer than the context")
+    C = L - T
+    out = np.empty(q.shape, dtype=np.float64)
+    for t in range(T):
+        out[t] = decode_attention(q[t], K[:C + t + 1], V[:C + t + 1], scale)
     return out
 
 

@@ -5,6 +5,12 @@ tokens from a pool whose free list starts in the seeded order; the context
 K/V rows, drawn in sequence order, are written at the returned slots; each
 sequence's query then attends over its L_i tokens.
 
+``PrefillRun``: chunked prefill of a set of prompts.  Per step, for every
+prompt with tokens left: allocate (first chunk) or append its next chunk's
+tokens, write their K/V rows at the returned slots, then each chunk query
+attends causally over the sequence as it now stands (gathered through the
+block table).
+
 ``PrefixSharedRun``: the continuous-batching loop.  Per iteration, in
 order: append one token to every live decoding sequence (ascending id) ->
 copy-on-write copies, then the new K/V rows at their slots -> decode every
@@ -24,7 +30,7 @@ from workloads.churn import (STREAM_ITER_BASE, STREAM_PREFIX_K, STREAM_PREFIX_V,
                              STREAM_TAIL_K, STREAM_TAIL_V, choose_churn)
 
 from .allocator import OracleAllocator
-from .attention import decode_attention, storage_to_f64
+from .attention import decode_attention, prefill_attention, storage_to_f64
 from .kvcache import MirrorPool
 
 
@@ -132,3 +138,55 @@ class PrefixSharedRun:
         dt = self.cfg.dtype
         return decode_attention(storage_to_f64(q_bits, dt), storage_to_f64(K, dt),
                                 storage_to_f64(V, dt), self.cfg.scale)
+
+
+class PrefillRun:
+    """Drives a ``workloads.prefill`` schedule through the oracle allocator
+    and a mirrored pool."""
+
+    def __init__(self, cfg, shapes, max_blocks_per_seq: int, values):
+        from workloads.prefill import prompt_offsets
+        self.cfg = cfg
+        self.shapes = shapes
+        self.alloc = OracleAllocator(shapes.num_blocks, cfg.block_size, max_blocks_per_seq,
+                                     shapes.free_order)
+        self.mirror = MirrorPool(shapes.num_blocks, cfg.num_kv_heads, cfg.head_dim,
+                                 STORAGE_NUMPY[cfg.dtype], cfg.block_size)
+        self.q, self.k, self.v = values
+        self.row0 = prompt_offsets(shapes.prompts)
+        self.step_index = 0
+
+    def append_step(self):
+        """Allocate / append the next chunk of every unfinished prompt and
+        write its K/V rows.  Returns [(seq, first token, tokens, slots)]."""
+        items = []
+        for seq, t0, n in self.shapes.steps[self.step_index]:
+            if t0 == 0:
+                sid, slots = self.alloc.alloc(n)
+                assert sid == seq
+            else:
+                slots = self.alloc.append(seq, n)
+            slots = np.asarray(slots, dtype=np.int64)
+            r = int(self.row0[seq]) + t0
+            self.mirror.write_kv(self.k[r:r + n], self.v[r:r + n], slots)
+            items.append((seq, t0, n, slots))
+        self.step_index += 1
+        return items
+
+    def attend(self, seq: int, t0: int, n: int, rows=None) -> np.ndarray:
+        """fp64 outputs [n][H_q][d] of chunk tokens t0 .. t0 + n - 1 of
+        ``seq`` (the sequence must hold exactly t0 + n tokens).  ``rows``
+        (optional) picks a subset of the chunk's tokens; the result then
+        has len(rows) entries."""
+        L = self.alloc.length(seq)
+        assert L == t0 + n
+        K, V = self.mirror.gather(self.alloc.table(seq), L)
+        dt = self.cfg.dtype
+        r = int(self.row0[seq]) + t0
+        q = storage_to_f64(self.q[r:r + n], dt)
+        K, V = storage_to_f64(K, dt), storage_to_f64(V, dt)
+        if rows is None:
+            return prefill_attention(q, K, V, self.cfg.scale)
+        C = L - n
+        return np.stack([decode_attention(q[t], K[:C + t + 1], V[:C + t + 1], self.cfg.scale)
+                         for t in rows])
