@@ -207,6 +207,42 @@ size_t pkv_decode_workspace_bound(int32_t max_seqs, int32_t max_context_len, int
 int32_t pkv_default_partition_tokens(void);
 
 /* ---------------------------------------------------------------------------
+ * Host: chunked-prefill plan
+ * ------------------------------------------------------------------------ */
+
+/* Work list of a chunked-prefill launch ("PagedAttention e continuous
+ * batching", 01 · Conceito, the scheduler paragraph: long prefills are cut
+ * into slices).  Sequence i brings q_lens[i] >= 1 new tokens that are the
+ * last q_lens[i] of its context_lens[i] tokens (already appended and
+ * written).  A work item is one tile of tile_tokens consecutive query
+ * tokens of one sequence; the kernel runs every item for every KV head.
+ * tile_tokens is 64 / Gw with Gw the largest power of two <= 16 dividing
+ * H_q / H_kv (Gw query heads of one KV head share a tile).  Items are
+ * ordered by decreasing number of keys they attend.
+ *
+ * plan (host int32, cap >= pkv_prefill_plan_ints(...)) receives
+ *   [0, 2*n_work)                      items (sequence, tile index)
+ *   [2*n_work, 2*n_work + num_seqs + 1) q_start: first query row of each
+ *                                       sequence in q / out (prefix sums)
+ * Upload it unchanged and pass the device copy to pkv_paged_prefill. */
+typedef struct {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t tile_tokens;
+  int32_t n_work;
+  int32_t total_q;
+  int32_t max_context_len;
+  int32_t plan_ints;
+} pkv_prefill_plan_info;
+
+pkv_status pkv_prefill_plan_ints(const int32_t* q_lens, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t* plan_ints);
+pkv_status pkv_prefill_plan(const int32_t* q_lens, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t* plan, int32_t cap,
+                            pkv_prefill_plan_info* info);
+
+/* ---------------------------------------------------------------------------
  * Host: one decode iteration's metadata in one staging buffer
  * ------------------------------------------------------------------------ */
 
@@ -363,6 +399,23 @@ pkv_status pkv_paged_decode_reduce(const pkv_pool* pool, const void* q, const vo
                                    int32_t table_stride, const int32_t* context_lens, float scale,
                                    const int32_t* plan, const pkv_decode_plan_info* info,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Causal attention of chunked-prefill queries through the block tables:
+ * query t of sequence i (row q_start[i] + t of q and out) sits at position
+ * context_lens[i] - q_lens[i] + t and attends to that sequence's positions
+ * 0 .. that position ("PagedAttention e continuous batching", 01 · Conceito:
+ * the kernel reads through the block table, paragraph 5; long prefills are
+ * sliced, the scheduler paragraph).  The chunk's K/V must already be in the
+ * pool (pkv_seq_append / pkv_write_kv).  q: device [total_q][H_q][head_dim]
+ * in the pool dtype; out: device fp32 [total_q][H_q][head_dim]; block_tables
+ * / context_lens as for decode; plan / info from pkv_prefill_plan (plan
+ * uploaded).  fp16 and bf16 pools, head_dim 64 or 128 (else
+ * PKV_E_UNSUPPORTED); the products run on the matrix cores with fp32
+ * accumulation.  Asynchronous on `stream`; allocates nothing. */
+pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, float* out, int32_t num_seqs,
+                             int32_t num_q_heads, const int32_t* block_tables, int32_t table_stride,
+                             const int32_t* context_lens, float scale, const int32_t* plan,
+                             const pkv_prefill_plan_info* info, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,8 +27,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")
 ARCH = "gfx950"
 
-HOST_SOURCES = ["host/pool.cpp", "host/plan.cpp", "host/prepare.cpp"]
-HIP_SOURCES = ["kernels/kv_write.hip", "kernels/paged_decode.hip", "kernels/stepper.cpp"]
+HOST_SOURCES = ["host/pool.cpp", "host/plan.cpp", "host/prepare.cpp", "host/prefill_plan.cpp"]
+HIP_SOURCES = ["kernels/kv_write.hip", "kernels/paged_decode.hip", "kernels/paged_prefill.hip",
+               "kernels/stepper.cpp"]
 
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -110,6 +110,10 @@ inline int dtype_bytes(int32_t dt) { return dt == PKV_F32 ? 4 : 2; }
 // partitions add combine work and more workgroups than the chip needs.
 constexpr int32_t kDefaultPartitionTokens = 2048;
 
+// Query rows (token, head pairs) of one chunked-prefill workgroup: four
+// waves of 16 rows each.
+constexpr int32_t kPrefillTileRows = 64;
+
 // Live sequence with this id, or null.
 inline pkv_seq_state* find_seq(pkv_pool* p, int32_t id) {
   const int32_t s = p->index.find(id);

@@ -1,0 +1,402 @@
+// Chunked paged prefill attention for gfx950, on the matrix cores.
+//
+// A chunk of T new tokens of a sequence, appended after C cached ones
+// (L = C + T), brings T queries; query t sits at position C + t and attends
+// causally to positions 0 .. C + t of its sequence, reading K/V through the
+// block table ("PagedAttention e continuous batching", 01 · Conceito:
+// the kernel follows the block table, paragraph 5; long prefills are cut
+// into slices, the scheduler paragraph).  Unlike decode, many queries share
+// every K/V tile, so the products are dense contractions and run as MFMA.
+//
+// Work decomposition.  A workgroup of 4 waves takes one tile of query rows
+// of one sequence and one KV head: 64 rows = (token, head) pairs, where the
+// Gw query heads of that KV head that share the tile are packed into the
+// rows (Gw = 1 for MHA: 64 tokens of one head; Gw = 4 for GQA-4: 16 tokens
+// x 4 heads).  Each wave owns 16 rows.  The workgroup walks the sequence's
+// keys in stages of 32 tokens (two blocks) up to its last query's position.
+//
+// Per stage.  All 256 threads stage the two K tiles into LDS as they are
+// (rows padded by 16 bytes against bank conflicts) and the two V tiles
+// transposed (V^T, d-major), while the previous stage is computed.  A wave
+// then forms S^T = K Q^T with v_mfma_f32_16x16x32_{f16,bf16}: K from LDS is
+// the A operand (lane = 16 g + n holds token n, d-chunk 8 g), Q^T from
+// registers the B operand (query row n, d-chunk 8 g), and the accumulator
+// leaves lane (g, n) with tokens 4 g .. 4 g + 3 of each block for query row
+// n.  That is the B-operand layout of the next product, so after the online
+// softmax (base 2, one state per query row held by the four lanes of the
+// row) P^T goes straight into O^T += V^T P^T, with V^T from LDS as the A
+// operand (slot order: the 4 tokens of the first block, then the 4 of the
+// second, on both sides).  Masking: keys past the query's position or past
+// the context get -inf; V rows past the context are staged as zeros, so
+// stale or NaN slots never reach the output.
+//
+// Precision.  Products of 16-bit inputs accumulate in fp32.  The softmax
+// weights must become 16-bit MFMA operands: for fp16 they are rounded to
+// fp16 (11-bit significand); for bf16 they are split into a bf16 head and a
+// bf16 remainder (two MFMAs, ~16 bits), since bf16 weights alone put the
+// error of short contexts above 2e-3.  The normaliser sums the weights as
+// rounded, so the output is an exactly normalised mix of V rows.
+#include "device_common.h"
+
+namespace pkv {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = kWave * kPfWaves;
+constexpr int kStage = 32;  // key tokens per stage (two blocks)
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kNegBig = -3.0e38f;  // finite "no key yet" running max
+
+struct PrefillParams {
+  const char* q;             // [total_q][H_q][D]
+  float* out;                // [total_q][H_q][D]
+  const char* k_cache;
+  const char* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* work;       // [n_work][2] (sequence, tile)
+  const int32_t* q_start;    // [num_seqs + 1]
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;             // H_q / H_kv
+  int32_t hgroups_per_kv;    // group / Gw
+  int32_t table_stride;
+  int32_t num_blocks;
+  float scale_log2;
+};
+
+template <int DT>
+__device__ __forceinline__ f4 mfma32(const u32x4& a, const u32x4& b, const f4& c);
+
+template <>
+__device__ __forceinline__ f4 mfma32<PKV_F16>(const u32x4& a, const u32x4& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b),
+                                                c, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f4 mfma32<PKV_BF16>(const u32x4& a, const u32x4& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b),
+                                                 c, 0, 0, 0);
+}
+
+// Round an fp32 value to the 16-bit type (nearest even): returns the bits
+// and, in *back, the rounded value as fp32.
+template <int DT>
+__device__ __forceinline__ uint32_t round16(float x, float* back);
+
+template <>
+__device__ __forceinline__ uint32_t round16<PKV_F16>(float x, float* back) {
+  const _Float16 h = static_cast<_Float16>(x);
+  *back = static_cast<float>(h);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+template <>
+__device__ __forceinline__ uint32_t round16<PKV_BF16>(float x, float* back) {
+  const __bf16 h = static_cast<__bf16>(x);
+  *back = static_cast<float>(h);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+template <int DT, int D, int GW>
+__global__ __launch_bounds__(kPfThreads) void paged_prefill_kernel(const PrefillParams p) {
+  constexpr int TPW = 16 / GW;             // query tokens per wave
+  constexpr int TQ = kPfWaves * TPW;       // query tokens per workgroup
+  constexpr int CH = D / 8;                // 16-byte chunks per row
+  constexpr int ROWB = D * 2;              // bytes per token row of one head
+  constexpr int TILE = kBlockTokens * ROWB;
+  constexpr int KROW = D + 8;              // K row stride in LDS (16-bit elements)
+  constexpr int VROW = kStage + 4;         // V^T row stride in LDS
+  constexpr int KL = kStage * CH / kPfThreads;  // K chunks each thread stages
+  constexpr int VPAIRS = CH * (kStage / 2);     // (chunk, token pair) items of V
+  constexpr int KT = D / 32;               // k-steps of S^T = K Q^T
+  constexpr int NDT = D / 16;              // d-tiles of O^T
+  static_assert(KL >= 1 && KL * kPfThreads == kStage * CH, "staging split");
+  static_assert(VPAIRS <= kPfThreads, "one V pair per thread");
+
+  __shared__ __attribute__((aligned(16))) uint16_t lk[2][kStage * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t lv[2][D * VROW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int hgroups = p.num_kv_heads * p.hgroups_per_kv;
+  const int wi = blockIdx.x / hgroups;
+  const int hg = blockIdx.x - wi * hgroups;
+  const int seq = p.work[2 * wi];
+  const int tile = p.work[2 * wi + 1];
+  const int kvh = hg / p.hgroups_per_kv;
+  const int qh0 = kvh * p.group + (hg - kvh * p.hgroups_per_kv) * GW;
+  const int L = p.context_lens[seq];
+  const int qs = p.q_start[seq];
+  const int T = p.q_start[seq + 1] - qs;
+  const int C = L - T;
+  const int t0 = tile * TQ;
+  const int nblk = min((L + kBlockTokens - 1) / kBlockTokens, p.table_stride);
+  const int32_t* trow = p.block_tables + int64_t(seq) * p.table_stride;
+  const int64_t blk_stride = int64_t(p.num_kv_heads) * TILE;
+  const char* kbase = p.k_cache + int64_t(kvh) * TILE;
+  const char* vbase = p.v_cache + int64_t(kvh) * TILE;
+
+  // this lane's query row: token tq of the chunk, head h
+  const int tq = t0 + wave * TPW + n / GW;
+  const int h = qh0 + n % GW;
+  const bool row_ok = tq < T;
+  const int qpos = C + tq;
+  const int wave_first = t0 + wave * TPW;
+  const int wave_last = min(wave_first + TPW, T) - 1;  // < wave_first: no rows
+  const int wg_last = min(t0 + TQ, T) - 1;
+  const int wg_stages = (C + wg_last) / kStage + 1;
+  const int wave_stages = wave_last >= wave_first ? (C + wave_last) / kStage + 1 : 0;
+  const int mask_from = (C + wave_first) / kStage;  // first stage with a masked key
+
+  u32x4 qb[KT];
+  {
+    const char* qrow = p.q + (int64_t(qs + (row_ok ? tq : 0)) * p.num_q_heads + h) * ROWB;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+      qb[kt] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + (32 * kt + 8 * g) * 2)
+                      : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // ---- staging: global -> registers -> LDS ----------------------------------
+  u32x4 kr[KL];
+  u32x4 vr0 = {0u, 0u, 0u, 0u}, vr1 = {0u, 0u, 0u, 0u};
+  auto tile_rsrc = [&](const char* base, int b) __attribute__((always_inline)) {
+    const int blk = b < nblk ? trow[b] : -1;
+    const bool ok = unsigned(blk) < unsigned(p.num_blocks);
+    return make_rsrc(base + (ok ? int64_t(blk) * blk_stride : 0), ok ? TILE : 0);
+  };
+  auto load_stage = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int idx = tid + i * kPfThreads;
+      const int tok = idx / CH, ch = idx - (idx / CH) * CH;
+      const auto rs = tile_rsrc(kbase, st * 2 + tok / kBlockTokens);
+      kr[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (tok % kBlockTokens) * ROWB + ch * 16, 0, 0));
+    }
+    if (tid < VPAIRS) {
+      const int ch = tid % CH, tok = 2 * (tid / CH);
+      const auto rs = tile_rsrc(vbase, st * 2 + tok / kBlockTokens);
+      const int off = (tok % kBlockTokens) * ROWB + ch * 16;
+      vr0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+      vr1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + ROWB, 0, 0));
+    }
+  };
+  auto store_stage = [&](int buf, int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int idx = tid + i * kPfThreads;
+      const int tok = idx / CH, ch = idx - (idx / CH) * CH;
+      *reinterpret_cast<u32x4*>(&lk[buf][tok * KROW + ch * 8]) = kr[i];
+    }
+    if (tid < VPAIRS) {
+      const int ch = tid % CH, tok = 2 * (tid / CH);
+      const int kp = st * kStage + tok;
+      const uint32_t z0 = kp < L ? 0xFFFFFFFFu : 0u;  // rows past the context -> 0
+      const uint32_t z1 = kp + 1 < L ? 0xFFFFFFFFu : 0u;
+      const uint32_t a[4] = {vr0.x & z0, vr0.y & z0, vr0.z & z0, vr0.w & z0};
+      const uint32_t b[4] = {vr1.x & z1, vr1.y & z1, vr1.z & z1, vr1.w & z1};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t ea = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const uint32_t eb = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        *reinterpret_cast<uint32_t*>(&lv[buf][(ch * 8 + e) * VROW + tok]) = ea | (eb << 16);
+      }
+    }
+  };
+
+  // ---- compute ----------------------------------------------------------------
+  float m = kNegBig, lsum = 0.f;
+  f4 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf, int st) __attribute__((always_inline)) {
+    f4 sa[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      sa[blk] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&lk[buf][(blk * 16 + n) * KROW + 32 * kt + 8 * g]);
+        sa[blk] = mfma32<DT>(a, qb[kt], sa[blk]);
+      }
+    }
+    float s[8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s[blk * 4 + v] = sa[blk][v] * p.scale_log2;
+    // blocks outside the pool contribute nothing (wave-uniform)
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int b = st * 2 + blk;
+      const int id = b < nblk ? trow[b] : -1;
+      if (!(unsigned(id) < unsigned(p.num_blocks)))
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s[blk * 4 + v] = -INFINITY;
+    }
+    if (st >= mask_from) {  // causal / context mask (wave-uniform branch)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int kp = st * kStage + blk * 16 + 4 * g + v;
+          if (kp > qpos || kp >= L) s[blk * 4 + v] = -INFINITY;
+        }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    uint32_t ph[4], pl[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x0 = __builtin_amdgcn_exp2f(s[2 * j] - mn);
+      const float x1 = __builtin_amdgcn_exp2f(s[2 * j + 1] - mn);
+      float r0, r1;
+      ph[j] = round16<DT>(x0, &r0) | (round16<DT>(x1, &r1) << 16);
+      psum += r0 + r1;
+      if constexpr (DT == PKV_BF16) {
+        float e0, e1;
+        pl[j] = round16<DT>(x0 - r0, &e0) | (round16<DT>(x1 - r1, &e1) << 16);
+        psum += e0 + e1;
+      }
+    }
+    lsum = lsum * alpha + psum;
+    const u32x4 pb = {ph[0], ph[1], ph[2], ph[3]};
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      o[dt] *= alpha;
+      const uint16_t* vrow = &lv[buf][(dt * 16 + n) * VROW];
+      const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + 4 * g);
+      const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + 16 + 4 * g);
+      const u32x4 a = {a0.x, a0.y, a1.x, a1.y};
+      o[dt] = mfma32<DT>(a, pb, o[dt]);
+      if constexpr (DT == PKV_BF16) {
+        const u32x4 pbl = {pl[0], pl[1], pl[2], pl[3]};
+        o[dt] = mfma32<DT>(a, pbl, o[dt]);
+      }
+    }
+  };
+
+  load_stage(0);
+  store_stage(0, 0);
+  __syncthreads();
+  for (int st = 0; st < wg_stages; ++st) {
+    const int buf = st & 1;
+    const bool more = st + 1 < wg_stages;
+    if (more) load_stage(st + 1);
+    if (st < wave_stages) compute(buf, st);
+    if (more) store_stage(buf ^ 1, st + 1);
+    __syncthreads();
+  }
+
+  float lt = lsum + __shfl_xor(lsum, 16);
+  lt += __shfl_xor(lt, 32);
+  if (row_ok) {
+    const float inv = 1.f / lt;
+    float* orow = p.out + (int64_t(qs + tq) * p.num_q_heads + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<f4*>(orow + dt * 16 + 4 * g) = o[dt] * inv;
+  }
+}
+
+typedef void (*PrefillFn)(const PrefillParams);
+
+template <int DT, int D>
+PrefillFn pick_gw(int gw) {
+  switch (gw) {
+    case 1: return paged_prefill_kernel<DT, D, 1>;
+    case 2: return paged_prefill_kernel<DT, D, 2>;
+    case 4: return paged_prefill_kernel<DT, D, 4>;
+    case 8: return paged_prefill_kernel<DT, D, 8>;
+    case 16: return paged_prefill_kernel<DT, D, 16>;
+  }
+  return nullptr;
+}
+
+PrefillFn pick_prefill(int32_t dtype, int32_t head_dim, int gw) {
+  if (dtype == PKV_F16) {
+    if (head_dim == 64) return pick_gw<PKV_F16, 64>(gw);
+    if (head_dim == 128) return pick_gw<PKV_F16, 128>(gw);
+  } else if (dtype == PKV_BF16) {
+    if (head_dim == 64) return pick_gw<PKV_BF16, 64>(gw);
+    if (head_dim == 128) return pick_gw<PKV_BF16, 128>(gw);
+  }
+  return nullptr;
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, float* out,
+                                        int32_t num_seqs, int32_t num_q_heads,
+                                        const int32_t* block_tables, int32_t table_stride,
+                                        const int32_t* context_lens, float scale, const int32_t* plan,
+                                        const pkv_prefill_plan_info* info, void* stream) {
+  if (!pool) return fail(PKV_E_BAD_ARG, "null pool");
+  const pkv_pool_desc& d = pool->desc;
+  if (!pool->k_cache || !pool->v_cache) return fail(PKV_E_BAD_ARG, "pool has no device K/V arrays");
+  if (d.block_size != kBlockTokens) return fail(PKV_E_UNSUPPORTED, "device kernels take block_size 16 only");
+  if (d.dtype != PKV_F16 && d.dtype != PKV_BF16)
+    return fail(PKV_E_UNSUPPORTED, "paged prefill takes fp16 or bf16 pools");
+  if (d.head_dim != 64 && d.head_dim != 128)
+    return fail(PKV_E_UNSUPPORTED, "paged prefill takes head_dim 64 or 128");
+  if (!info) return fail(PKV_E_BAD_ARG, "null plan info");
+  if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0)
+    return fail(PKV_E_BAD_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+  const int group = num_q_heads / d.num_kv_heads;
+  int gw = 1;
+  while (gw < 16 && group % (2 * gw) == 0) gw *= 2;
+  if (info->num_seqs != num_seqs || info->num_q_heads != num_q_heads ||
+      info->num_kv_heads != d.num_kv_heads || info->tile_tokens != kPrefillTileRows / gw ||
+      info->n_work < 0)
+    return fail(PKV_E_BAD_ARG, "plan info does not match this batch");
+  if (table_stride < 1) return fail(PKV_E_BAD_ARG, "table_stride must be >= 1");
+  if (int64_t(info->max_context_len) > int64_t(table_stride) * kBlockTokens)
+    return fail(PKV_E_BAD_ARG, "a context is longer than its table can address");
+  if (num_seqs == 0 || info->n_work == 0) return PKV_OK;
+  if (!q || !out || !block_tables || !context_lens || !plan)
+    return fail(PKV_E_BAD_ARG, "null device pointer");
+  PrefillParams prm;
+  prm.q = static_cast<const char*>(q);
+  prm.out = out;
+  prm.k_cache = static_cast<const char*>(pool->k_cache);
+  prm.v_cache = static_cast<const char*>(pool->v_cache);
+  prm.block_tables = block_tables;
+  prm.context_lens = context_lens;
+  prm.work = plan;
+  prm.q_start = plan + 2 * int64_t(info->n_work);
+  prm.num_q_heads = num_q_heads;
+  prm.num_kv_heads = d.num_kv_heads;
+  prm.group = group;
+  prm.hgroups_per_kv = group / gw;
+  prm.table_stride = table_stride;
+  prm.num_blocks = d.num_blocks;
+  prm.scale_log2 = scale * kLog2eF;
+  const int64_t grid = int64_t(info->n_work) * d.num_kv_heads * (group / gw);
+  if (grid > INT32_MAX) return fail(PKV_E_BAD_ARG, "batch too large for one launch");
+  PrefillFn fn = pick_prefill(d.dtype, d.head_dim, gw);
+  if (!fn) return fail(PKV_E_UNSUPPORTED, "no prefill kernel for this dtype / head_dim / group");
+  hipLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kPfThreads), 0, static_cast<hipStream_t>(stream), prm);
+  return launch_status("paged_prefill launch");
+}

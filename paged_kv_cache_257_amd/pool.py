@@ -12,7 +12,7 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 from . import _capi
-from ._capi import PlanInfo, PoolDesc, Stats, check, i32p, i64p
+from ._capi import PlanInfo, PoolDesc, PrefillPlanInfo, Stats, check, i32p, i64p
 
 
 def _stream_ptr(stream) -> Optional[int]:
@@ -175,6 +175,34 @@ class Pool:
             check(self.lib, self.lib.pkv_paged_decode_reduce(*args))
         else:
             check(self.lib, self.lib.pkv_paged_decode(*args))
+
+
+    def paged_prefill(self, q, out, block_tables, context_lens, scale: float, plan,
+                      info: PrefillPlanInfo, stream=None) -> None:
+        """Causal attention of chunked-prefill queries (see pkv_paged_prefill).
+
+        q: device [total_q][H_q][d] (pool dtype); out: device fp32, same
+        shape; ``plan``/``info`` from ``prefill_plan`` (plan on the device)."""
+        Hq = int(q.shape[1])
+        check(self.lib, self.lib.pkv_paged_prefill(
+            self.handle, _dptr(q), _dptr(out), int(info.num_seqs), Hq, _dptr(block_tables),
+            int(block_tables.shape[1]), _dptr(context_lens), float(scale), _dptr(plan),
+            C.byref(info), _stream_ptr(stream)))
+
+
+def prefill_plan(q_lens, context_lens, num_q_heads: int, num_kv_heads: int,
+                 host_only: bool = False) -> Tuple[np.ndarray, PrefillPlanInfo]:
+    """Host work list of a chunked-prefill launch (see pkv_prefill_plan)."""
+    lib = _capi.load(host_only=host_only)
+    ql = np.ascontiguousarray(q_lens, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    n = C.c_int32()
+    check(lib, lib.pkv_prefill_plan_ints(i32p(ql), len(ql), num_q_heads, num_kv_heads, C.byref(n)))
+    plan = np.empty(max(n.value, 1), dtype=np.int32)
+    info = PrefillPlanInfo()
+    check(lib, lib.pkv_prefill_plan(i32p(ql), i32p(cl), len(ql), num_q_heads, num_kv_heads,
+                                    i32p(plan), len(plan), C.byref(info)))
+    return plan[:info.plan_ints], info
 
 
 def decode_plan(context_lens: np.ndarray, partition_tokens: int = 0, block_size: int = 16,

@@ -1,0 +1,181 @@
+"""GPU parity of chunked paged prefill (pkv_paged_prefill) against the oracle.
+
+Each workload's chunk schedule runs on both sides: the C++ allocator and
+the oracle allocator hand out the same slots (checked bit for bit), the
+chunk's K/V go into the pool with write_kv, and the prefill kernel's fp32
+outputs are compared with the oracle's float64 causal attention.  The tiny
+workloads compare every output; the 30,000-token prompt and the 16-prompt
+GQA batch run at their full size and compare a seeded sample of rows of
+every step (first, last and random tokens of each chunk), which the oracle
+computes one query at a time.  Tolerance: 2e-3 max-abs for 16-bit inputs.
+Also: NaN-filled pools (stale slots must not leak), a sweep of cached
+lengths / chunk lengths / head groupings, and the unsupported dtype.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.runs import PrefillRun
+from paged_kv_cache_257_amd import PkvError, Pool, prefill_plan
+from tests.gpu_helpers import TOL, TORCH_DTYPE, sync, to_device
+from workloads.prefill import (PrefillConfig, draw_prefill_shapes, draw_prefill_values,
+                               prefill_config_by_name, prompt_offsets)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+class PrefillCase:
+    """A prefill schedule on the HIP path and on the oracle, step by step."""
+
+    def __init__(self, cfg, shapes=None, fill=0.0, values=None):
+        self.cfg = cfg
+        self.sh = shapes or draw_prefill_shapes(cfg)
+        self.vals = values or draw_prefill_values(cfg, self.sh.prompts)
+        self.width = -(-int(self.sh.prompts.max()) // 16)
+        H, d, dt = cfg.num_kv_heads, cfg.head_dim, cfg.dtype
+        shape = (self.sh.num_blocks, H, 16, d)
+        self.k_cache = torch.full(shape, fill, dtype=TORCH_DTYPE[dt], device="cuda")
+        self.v_cache = torch.full(shape, fill, dtype=TORCH_DTYPE[dt], device="cuda")
+        self.pool = Pool(self.sh.num_blocks, H, d, dt, self.width, 16, self.sh.free_order,
+                         self.k_cache, self.v_cache)
+        self.ora = PrefillRun(cfg, self.sh, self.width, self.vals)
+        self.row0 = prompt_offsets(self.sh.prompts)
+        self.q_dev = to_device(self.vals[0], dt)
+        self.k_dev = to_device(self.vals[1], dt)
+        self.v_dev = to_device(self.vals[2], dt)
+
+    def step(self):
+        """Run the next step on both sides; returns (items, device out [total_q][H_q][d])."""
+        items = self.ora.append_step()
+        seqs, q_rows, kv_rows, slots = [], [], [], []
+        for seq, t0, n, s_o in items:
+            if t0 == 0:
+                sid, s = self.pool.alloc(n)
+                assert sid == seq
+            else:
+                s = self.pool.append(seq, n)
+            assert np.array_equal(s, s_o)
+            seqs.append(seq)
+            r = int(self.row0[seq]) + t0
+            q_rows.append(np.arange(r, r + n))
+            slots.append(s)
+        rows = torch.from_numpy(np.concatenate(q_rows)).cuda()
+        slot_t = torch.from_numpy(np.concatenate(slots)).cuda()
+        self.pool.write_kv(self.k_dev.index_select(0, rows), self.v_dev.index_select(0, rows), slot_t)
+        tables, lens = self.pool.build_batch(seqs, self.width)
+        q_lens = np.array([n for _, _, n, _ in items])
+        plan, info = prefill_plan(q_lens, lens, self.cfg.num_q_heads, self.cfg.num_kv_heads)
+        out = torch.full((int(q_lens.sum()), self.cfg.num_q_heads, self.cfg.head_dim), float("nan"),
+                         dtype=torch.float32, device="cuda")
+        self.pool.paged_prefill(self.q_dev.index_select(0, rows), out, torch.from_numpy(tables).cuda(),
+                                torch.from_numpy(lens).cuda(), self.cfg.scale,
+                                torch.from_numpy(plan).cuda(), info)
+        return items, out
+
+    def close(self):
+        self.pool.close()
+
+
+def run_full(cfg, fill=0.0):
+    case = PrefillCase(cfg, fill=fill)
+    try:
+        worst = 0.0
+        for k in range(len(case.sh.steps)):
+            items, out = case.step()
+            sync()
+            got = out.cpu().numpy().astype(np.float64)
+            pos = 0
+            for seq, t0, n, _ in items:
+                ref = case.ora.attend(seq, t0, n)
+                err = float(np.max(np.abs(got[pos:pos + n] - ref)))
+                worst = max(worst, err)
+                assert err <= TOL[cfg.dtype], (cfg.name, k, seq, t0, n, err)
+                pos += n
+        return worst
+    finally:
+        case.close()
+
+
+@pytest.mark.parametrize("name", ["pf_tiny_f16", "pf_tiny_gqa_bf16"])
+def test_tiny_workloads_every_output(name):
+    cfg = prefill_config_by_name(name)
+    worst = run_full(cfg)
+    print(f"\n[gpu] prefill {name}: max_err={worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["pf_tiny_f16", "pf_tiny_gqa_bf16"])
+def test_nan_filled_pool(name):
+    cfg = prefill_config_by_name(name)
+    worst = run_full(cfg, fill=float("nan"))
+    print(f"\n[gpu] prefill {name} NaN pool: max_err={worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["pf_batch_bf16", "pf_long_f16"])
+def test_full_size_sampled_rows(name):
+    cfg = prefill_config_by_name(name)
+    case = PrefillCase(cfg)
+    rng = np.random.default_rng(cfg.seed + 5)
+    try:
+        worst = 0.0
+        for k in range(len(case.sh.steps)):
+            print(f"[gpu] prefill {name} step {k}", flush=True)
+            items, out = case.step()
+            sync()
+            pos = 0
+            for idx, (seq, t0, n, _) in enumerate(items):
+                if len(items) > 4 and idx % 4 != k % 4:  # a quarter of the sequences per step
+                    pos += n
+                    continue
+                rows = sorted({0, n - 1, *rng.integers(0, n, size=3).tolist()})
+                got = out[pos:pos + n].cpu().numpy().astype(np.float64)[rows]
+                ref = case.ora.attend(seq, t0, n, rows=rows)
+                err = float(np.max(np.abs(got - ref)))
+                worst = max(worst, err)
+                assert err <= TOL[cfg.dtype], (name, k, seq, t0, n, err)
+                pos += n
+        print(f"[gpu] prefill {name}: {len(case.sh.steps)} steps, sampled max_err={worst:.3e}",
+              flush=True)
+    finally:
+        case.close()
+
+
+SWEEP = [
+    # (dtype, H_q, H_kv, d, prompts, chunk)
+    ("f16", 8, 8, 128, (1, 2, 31, 32, 33), 7),
+    ("bf16", 16, 4, 64, (100, 65), 64),
+    ("f16", 24, 8, 128, (70, 3), 40),       # group 3 -> one head per tile row
+    ("bf16", 32, 2, 128, (45,), 45),        # group 16
+    ("f16", 64, 2, 64, (90, 17), 33),       # group 32 -> two head groups of 16
+    ("bf16", 4, 4, 128, (300,), 300),       # one chunk, many tiles
+    ("f16", 2, 2, 64, (129, 1, 64), 128),
+]
+
+
+@pytest.mark.parametrize("dt,Hq,Hkv,d,prompts,chunk", SWEEP)
+def test_shape_sweep(dt, Hq, Hkv, d, prompts, chunk):
+    cfg = PrefillConfig(name="sweep", index=20, dtype=dt, num_q_heads=Hq, num_kv_heads=Hkv,
+                        head_dim=d, chunk_tokens=chunk, fixed_prompts=tuple(prompts))
+    worst = run_full(cfg)
+    print(f"\n[gpu] prefill sweep {dt} {Hq}/{Hkv} d={d} {prompts} chunk={chunk}: max_err={worst:.3e}",
+          flush=True)
+
+
+def test_unsupported_dtype_is_refused():
+    cfg = dataclasses.replace(prefill_config_by_name("pf_tiny_f16"), dtype="f32")
+    sh = draw_prefill_shapes(cfg)
+    kc = torch.zeros((sh.num_blocks, 4, 16, 64), dtype=torch.float32, device="cuda")
+    pool = Pool(sh.num_blocks, 4, 64, "f32", 8, 16, sh.free_order, kc, kc.clone())
+    try:
+        plan, info = prefill_plan([5], [5], 4, 4)
+        q = torch.zeros((5, 4, 64), dtype=torch.float32, device="cuda")
+        with pytest.raises(PkvError) as e:
+            pool.paged_prefill(q, q.clone(), torch.zeros((1, 8), dtype=torch.int32, device="cuda"),
+                               torch.tensor([5], dtype=torch.int32, device="cuda"), 0.125,
+                               torch.from_numpy(plan).cuda(), info)
+        assert e.value.kind == "unsupported"
+    finally:
+        pool.close()

@@ -1,0 +1,60 @@
+"""The host chunked-prefill work list (pkv_prefill_plan), checked by enumeration (CPU)."""
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_257_amd import PkvError, prefill_plan
+from workloads.prefill import PREFILL_CONFIGS, draw_prefill_shapes
+
+
+def tile_for(Hq, Hkv):
+    G = Hq // Hkv
+    gw = 1
+    while gw < 16 and G % (2 * gw) == 0:
+        gw *= 2
+    return 64 // gw
+
+
+def check(q_lens, ctx, Hq, Hkv):
+    plan, info = prefill_plan(q_lens, ctx, Hq, Hkv, host_only=True)
+    B = len(q_lens)
+    tile = tile_for(Hq, Hkv)
+    assert info.tile_tokens == tile
+    nw = info.n_work
+    work = plan[:2 * nw].reshape(nw, 2)
+    want = sorted((i, j) for i in range(B) for j in range(-(-int(q_lens[i]) // tile)))
+    assert sorted(map(tuple, work.tolist())) == want
+    cost = [int(ctx[s]) - int(q_lens[s]) + min((j + 1) * tile, int(q_lens[s])) for s, j in work.tolist()]
+    assert cost == sorted(cost, reverse=True)
+    q_start = plan[2 * nw:2 * nw + B + 1]
+    assert q_start.tolist() == [0] + np.cumsum(q_lens).tolist()
+    assert info.total_q == int(np.sum(q_lens)) and info.max_context_len == int(max(ctx))
+    assert info.plan_ints == 2 * nw + B + 1 == len(plan)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (32, 8), (12, 4), (48, 2), (6, 1)])
+def test_plan_enumerates_tiles_longest_first(Hq, Hkv):
+    rng = np.random.default_rng(Hq * 10 + Hkv)
+    q_lens = rng.integers(1, 300, size=9)
+    ctx = q_lens + rng.integers(0, 5000, size=9)
+    check(q_lens, ctx, Hq, Hkv)
+
+
+def test_plan_for_every_workload_step():
+    for cfg in PREFILL_CONFIGS:
+        sh = draw_prefill_shapes(cfg)
+        for step in sh.steps:
+            q_lens = np.array([n for _, _, n in step])
+            ctx = np.array([t0 + n for _, t0, n in step])
+            check(q_lens, ctx, cfg.num_q_heads, cfg.num_kv_heads)
+
+
+def test_plan_errors():
+    with pytest.raises(PkvError):
+        prefill_plan([0], [5], 4, 4, host_only=True)
+    with pytest.raises(PkvError):
+        prefill_plan([6], [5], 4, 4, host_only=True)
+    with pytest.raises(PkvError):
+        prefill_plan([3], [5], 6, 4, host_only=True)
+    plan, info = prefill_plan([], [], 4, 4, host_only=True)
+    assert info.n_work == 0 and plan.tolist() == [0]
