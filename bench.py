@@ -319,6 +319,127 @@ def bench_prefix_shared(args, cfg):
     return 0
 
 
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix-core peak
+
+
+def prefill_flops(q_len: int, ctx_len: int, num_q_heads: int, head_dim: int) -> int:
+    """Algorithmic flops of causal attention for one chunk: every (query,
+    visible key) pair costs 2 d for q.k and 2 d for p.v, per query head."""
+    C = ctx_len - q_len
+    pairs = q_len * C + q_len * (q_len + 1) // 2
+    return 4 * head_dim * num_q_heads * pairs
+
+
+def bench_prefill(args, cfg):
+    """Chunked prefill of a workload's prompts.  All chunks' K/V are written
+    first (blocks never move once allocated, so step k's tables are the
+    prefix of the final ones); a bench step is then the whole chunk
+    schedule, one prefill launch per chunk step with that step's context
+    lengths.  The flops are causal attention's; the bound is the matrix
+    cores."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_257_amd import Pool, prefill_plan
+    from workloads import draw_normal_storage
+    from workloads.prefill import draw_prefill_shapes
+
+    sh = draw_prefill_shapes(cfg)
+    H, Hq, d, dt = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.dtype
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    width = -(-int(sh.prompts.max()) // 16)
+
+    def dev(bits):
+        a = np.ascontiguousarray(bits)
+        t = torch.from_numpy(a.view(np.int16) if dt == "bf16" else a)
+        return (t.view(torch.bfloat16) if dt == "bf16" else t).to("cuda")
+
+    kc = torch.zeros((sh.num_blocks, H, 16, d), dtype=tdt, device="cuda")
+    vc = torch.zeros_like(kc)
+    pool = Pool(sh.num_blocks, H, d, dt, width, 16, sh.free_order, kc, vc)
+    slots = []
+    for step in sh.steps:
+        for seq, t0, n in step:
+            if t0 == 0:
+                sid, s_ = pool.alloc(n)
+                assert sid == seq
+            else:
+                s_ = pool.append(seq, n)
+            slots.append(s_)
+    slots = torch.from_numpy(np.concatenate(slots)).cuda()
+    # K/V: a seeded 8192-token chunk written over and over (values do not
+    # change the work)
+    chunk = 8192
+    ck = dev(draw_normal_storage((cfg.seed, 60), (chunk, H, d), dt))
+    cv = dev(draw_normal_storage((cfg.seed, 61), (chunk, H, d), dt))
+    for o in range(0, slots.numel(), chunk):
+        sl = slots[o:o + chunk]
+        pool.write_kv(ck[:sl.numel()], cv[:sl.numel()], sl)
+    del ck, cv
+    launches, flops = [], []
+    max_q = max(sum(n for _, _, n in step) for step in sh.steps)
+    q_all = dev(draw_normal_storage((cfg.seed, 62), (max_q, Hq, d), dt))
+    out = torch.empty((max_q, Hq, d), dtype=torch.float32, device="cuda")
+    for step in sh.steps:
+        seqs = [x for x, _, _ in step]
+        q_lens = np.array([n for _, _, n in step])
+        lens = np.array([t0 + n for _, t0, n in step], dtype=np.int32)
+        tables, _ = pool.build_batch(seqs, width)
+        plan, info = prefill_plan(q_lens, lens, Hq, H)
+        launches.append((torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                         torch.from_numpy(plan).cuda(), info, int(q_lens.sum())))
+        flops.append(sum(prefill_flops(int(n), int(L), Hq, d) for n, L in zip(q_lens, lens)))
+    total_tokens = int(sh.prompts.sum())
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches] for _ in range(args.warmup + args.steps)]
+
+    def schedule(r):
+        for k, (tb, ln, pl, info, nq) in enumerate(launches):
+            ev[r][k][0].record()
+            pool.paged_prefill(q_all[:nq], out[:nq], tb, ln, cfg.scale, pl, info)
+            ev[r][k][1].record()
+
+    for r in range(args.warmup):
+        schedule(r)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(args.warmup, args.warmup + args.steps):
+        schedule(r)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = np.array([[ev[r][k][0].elapsed_time(ev[r][k][1]) for k in range(len(launches))]
+                        for r in range(args.warmup, args.warmup + args.steps)])
+    per_launch_ms = kern_ms.mean(axis=0)
+    total_flops = float(sum(flops))
+    kern_total_s = float(per_launch_ms.sum()) / 1e3
+    k_big = int(np.argmax(flops))
+    pool.close()
+    res = {
+        "metric": "chunked paged prefill: causal attention TFLOP/s",
+        "value": round(total_flops * args.steps / wall / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "prompts": len(sh.prompts), "prompt_tokens": total_tokens,
+                   "chunk_tokens": cfg.chunk_tokens, "launches_per_step": len(launches),
+                   "num_q_heads": Hq, "num_kv_heads": H, "head_dim": d, "block_size": 16,
+                   "accumulate": "f32", "output": "f32"},
+        "prompt_tokens_per_s": round(total_tokens * args.steps / wall, 1),
+        "roofline": {"bound": "mfma", "achieved": round(total_flops / kern_total_s / 1e12, 2),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(total_flops / kern_total_s / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "paged_prefill_kernel",
+                     "kernel_ms_per_step": round(float(per_launch_ms.sum()), 4),
+                     "largest_launch": {"flops": flops[k_big], "ms": round(float(per_launch_ms[k_big]), 4),
+                                        "TFLOPs": round(flops[k_big] / per_launch_ms[k_big] / 1e9, 1)},
+                     "algorithmic_flops_per_step": int(total_flops)},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -337,6 +458,10 @@ def main(argv=None):
     from workloads import config_by_name, draw_decode_values, draw_normal_storage
     from workloads.configs import PrefixSharedConfig, draw_decode_shapes
 
+    from workloads.prefill import PREFILL_CONFIGS
+    pf = {c.name: c for c in PREFILL_CONFIGS}
+    if args.workload in pf:
+        return bench_prefill(args, pf[args.workload])
     cfg = config_by_name(args.workload)
     if isinstance(cfg, PrefixSharedConfig):
         return bench_prefix_shared(args, cfg)

@@ -216,7 +216,7 @@ int32_t pkv_default_partition_tokens(void);
  * last q_lens[i] of its context_lens[i] tokens (already appended and
  * written).  A work item is one tile of tile_tokens consecutive query
  * tokens of one sequence; the kernel runs every item for every KV head.
- * tile_tokens is 64 / Gw with Gw the largest power of two <= 16 dividing
+ * tile_tokens is 128 / Gw with Gw the largest power of two <= 16 dividing
  * H_q / H_kv (Gw query heads of one KV head share a tile).  Items are
  * ordered by decreasing number of keys they attend.
  *

@@ -111,8 +111,8 @@ inline int dtype_bytes(int32_t dt) { return dt == PKV_F32 ? 4 : 2; }
 constexpr int32_t kDefaultPartitionTokens = 2048;
 
 // Query rows (token, head pairs) of one chunked-prefill workgroup: four
-// waves of 16 rows each.
-constexpr int32_t kPrefillTileRows = 64;
+// waves of two 16-row groups each.
+constexpr int32_t kPrefillTileRows = 128;
 
 // Live sequence with this id, or null.
 inline pkv_seq_state* find_seq(pkv_pool* p, int32_t id) {

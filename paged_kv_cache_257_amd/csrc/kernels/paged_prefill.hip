@@ -9,11 +9,13 @@
 // every K/V tile, so the products are dense contractions and run as MFMA.
 //
 // Work decomposition.  A workgroup of 4 waves takes one tile of query rows
-// of one sequence and one KV head: 64 rows = (token, head) pairs, where the
+// of one sequence and one KV head: 128 rows = (token, head) pairs, where the
 // Gw query heads of that KV head that share the tile are packed into the
-// rows (Gw = 1 for MHA: 64 tokens of one head; Gw = 4 for GQA-4: 16 tokens
-// x 4 heads).  Each wave owns 16 rows.  The workgroup walks the sequence's
-// keys in stages of 32 tokens (two blocks) up to its last query's position.
+// rows (Gw = 1 for MHA: 128 tokens of one head; Gw = 4 for GQA-4: 32 tokens
+// x 4 heads).  Each wave owns two groups of 16 rows; every K or V^T operand
+// it reads from LDS feeds one MFMA per group.  The workgroup walks the
+// sequence's keys in stages of 32 tokens (two blocks) up to its last
+// query's position.
 //
 // Per stage.  All 256 threads stage the two K tiles into LDS as they are
 // (rows padded by 16 bytes against bank conflicts) and the two V tiles
@@ -34,8 +36,9 @@
 // weights must become 16-bit MFMA operands: for fp16 they are rounded to
 // fp16 (11-bit significand); for bf16 they are split into a bf16 head and a
 // bf16 remainder (two MFMAs, ~16 bits), since bf16 weights alone put the
-// error of short contexts above 2e-3.  The normaliser sums the weights as
-// rounded, so the output is an exactly normalised mix of V rows.
+// error of short contexts above 2e-3.  The normaliser sums the fp32 weights.
+// The accumulators are rescaled only in stages where some row's running
+// maximum grew (a wave-wide vote); otherwise the factor is exactly 1.
 #include "device_common.h"
 
 namespace pkv {
@@ -47,6 +50,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPfWaves = 4;
+constexpr int kPfRowGroups = kPrefillTileRows / (16 * kPfWaves);  // 16-row groups per wave
 constexpr int kPfThreads = kWave * kPfWaves;
 constexpr int kStage = 32;  // key tokens per stage (two blocks)
 constexpr float kLog2eF = 1.4426950408889634f;
@@ -106,7 +110,8 @@ __device__ __forceinline__ uint32_t round16<PKV_BF16>(float x, float* back) {
 
 template <int DT, int D, int GW>
 __global__ __launch_bounds__(kPfThreads) void paged_prefill_kernel(const PrefillParams p) {
-  constexpr int TPW = 16 / GW;             // query tokens per wave
+  constexpr int RG = kPfRowGroups;         // 16-row groups per wave
+  constexpr int TPW = 16 * RG / GW;        // query tokens per wave
   constexpr int TQ = kPfWaves * TPW;       // query tokens per workgroup
   constexpr int CH = D / 8;                // 16-byte chunks per row
   constexpr int ROWB = D * 2;              // bytes per token row of one head
@@ -117,8 +122,12 @@ __global__ __launch_bounds__(kPfThreads) void paged_prefill_kernel(const Prefill
   constexpr int VPAIRS = CH * (kStage / 2);     // (chunk, token pair) items of V
   constexpr int KT = D / 32;               // k-steps of S^T = K Q^T
   constexpr int NDT = D / 16;              // d-tiles of O^T
+  constexpr int KTOK_PER_WAVE = kWave / CH;         // K tokens one wave stages per load
+  constexpr int VTOK_PER_WAVE = 2 * (kWave / CH);   // V tokens one wave stages
   static_assert(KL >= 1 && KL * kPfThreads == kStage * CH, "staging split");
   static_assert(VPAIRS <= kPfThreads, "one V pair per thread");
+  static_assert(kBlockTokens % KTOK_PER_WAVE == 0 && kBlockTokens % VTOK_PER_WAVE == 0,
+                "a wave's staged rows lie in one block");
 
   __shared__ __attribute__((aligned(16))) uint16_t lk[2][kStage * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t lv[2][D * VROW];
@@ -146,31 +155,41 @@ __global__ __launch_bounds__(kPfThreads) void paged_prefill_kernel(const Prefill
   const char* kbase = p.k_cache + int64_t(kvh) * TILE;
   const char* vbase = p.v_cache + int64_t(kvh) * TILE;
 
-  // this lane's query row: token tq of the chunk, head h
-  const int tq = t0 + wave * TPW + n / GW;
+  // query rows of this lane: group j holds row 16 j + n of the wave, i.e.
+  // chunk token tq[j] = first + (16 j + n) / GW, head qh0 + n % GW
   const int h = qh0 + n % GW;
-  const bool row_ok = tq < T;
-  const int qpos = C + tq;
   const int wave_first = t0 + wave * TPW;
+  int tq[RG], qpos[RG];
+  bool row_ok[RG];
+#pragma unroll
+  for (int j = 0; j < RG; ++j) {
+    tq[j] = wave_first + (16 * j + n) / GW;
+    row_ok[j] = tq[j] < T;
+    qpos[j] = C + tq[j];
+  }
   const int wave_last = min(wave_first + TPW, T) - 1;  // < wave_first: no rows
   const int wg_last = min(t0 + TQ, T) - 1;
   const int wg_stages = (C + wg_last) / kStage + 1;
   const int wave_stages = wave_last >= wave_first ? (C + wave_last) / kStage + 1 : 0;
   const int mask_from = (C + wave_first) / kStage;  // first stage with a masked key
 
-  u32x4 qb[KT];
-  {
-    const char* qrow = p.q + (int64_t(qs + (row_ok ? tq : 0)) * p.num_q_heads + h) * ROWB;
+  u32x4 qb[RG][KT];
+#pragma unroll
+  for (int j = 0; j < RG; ++j) {
+    const char* qrow = p.q + (int64_t(qs + (row_ok[j] ? tq[j] : 0)) * p.num_q_heads + h) * ROWB;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
-      qb[kt] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + (32 * kt + 8 * g) * 2)
-                      : u32x4{0u, 0u, 0u, 0u};
+      qb[j][kt] = row_ok[j] ? *reinterpret_cast<const u32x4*>(qrow + (32 * kt + 8 * g) * 2)
+                            : u32x4{0u, 0u, 0u, 0u};
   }
 
   // ---- staging: global -> registers -> LDS ----------------------------------
+  // Every wave's staged rows lie in one block, so the block index and the
+  // buffer resource are wave-uniform (scalar registers, one table read).
   u32x4 kr[KL];
   u32x4 vr0 = {0u, 0u, 0u, 0u}, vr1 = {0u, 0u, 0u, 0u};
   auto tile_rsrc = [&](const char* base, int b) __attribute__((always_inline)) {
+    b = __builtin_amdgcn_readfirstlane(b);
     const int blk = b < nblk ? trow[b] : -1;
     const bool ok = unsigned(blk) < unsigned(p.num_blocks);
     return make_rsrc(base + (ok ? int64_t(blk) * blk_stride : 0), ok ? TILE : 0);
@@ -180,13 +199,15 @@ __global__ __launch_bounds__(kPfThreads) void paged_prefill_kernel(const Prefill
     for (int i = 0; i < KL; ++i) {
       const int idx = tid + i * kPfThreads;
       const int tok = idx / CH, ch = idx - (idx / CH) * CH;
-      const auto rs = tile_rsrc(kbase, st * 2 + tok / kBlockTokens);
+      const int wtok = (wave * kWave + i * kPfThreads) / CH;  // first token of this wave's rows
+      const auto rs = tile_rsrc(kbase, st * 2 + wtok / kBlockTokens);
       kr[i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (tok % kBlockTokens) * ROWB + ch * 16, 0, 0));
     }
-    if (tid < VPAIRS) {
+    if (wave * kWave < VPAIRS) {
       const int ch = tid % CH, tok = 2 * (tid / CH);
-      const auto rs = tile_rsrc(vbase, st * 2 + tok / kBlockTokens);
+      const int wtok = 2 * (wave * kWave / CH);
+      const auto rs = tile_rsrc(vbase, st * 2 + wtok / kBlockTokens);
       const int off = (tok % kBlockTokens) * ROWB + ch * 16;
       vr0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
       vr1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + ROWB, 0, 0));
@@ -199,7 +220,7 @@ __global__ __launch_bounds__(kPfThreads) void paged_prefill_kernel(const Prefill
       const int tok = idx / CH, ch = idx - (idx / CH) * CH;
       *reinterpret_cast<u32x4*>(&lk[buf][tok * KROW + ch * 8]) = kr[i];
     }
-    if (tid < VPAIRS) {
+    if (wave * kWave < VPAIRS) {
       const int ch = tid % CH, tok = 2 * (tid / CH);
       const int kp = st * kStage + tok;
       const uint32_t z0 = kp < L ? 0xFFFFFFFFu : 0u;  // rows past the context -> 0
@@ -216,81 +237,103 @@ __global__ __launch_bounds__(kPfThreads) void paged_prefill_kernel(const Prefill
   };
 
   // ---- compute ----------------------------------------------------------------
-  float m = kNegBig, lsum = 0.f;
-  f4 o[NDT];
+  // Running maxima are kept in scaled base-2 units (score * scale * log2 e).
+  const float c2 = p.scale_log2;
+  float m[RG], lsum[RG];
+  f4 o[RG][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < RG; ++j) {
+    m[j] = kNegBig;
+    lsum[j] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[j][dt] = f4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto compute = [&](int buf, int st) __attribute__((always_inline)) {
-    f4 sa[2];
+    f4 sa[RG][2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      sa[blk] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < RG; ++j) sa[j][blk] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(&lk[buf][(blk * 16 + n) * KROW + 32 * kt + 8 * g]);
-        sa[blk] = mfma32<DT>(a, qb[kt], sa[blk]);
+#pragma unroll
+        for (int j = 0; j < RG; ++j) sa[j][blk] = mfma32<DT>(a, qb[j][kt], sa[j][blk]);
       }
     }
-    float s[8];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) s[blk * 4 + v] = sa[blk][v] * p.scale_log2;
     // blocks outside the pool contribute nothing (wave-uniform)
+    bool bad[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int b = st * 2 + blk;
       const int id = b < nblk ? trow[b] : -1;
-      if (!(unsigned(id) < unsigned(p.num_blocks)))
-#pragma unroll
-        for (int v = 0; v < 4; ++v) s[blk * 4 + v] = -INFINITY;
+      bad[blk] = !(unsigned(id) < unsigned(p.num_blocks));
     }
-    if (st >= mask_from) {  // causal / context mask (wave-uniform branch)
+    const bool masked = st >= mask_from || bad[0] || bad[1];
+    u32x4 pb[RG], pl[RG];
+    float alpha[RG];
+    bool rescale = false;
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      float s[8];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int kp = st * kStage + blk * 16 + 4 * g + v;
-          if (kp > qpos || kp >= L) s[blk * 4 + v] = -INFINITY;
-        }
-    }
-    float mx = s[0];
+        for (int v = 0; v < 4; ++v) s[blk * 4 + v] = sa[j][blk][v];
+      if (masked) {  // causal / context / pool mask (wave-uniform branch)
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    m = mn;
-    uint32_t ph[4], pl[4];
-    float psum = 0.f;
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float x0 = __builtin_amdgcn_exp2f(s[2 * j] - mn);
-      const float x1 = __builtin_amdgcn_exp2f(s[2 * j + 1] - mn);
-      float r0, r1;
-      ph[j] = round16<DT>(x0, &r0) | (round16<DT>(x1, &r1) << 16);
-      psum += r0 + r1;
-      if constexpr (DT == PKV_BF16) {
-        float e0, e1;
-        pl[j] = round16<DT>(x0 - r0, &e0) | (round16<DT>(x1 - r1, &e1) << 16);
-        psum += e0 + e1;
+          for (int v = 0; v < 4; ++v) {
+            const int kp = st * kStage + blk * 16 + 4 * g + v;
+            if (bad[blk] || kp > qpos[j] || kp >= L) s[blk * 4 + v] = -INFINITY;
+          }
       }
+      float mx = s[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m[j], mx * c2);
+      alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
+      rescale |= mn > m[j];
+      m[j] = mn;
+      uint32_t ph[4], plo[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q2], c2, -mn));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q2 + 1], c2, -mn));
+        psum += x0 + x1;
+        float r0, r1;
+        ph[q2] = round16<DT>(x0, &r0) | (round16<DT>(x1, &r1) << 16);
+        if constexpr (DT == PKV_BF16) {
+          float e0, e1;
+          plo[q2] = round16<DT>(x0 - r0, &e0) | (round16<DT>(x1 - r1, &e1) << 16);
+        }
+      }
+      lsum[j] = lsum[j] * alpha[j] + psum;
+      pb[j] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+      if constexpr (DT == PKV_BF16) pl[j] = u32x4{plo[0], plo[1], plo[2], plo[3]};
     }
-    lsum = lsum * alpha + psum;
-    const u32x4 pb = {ph[0], ph[1], ph[2], ph[3]};
+    // rescale the accumulators only when some row's maximum moved
+    if (__builtin_amdgcn_ballot_w64(rescale)) {
+#pragma unroll
+      for (int j = 0; j < RG; ++j)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[j][dt] *= alpha[j];
+    }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      o[dt] *= alpha;
       const uint16_t* vrow = &lv[buf][(dt * 16 + n) * VROW];
       const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + 4 * g);
       const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + 16 + 4 * g);
       const u32x4 a = {a0.x, a0.y, a1.x, a1.y};
-      o[dt] = mfma32<DT>(a, pb, o[dt]);
-      if constexpr (DT == PKV_BF16) {
-        const u32x4 pbl = {pl[0], pl[1], pl[2], pl[3]};
-        o[dt] = mfma32<DT>(a, pbl, o[dt]);
+#pragma unroll
+      for (int j = 0; j < RG; ++j) {
+        o[j][dt] = mfma32<DT>(a, pb[j], o[j][dt]);
+        if constexpr (DT == PKV_BF16) o[j][dt] = mfma32<DT>(a, pl[j], o[j][dt]);
       }
     }
   };
@@ -307,14 +350,17 @@ __global__ __launch_bounds__(kPfThreads) void paged_prefill_kernel(const Prefill
     __syncthreads();
   }
 
-  float lt = lsum + __shfl_xor(lsum, 16);
-  lt += __shfl_xor(lt, 32);
-  if (row_ok) {
-    const float inv = 1.f / lt;
-    float* orow = p.out + (int64_t(qs + tq) * p.num_q_heads + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      *reinterpret_cast<f4*>(orow + dt * 16 + 4 * g) = o[dt] * inv;
+  for (int j = 0; j < RG; ++j) {
+    float lt = lsum[j] + __shfl_xor(lsum[j], 16);
+    lt += __shfl_xor(lt, 32);
+    if (row_ok[j]) {
+      const float inv = 1.f / lt;
+      float* orow = p.out + (int64_t(qs + tq[j]) * p.num_q_heads + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f4*>(orow + dt * 16 + 4 * g) = o[j][dt] * inv;
+    }
   }
 }
 

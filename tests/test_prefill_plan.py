@@ -12,7 +12,7 @@ def tile_for(Hq, Hkv):
     gw = 1
     while gw < 16 and G % (2 * gw) == 0:
         gw *= 2
-    return 64 // gw
+    return 128 // gw
 
 
 def check(q_lens, ctx, Hq, Hkv):
