@@ -436,8 +436,50 @@ def bench_prefill(args, cfg):
                                         "TFLOPs": round(flops[k_big] / per_launch_ms[k_big] / 1e9, 1)},
                      "algorithmic_flops_per_step": int(total_flops)},
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = prefill_cpu_baseline(cfg, sh, args.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def prefill_cpu_baseline(cfg, sh, budget_s):
+    """The fp64 oracle's chunked prefill on a bounded sample of the same
+    schedule: each pass replays every chunk step through the oracle
+    allocator and mirrored pool (not timed) and attends k seeded query rows
+    of each chunk (timed); passes repeat with k doubled until the budget is
+    spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle.runs import PrefillRun
+    from workloads.prefill import draw_prefill_values
+
+    cores = os.cpu_count() or 1
+    with threadpool_limits(limits=cores):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        vals = draw_prefill_values(cfg, sh.prompts)
+        rng = np.random.default_rng(cfg.seed + 9)
+        done, flops, spent, k, passes = 0, 0, 0.0, 4, 0
+        while spent <= budget_s:
+            run = PrefillRun(cfg, sh, -(-int(sh.prompts.max()) // 16), vals)
+            passes += 1
+            for _ in sh.steps:
+                items = run.append_step()
+                for seq, t0, n, _slots in items:
+                    rows = sorted(set(rng.integers(0, n, size=min(k, n)).tolist()))
+                    t = time.perf_counter()
+                    run.attend(seq, t0, n, rows=rows)
+                    spent += time.perf_counter() - t
+                    done += len(rows)
+                    flops += sum(4 * cfg.head_dim * cfg.num_q_heads * (t0 + r + 1) for r in rows)
+                if spent > budget_s:
+                    break
+            k *= 2
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{done} query rows of the same schedule ({passes} passes, seeded rows of "
+                      f"every chunk), fp64 numpy causal attention through the oracle allocator, "
+                      f"{spent:.1f} s"}
 
 
 def main(argv=None):
