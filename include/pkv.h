@@ -158,6 +158,30 @@ pkv_status pkv_build_batch(const pkv_pool* pool, const int32_t* seqs, int32_t n_
                            int32_t* block_tables, int32_t table_stride, int32_t* context_lens);
 
 /* ---------------------------------------------------------------------------
+ * Host: naive-vs-paged utilisation of one set of concurrent requests
+ * ------------------------------------------------------------------------ */
+
+/* The comparison the tutorial ("Paged Attention em Large Language Models
+ * LLMs", opening paragraph and "Cache KV Ingênuo") sets up: a naive cache
+ * reserves max_len tokens per request up front; the paged cache allocates
+ * each request's tokens in block_size-token blocks.  The paged side runs
+ * this library's allocator on a scratch host-only pool sized to fit (every
+ * request allocated, statistics read, pool destroyed); the naive side is
+ * n * max_len.  Token counts; lengths[i] in [1, max_len]. */
+typedef struct {
+  int64_t requests;
+  int64_t tokens_used;
+  int64_t naive_reserved_tokens;
+  int64_t paged_blocks;
+  int64_t paged_reserved_tokens;
+  int64_t naive_waste_tokens;
+  int64_t paged_waste_tokens;
+} pkv_utilisation_t;
+
+pkv_status pkv_utilisation(const int32_t* lengths, int32_t n, int32_t max_len, int32_t block_size,
+                           pkv_utilisation_t* out);
+
+/* ---------------------------------------------------------------------------
  * Host: decode plan
  * ------------------------------------------------------------------------ */
 

@@ -40,3 +40,18 @@ def dense_waste_fraction(mean_len: float, max_len: float) -> float:
 def padding_factor(padded_len: float, actual_len: float) -> float:
     """Work inflation of padding a sequence to the batch max ([preview] Problema 3)."""
     return padded_len / actual_len
+
+
+def utilisation_gap(lengths, max_len: int, block_size: int) -> dict:
+    """Naive contiguous reservation vs paged blocks for one set of
+    concurrent requests ([tutorial] opening paragraph and "Cache KV
+    Ingenuo": every request reserves max_len tokens up front; paging holds
+    ceil(L / block) blocks per request, [preview] steps 1-3).  Token counts;
+    multiply by the bytes per token for memory."""
+    used = sum(int(x) for x in lengths)
+    naive = len(lengths) * int(max_len)
+    blocks = sum(blocks_for_tokens(int(x), block_size) for x in lengths)
+    paged = blocks * block_size
+    return {"requests": len(lengths), "tokens_used": used, "naive_reserved_tokens": naive,
+            "paged_blocks": blocks, "paged_reserved_tokens": paged,
+            "naive_waste_tokens": naive - used, "paged_waste_tokens": paged - used}

@@ -42,6 +42,15 @@ class PrefillPlanInfo(C.Structure):
                                          "n_work", "total_q", "max_context_len", "plan_ints")]
 
 
+class Utilisation(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("requests", "tokens_used", "naive_reserved_tokens",
+                                         "paged_blocks", "paged_reserved_tokens",
+                                         "naive_waste_tokens", "paged_waste_tokens")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
 class BatchLayout(C.Structure):
     _fields_ = [("n_seqs", C.c_int32), ("append_tokens", C.c_int32), ("n_pairs", C.c_int32),
                 ("table_stride", C.c_int32), ("off_slots", C.c_int64), ("off_pairs", C.c_int64),
@@ -85,6 +94,7 @@ SIGNATURES = {
     "pkv_stats": [P, C.POINTER(Stats)],
     "pkv_take_cow": [P, PI32, I32, PI32],
     "pkv_build_batch": [P, PI32, I32, PI32, I32, PI32],
+    "pkv_utilisation": [PI32, I32, I32, I32, C.POINTER(Utilisation)],
     "pkv_decode_plan_ints": [PI32, I32, I32, I32, PI32],
     "pkv_decode_plan": [PI32, I32, I32, I32, PI32, I32, C.POINTER(PlanInfo)],
     "pkv_decode_workspace_bytes": [C.POINTER(PlanInfo), I32, I32],
