@@ -52,7 +52,8 @@ typedef enum {
   PKV_E_BAD_ARG = 3,     /* invalid argument (null, size, geometry, dtype) */
   PKV_E_TABLE_FULL = 4,  /* a sequence would exceed max_blocks_per_seq    */
   PKV_E_HIP = 5,         /* a HIP launch failed                           */
-  PKV_E_UNSUPPORTED = 6  /* valid, but not built (head_dim, dtype, ...)   */
+  PKV_E_UNSUPPORTED = 6, /* valid, but not built (head_dim, dtype, ...)   */
+  PKV_E_NO_SLOTS = 7     /* no free state slot (hybrid manager); nothing changed */
 } pkv_status;
 
 typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
@@ -156,6 +157,62 @@ pkv_status pkv_take_cow(pkv_pool* pool, int32_t* pairs, int32_t cap, int32_t* n)
  * block_tables[n_seqs][table_stride] and context_lens[n_seqs]. */
 pkv_status pkv_build_batch(const pkv_pool* pool, const int32_t* seqs, int32_t n_seqs,
                            int32_t* block_tables, int32_t table_stride, int32_t* context_lens);
+
+/* ---------------------------------------------------------------------------
+ * Host: hybrid two-pool manager
+ * ------------------------------------------------------------------------ */
+
+/* A hybrid model keeps paged K/V only for its attention layers; its other
+ * layers carry a recurrent state of fixed size per sequence, so a server
+ * aware of the hybrid runs two pools with different lifecycles
+ * ("PagedAttention e continuous batching", 01 · Conceito, paragraph 7).
+ * pkv_hybrid pairs a K/V pool with a pool of num_slots state slots of
+ * slot_bytes each (device memory at state_base, caller-owned; NULL for
+ * host-only use).  A sequence admitted through it holds blocks and one
+ * slot; a fork shares the parent's blocks (refcounts) but takes its own
+ * slot and queues a (parent slot, child slot) copy, since the state changes
+ * every step; free returns both.  Admission and fork are all-or-nothing
+ * across the two pools and refuse early ([lesson] paragraph 8) with
+ * PKV_E_NO_SLOTS or PKV_E_NO_BLOCKS.  The slot free list is a stack seeded
+ * by slot_order (NULL = 0..num_slots-1; slot_order[0] is handed out first).
+ * Sequences admitted here must be forked and freed here; appends go to the
+ * K/V pool directly (pkv_seq_append). */
+typedef struct pkv_hybrid pkv_hybrid;
+
+typedef struct {
+  int64_t free_slots;
+  int64_t used_slots;
+  int64_t refusals;      /* admissions / forks refused for lack of a slot or blocks */
+  int64_t state_copies;  /* state copies queued so far */
+} pkv_hybrid_stats_t;
+
+pkv_status pkv_hybrid_create(pkv_pool* kv, int32_t num_slots, int64_t slot_bytes, void* state_base,
+                             const int32_t* slot_order, pkv_hybrid** out);
+pkv_status pkv_hybrid_destroy(pkv_hybrid* h);
+pkv_status pkv_hybrid_admit(pkv_hybrid* h, int32_t n_tokens, int32_t* seq, int32_t* slot,
+                            int64_t* slots);
+pkv_status pkv_hybrid_fork(pkv_hybrid* h, int32_t parent, int32_t* child, int32_t* child_slot);
+pkv_status pkv_hybrid_free(pkv_hybrid* h, int32_t seq);
+pkv_status pkv_hybrid_slot(const pkv_hybrid* h, int32_t seq, int32_t* slot);
+/* Queued (src slot, dst slot) state copies.  With pairs == NULL (or cap too
+ * small) only *n is written and the queue is kept; otherwise the pairs are
+ * written and the queue is cleared. */
+pkv_status pkv_hybrid_take_copies(pkv_hybrid* h, int32_t* pairs, int32_t cap, int32_t* n);
+pkv_status pkv_hybrid_stats(const pkv_hybrid* h, pkv_hybrid_stats_t* out);
+/* Device: copy slot_bytes from slot pairs_dev[i][0] to slot pairs_dev[i][1]
+ * (device int32 [n][2]); pairs naming a slot outside the pool are skipped.
+ * Asynchronous on `stream`. */
+pkv_status pkv_hybrid_copy_states(pkv_hybrid* h, const int32_t* pairs_dev, int32_t n, void* stream);
+
+/* Split a joint memory budget into the two pools for sessions of
+ * session_tokens tokens: a session costs ceil(session_tokens / block_size)
+ * blocks of block_bytes plus one slot of slot_bytes ([lesson] paragraph 4's
+ * arithmetic: 2 GiB of K/V + 144 MiB of state per 32,768-token session, ten
+ * of which fit 23,859 MiB).  *sessions = budget / cost (floor); the state
+ * pool gets that many slots and the K/V pool every whole block left. */
+pkv_status pkv_hybrid_plan(int64_t budget_bytes, int64_t block_bytes, int32_t block_size,
+                           int64_t slot_bytes, int64_t session_tokens, int32_t* sessions,
+                           int32_t* num_blocks, int32_t* num_slots);
 
 /* ---------------------------------------------------------------------------
  * Host: naive-vs-paged utilisation of one set of concurrent requests

@@ -11,9 +11,10 @@ import os
 
 LIBDIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib")
 
-OK, E_NO_BLOCKS, E_BAD_SEQ, E_BAD_ARG, E_TABLE_FULL, E_HIP, E_UNSUPPORTED = range(7)
+OK, E_NO_BLOCKS, E_BAD_SEQ, E_BAD_ARG, E_TABLE_FULL, E_HIP, E_UNSUPPORTED, E_NO_SLOTS = range(8)
 STATUS_KIND = {E_NO_BLOCKS: "no_blocks", E_BAD_SEQ: "bad_seq", E_BAD_ARG: "bad_arg",
-               E_TABLE_FULL: "table_full", E_HIP: "hip", E_UNSUPPORTED: "unsupported"}
+               E_TABLE_FULL: "table_full", E_HIP: "hip", E_UNSUPPORTED: "unsupported",
+               E_NO_SLOTS: "no_slots"}
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 
 
@@ -46,6 +47,13 @@ class Utilisation(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("requests", "tokens_used", "naive_reserved_tokens",
                                          "paged_blocks", "paged_reserved_tokens",
                                          "naive_waste_tokens", "paged_waste_tokens")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+class HybridStats(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("free_slots", "used_slots", "refusals", "state_copies")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -95,6 +103,16 @@ SIGNATURES = {
     "pkv_take_cow": [P, PI32, I32, PI32],
     "pkv_build_batch": [P, PI32, I32, PI32, I32, PI32],
     "pkv_utilisation": [PI32, I32, I32, I32, C.POINTER(Utilisation)],
+    "pkv_hybrid_create": [P, I32, C.c_int64, P, PI32, C.POINTER(P)],
+    "pkv_hybrid_destroy": [P],
+    "pkv_hybrid_admit": [P, I32, PI32, PI32, PI64],
+    "pkv_hybrid_fork": [P, I32, PI32, PI32],
+    "pkv_hybrid_free": [P, I32],
+    "pkv_hybrid_slot": [P, I32, PI32],
+    "pkv_hybrid_take_copies": [P, PI32, I32, PI32],
+    "pkv_hybrid_stats": [P, C.POINTER(HybridStats)],
+    "pkv_hybrid_copy_states": [P, P, I32, P],
+    "pkv_hybrid_plan": [C.c_int64, C.c_int64, I32, C.c_int64, C.c_int64, PI32, PI32, PI32],
     "pkv_decode_plan_ints": [PI32, I32, I32, I32, PI32],
     "pkv_decode_plan": [PI32, I32, I32, I32, PI32, I32, C.POINTER(PlanInfo)],
     "pkv_decode_workspace_bytes": [C.POINTER(PlanInfo), I32, I32],
@@ -121,7 +139,8 @@ RESTYPES = {"pkv_last_error": C.c_char_p, "pkv_decode_workspace_bytes": C.c_size
             "pkv_decode_workspace_bound": C.c_size_t, "pkv_default_partition_tokens": C.c_int32,
             "pkv_prepare_decode_bytes": C.c_size_t, "pkv_stepper_slot_bytes": C.c_size_t}
 DEVICE_FUNCS = ("pkv_copy_blocks", "pkv_write_kv", "pkv_paged_decode", "pkv_paged_decode_partitions",
-                "pkv_paged_decode_reduce", "pkv_paged_prefill", "pkv_stepper_slot_bytes", "pkv_stepper_create",
+                "pkv_paged_decode_reduce", "pkv_paged_prefill", "pkv_hybrid_copy_states",
+                "pkv_stepper_slot_bytes", "pkv_stepper_create",
                 "pkv_stepper_destroy", "pkv_stepper_step")
 
 _LIBS = {}

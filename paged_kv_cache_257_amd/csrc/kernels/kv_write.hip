@@ -11,6 +11,9 @@
 // Both are plain byte moves: each thread moves one 16-byte chunk with a
 // 128-bit load and store; the threads of a wave cover consecutive chunks of
 // one (token, head) row or one block, so loads and stores are coalesced.
+#include <algorithm>
+
+#include "../host/hybrid_internal.h"
 #include "device_common.h"
 
 namespace pkv {
@@ -60,6 +63,23 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* __restr
     *reinterpret_cast<u32x4*>(kd + off) = *reinterpret_cast<const u32x4*>(ks + off);
     *reinterpret_cast<u32x4*>(vd + off) = *reinterpret_cast<const u32x4*>(vs + off);
   }
+}
+
+// Whole-slot copies of the hybrid manager's per-sequence state (a forked
+// sequence starts from its parent's state).  Same shape as copy_blocks.
+__global__ __launch_bounds__(256) void copy_states_kernel(const int32_t* __restrict__ pairs,
+                                                          char* __restrict__ base, int64_t slot_bytes,
+                                                          int32_t groups_per_pair, int32_t num_slots) {
+  const int32_t pair = blockIdx.x / groups_per_pair;
+  const int32_t g = blockIdx.x - pair * groups_per_pair;
+  const int32_t src = pairs[2 * pair];
+  const int32_t dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= num_slots || dst < 0 || dst >= num_slots || src == dst) return;
+  const char* s = base + int64_t(src) * slot_bytes;
+  char* d = base + int64_t(dst) * slot_bytes;
+  for (int64_t off = (int64_t(g) * 256 + threadIdx.x) * 16; off < slot_bytes;
+       off += int64_t(groups_per_pair) * 256 * 16)
+    *reinterpret_cast<u32x4*>(d + off) = *reinterpret_cast<const u32x4*>(s + off);
 }
 
 pkv_status check_device_pool(const pkv_pool* p) {
@@ -115,4 +135,23 @@ extern "C" pkv_status pkv_copy_blocks(const pkv_pool* pool, const int32_t* pairs
                      static_cast<hipStream_t>(stream), pairs, static_cast<char*>(pool->k_cache),
                      static_cast<char*>(pool->v_cache), block_bytes, groups, d.num_blocks);
   return launch_status("copy_blocks launch");
+}
+
+extern "C" pkv_status pkv_hybrid_copy_states(pkv_hybrid* h, const int32_t* pairs, int32_t n,
+                                             void* stream) {
+  if (!h) return fail(PKV_E_BAD_ARG, "null manager");
+  if (!h->state_base) return fail(PKV_E_BAD_ARG, "the manager has no device state memory");
+  if (n < 0) return fail(PKV_E_BAD_ARG, "negative n");
+  if (n == 0) return PKV_OK;
+  if (!pairs) return fail(PKV_E_BAD_ARG, "null pairs");
+  // enough workgroups per pair to fill the chip for a few pairs, each
+  // moving at least 64 KiB
+  const int64_t per_group = int64_t(256) * 16 * 16;
+  const int32_t gpp = int32_t(std::min<int64_t>(1024, (h->slot_bytes + per_group - 1) / per_group));
+  const int64_t grid = int64_t(n) * gpp;
+  if (grid > INT32_MAX) return fail(PKV_E_BAD_ARG, "too many pairs");
+  hipLaunchKernelGGL(copy_states_kernel, dim3(uint32_t(grid)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), pairs, static_cast<char*>(h->state_base),
+                     h->slot_bytes, gpp, h->num_slots);
+  return launch_status("copy_states launch");
 }
