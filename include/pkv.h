@@ -129,6 +129,14 @@ pkv_status pkv_seq_append_batch(pkv_pool* pool, const int32_t* seqs, int32_t n_s
  * every block's refcount goes up by one. */
 pkv_status pkv_seq_fork(pkv_pool* pool, int32_t parent, int32_t* child);
 
+/* New sequence sharing the first n_tokens tokens of `parent` (0 <= n_tokens
+ * <= its length): the child's table is the parent's first
+ * ceil(n_tokens / block_size) blocks, each gaining a reference; requests
+ * with an identical prompt prefix point at the same read-only blocks
+ * ([lesson] paragraph 7).  If n_tokens ends inside a block, the child's
+ * first append copies that block (copy-on-write). */
+pkv_status pkv_seq_fork_prefix(pkv_pool* pool, int32_t parent, int32_t n_tokens, int32_t* child);
+
 /* Release a sequence: each block of its table, front to back, loses one
  * reference; blocks reaching zero go back on the free list. */
 pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq);
@@ -157,6 +165,123 @@ pkv_status pkv_take_cow(pkv_pool* pool, int32_t* pairs, int32_t cap, int32_t* n)
  * block_tables[n_seqs][table_stride] and context_lens[n_seqs]. */
 pkv_status pkv_build_batch(const pkv_pool* pool, const int32_t* seqs, int32_t n_seqs,
                            int32_t* block_tables, int32_t table_stride, int32_t* context_lens);
+
+/* ---------------------------------------------------------------------------
+ * Host: continuous-batching scheduler with preemption
+ * ------------------------------------------------------------------------ */
+
+/* One iteration-level scheduler over one pool ("PagedAttention e continuous
+ * batching", 01 · Conceito: composition revisited at every iteration
+ * boundary, finished sequences leave, waiting ones enter, running ones
+ * advance one token; the scheduler weighs free blocks, tokens per batch and
+ * the prefill/decode mix, slicing long prefills; admission reasons in
+ * blocks and refuses early; paragraph 9 names the metrics kept here).
+ * The pages give the goals, not the rules; the rules below are readings.
+ *
+ * Requests are known up front with an arrival iteration; the policy does
+ * not look at output_len except to end a request.  A request's K/V length
+ * is prompt_len + generated - 1 once it has generated >= 1 tokens.  Each
+ * pkv_sched_step(), at iteration t:
+ *   1. requests arriving at t join the back of the waiting queue (id order);
+ *   2. every running sequence past its prefill needs room for one token;
+ *      while the blocks this needs exceed the free blocks, the most recently
+ *      admitted running sequence is preempted: its blocks are freed and it
+ *      goes to the front of the waiting queue, to be recomputed (prefilled
+ *      again over prompt_len + generated - 1 tokens) when readmitted;
+ *   3. each of those sequences appends one token and generates one (DECODE
+ *      item);
+ *   4. budget = max_batch_tokens - decode tokens; running sequences still
+ *      in prefill take, in admission order, min(rest, chunk_tokens, budget)
+ *      tokens (PREFILL item), stopping at the first that does not fit in the
+ *      free blocks;
+ *   5. while budget > 0, the queue is not empty and fewer than max_running
+ *      run: a head request that could never fit (its final length needs more
+ *      blocks than the pool or a table holds) is rejected; otherwise it is
+ *      admitted if its first slice fits, else admission stops (first come,
+ *      first served).  If another running sequence of the same prefix_id has
+ *      prefilled the prefix, the new sequence forks those prefix_len tokens
+ *      (pkv_seq_fork_prefix: prefix hits) and prefills only the rest;
+ *   6. a prefill that completes generates the request's first token (not
+ *      again after a preemption); requests that reach output_len tokens
+ *      finish; their sequences are freed at the start of the next step, so
+ *      the items of a step stay valid until the next pkv_sched_step call
+ *      (one more call after the last request finishes frees the rest).
+ * Items list what the device must compute this iteration: (request, seq,
+ * kind, first position, tokens); their K/V slots follow from the tables.
+ * Copy-on-write pairs accumulate in the pool (pkv_take_cow). */
+typedef struct {
+  int32_t arrival;     /* iteration at which the request joins the queue    */
+  int32_t prompt_len;  /* >= 1                                             */
+  int32_t output_len;  /* tokens to generate, >= 1                        */
+  int32_t klass;       /* request class, for metrics                      */
+  int32_t prefix_id;   /* -1, or a shared-prompt-prefix id                 */
+  int32_t prefix_len;  /* shared prefix tokens: a multiple of block_size,
+                          0 <= prefix_len < prompt_len                     */
+} pkv_request;
+
+typedef struct {
+  int32_t max_batch_tokens;  /* decode + prefill tokens per iteration       */
+  int32_t chunk_tokens;      /* longest prefill slice per sequence per step */
+  int32_t max_running;       /* running sequences at most                  */
+} pkv_sched_config;
+
+enum { PKV_ITEM_PREFILL = 0, PKV_ITEM_DECODE = 1 };
+typedef struct {
+  int32_t request;
+  int32_t seq;
+  int32_t kind;      /* PKV_ITEM_PREFILL or PKV_ITEM_DECODE */
+  int32_t pos;       /* position of the first token computed */
+  int32_t n_tokens;
+} pkv_sched_item;
+
+typedef struct {
+  int32_t iteration;
+  int32_t n_items;
+  int32_t prefill_tokens;
+  int32_t decode_tokens;
+  int32_t admitted;
+  int32_t preempted;
+  int32_t finished;
+  int32_t rejected;
+} pkv_sched_step_info;
+
+enum { PKV_REQ_PENDING = 0, PKV_REQ_WAITING = 1, PKV_REQ_RUNNING = 2, PKV_REQ_FINISHED = 3,
+       PKV_REQ_REJECTED = 4 };
+typedef struct {
+  int32_t state;           /* PKV_REQ_*                                    */
+  int32_t seq;             /* current sequence, or -1                      */
+  int32_t admitted_at;     /* first admission iteration, or -1             */
+  int32_t first_token_at;  /* iteration of the first generated token, or -1 */
+  int32_t finished_at;     /* or -1                                        */
+  int32_t generated;
+  int32_t preemptions;
+  int32_t prefix_hit_tokens;
+} pkv_request_state;
+
+typedef struct {
+  int64_t iterations;
+  int64_t waiting;
+  int64_t running;
+  int64_t finished;
+  int64_t rejected;
+  int64_t preemptions;
+  int64_t prompt_tokens_admitted;  /* tokens each admission had to cover    */
+  int64_t prefix_hit_tokens;       /* of those, served by shared blocks     */
+  int64_t prefill_tokens;
+  int64_t decode_tokens;
+} pkv_sched_stats_t;
+
+typedef struct pkv_sched pkv_sched;
+
+/* reqs (host, n entries) are copied; request ids are their indices.  The
+ * pool must hold no sequence the scheduler does not own while it runs. */
+pkv_status pkv_sched_create(pkv_pool* pool, const pkv_sched_config* cfg, const pkv_request* reqs,
+                            int32_t n, pkv_sched** out);
+pkv_status pkv_sched_destroy(pkv_sched* s);
+/* Run one iteration; items needs room for max_running entries. */
+pkv_status pkv_sched_step(pkv_sched* s, pkv_sched_item* items, int32_t cap, pkv_sched_step_info* info);
+pkv_status pkv_sched_request(const pkv_sched* s, int32_t request, pkv_request_state* out);
+pkv_status pkv_sched_stats(const pkv_sched* s, pkv_sched_stats_t* out);
 
 /* ---------------------------------------------------------------------------
  * Host: hybrid two-pool manager

@@ -185,6 +185,21 @@ class OracleAllocator:
         self.forks += 1
         return sid
 
+    def fork_prefix(self, parent: int, n_tokens: int) -> int:
+        """New sequence sharing the first n_tokens tokens of ``parent``: its
+        table is the parent's first ceil(n / block) blocks (refcounts + 1)."""
+        p = self._get(parent)
+        if n_tokens < 0 or n_tokens > p.length:
+            raise AllocError(BAD_ARG, "prefix longer than the parent")
+        table = p.table[:-(-n_tokens // self.block_size)] if n_tokens else []
+        for b in table:
+            self.rc[b] += 1
+        sid = self.next_id
+        self.next_id += 1
+        self.seqs[sid] = _Seq(list(table), n_tokens)
+        self.forks += 1
+        return sid
+
     def free_seq(self, seq: int) -> None:
         s = self._get(seq)
         del self.seqs[int(seq)]

@@ -59,6 +59,44 @@ class HybridStats(C.Structure):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
 
 
+class Request(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("arrival", "prompt_len", "output_len", "klass", "prefix_id",
+                                         "prefix_len")]
+
+
+class SchedConfig(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("max_batch_tokens", "chunk_tokens", "max_running")]
+
+
+class SchedItem(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("request", "seq", "kind", "pos", "n_tokens")]
+
+
+class SchedStepInfo(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("iteration", "n_items", "prefill_tokens", "decode_tokens",
+                                         "admitted", "preempted", "finished", "rejected")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+class RequestState(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("state", "seq", "admitted_at", "first_token_at", "finished_at",
+                                         "generated", "preemptions", "prefix_hit_tokens")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+class SchedStats(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("iterations", "waiting", "running", "finished", "rejected",
+                                         "preemptions", "prompt_tokens_admitted", "prefix_hit_tokens",
+                                         "prefill_tokens", "decode_tokens")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
 class BatchLayout(C.Structure):
     _fields_ = [("n_seqs", C.c_int32), ("append_tokens", C.c_int32), ("n_pairs", C.c_int32),
                 ("table_stride", C.c_int32), ("off_slots", C.c_int64), ("off_pairs", C.c_int64),
@@ -93,6 +131,12 @@ SIGNATURES = {
     "pkv_seq_append": [P, I32, I32, PI64],
     "pkv_seq_append_batch": [P, PI32, I32, I32, PI64],
     "pkv_seq_fork": [P, I32, PI32],
+    "pkv_seq_fork_prefix": [P, I32, I32, PI32],
+    "pkv_sched_create": [P, C.POINTER(SchedConfig), C.POINTER(Request), I32, C.POINTER(P)],
+    "pkv_sched_destroy": [P],
+    "pkv_sched_step": [P, C.POINTER(SchedItem), I32, C.POINTER(SchedStepInfo)],
+    "pkv_sched_request": [P, I32, C.POINTER(RequestState)],
+    "pkv_sched_stats": [P, C.POINTER(SchedStats)],
     "pkv_seq_free": [P, I32],
     "pkv_seq_length": [P, I32, PI32],
     "pkv_seq_table": [P, I32, PI32, I32, PI32],

@@ -28,7 +28,7 @@ CXX = os.environ.get("CXX", "g++")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["host/pool.cpp", "host/plan.cpp", "host/prepare.cpp", "host/prefill_plan.cpp",
-                "host/utilisation.cpp", "host/hybrid.cpp"]
+                "host/utilisation.cpp", "host/hybrid.cpp", "host/sched.cpp"]
 HIP_SOURCES = ["kernels/kv_write.hip", "kernels/paged_decode.hip", "kernels/paged_prefill.hip",
                "kernels/stepper.cpp"]
 

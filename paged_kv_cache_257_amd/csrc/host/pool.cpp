@@ -297,6 +297,24 @@ pkv_status pkv_seq_fork(pkv_pool* p, int32_t parent, int32_t* child) {
   return PKV_OK;
 }
 
+pkv_status pkv_seq_fork_prefix(pkv_pool* p, int32_t parent, int32_t n_tokens, int32_t* child) {
+  if (pkv_status st = check_pool(p)) return st;
+  if (!child) return fail(PKV_E_BAD_ARG, "null child");
+  const pkv_seq_state* par0 = find_seq(p, parent);
+  if (!par0) return fail(PKV_E_BAD_SEQ, unknown(parent));
+  if (n_tokens < 0 || n_tokens > par0->length)
+    return fail(PKV_E_BAD_ARG, "prefix longer than the parent");
+  pkv_seq_state& c = new_seq(p);  // may move `slots`: look the parent up again
+  const pkv_seq_state& par = *find_seq(p, parent);
+  const int32_t nb = int32_t(blocks_for(n_tokens, p->desc.block_size));
+  c.table.assign(par.table.begin(), par.table.begin() + nb);
+  c.length = n_tokens;
+  for (int32_t b : c.table) p->rc[b]++;
+  p->forks++;
+  *child = c.id;
+  return PKV_OK;
+}
+
 pkv_status pkv_seq_free(pkv_pool* p, int32_t seq) {
   if (pkv_status st = check_pool(p)) return st;
   const int32_t slot = p->index.find(seq);

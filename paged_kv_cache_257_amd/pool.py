@@ -89,6 +89,11 @@ class Pool:
         check(self.lib, self.lib.pkv_seq_fork(self.handle, parent, C.byref(c)))
         return c.value
 
+    def fork_prefix(self, parent: int, n_tokens: int) -> int:
+        c = C.c_int32()
+        check(self.lib, self.lib.pkv_seq_fork_prefix(self.handle, parent, n_tokens, C.byref(c)))
+        return c.value
+
     def free(self, seq: int) -> None:
         check(self.lib, self.lib.pkv_seq_free(self.handle, seq))
 

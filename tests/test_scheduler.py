@@ -1,0 +1,125 @@
+"""The continuous-batching scheduler (pkv_sched_*) in lockstep with the oracle (CPU).
+
+Seeded request streams run through the library scheduler (on the C++
+allocator) and the oracle scheduler (on the oracle allocator) side by side;
+after every iteration the items, the events, every request's state and the
+two pools' tables must agree exactly.  Invariants checked along the way:
+every running sequence past its prefill either decoded or finished its
+prefill in this iteration, not both;
+every item's tokens fit the step's token budget; a sequence's K/V length
+equals prompt + generated - 1 while it decodes; the pool's used blocks
+never exceed its size; at the end every request is finished (with all its
+tokens) or rejected, and every block is free again.  Small pools force
+preemptions; shared prefixes produce prefix hits; an impossible request is
+rejected early.
+"""
+
+import numpy as np
+import pytest
+
+from oracle.allocator import OracleAllocator
+from oracle.scheduler import DECODE, FINISHED, REJECTED, OracleRequest, OracleScheduler
+from paged_kv_cache_257_amd import PkvError, Pool
+from paged_kv_cache_257_amd.sched import Scheduler, request_metrics
+from workloads.requests import draw_request_trace
+
+KEYS = ("state", "seq", "admitted_at", "first_token_at", "finished_at", "generated", "preemptions",
+        "prefix_hit_tokens")
+
+
+def run_lockstep(reqs, blocks, width, mbt, chunk, max_running, order=None, max_steps=20000):
+    pool = Pool(blocks, 1, 8, "f16", width, 16, order, host_only=True)
+    sch = Scheduler(pool, reqs, mbt, chunk, max_running)
+    ora = OracleScheduler(OracleAllocator(blocks, 16, width, order), mbt, chunk, max_running,
+                          [OracleRequest(**r) for r in reqs])
+    try:
+        steps = 0
+        while not ora.done():
+            items, ev = sch.step()
+            o_items, o_ev = ora.step()
+            assert items == o_items, steps
+            assert {k: ev[k] for k in o_ev} == o_ev, steps
+            assert sum(n for *_, n in items) <= mbt
+            decode = {i for i, _, kind, _, _ in items if kind == DECODE}
+            prefill = {i for i, _, kind, _, _ in items if kind != DECODE}
+            for i in ora.running:
+                r = ora.reqs[i]
+                if r.prefilled == r.target:  # past its prefill: decoded now, or prefilled now
+                    assert (i in decode) != (i in prefill)
+                if r.prefilled == r.target and r.generated >= 1:
+                    assert ora.a.length(r.seq) == r.prompt_len + r.generated - 1
+            for i in range(len(reqs)):
+                st = sch.request(i)
+                r = ora.reqs[i]
+                assert tuple(st[k] for k in KEYS) == tuple(getattr(r, k) for k in KEYS), (steps, i)
+                if r.seq >= 0:
+                    assert pool.table(r.seq) == ora.a.table(r.seq)
+            assert pool.stats()["used_blocks"] <= blocks
+            steps += 1
+            assert steps < max_steps
+        assert sch.done()
+        assert sch.step()[0] == ora.step()[0] == []  # frees the last finished sequences
+        for i, r in enumerate(ora.reqs):
+            assert r.state in (FINISHED, REJECTED)
+            if r.state == FINISHED:
+                assert r.generated == r.output_len
+        assert pool.stats()["free_blocks"] == blocks
+        st = sch.stats()
+        for k in ("preemptions", "rejected", "finished", "prompt_tokens_admitted", "prefix_hit_tokens",
+                  "prefill_tokens", "decode_tokens"):
+            assert st[k] == ora.stats[k], k
+        return st, [sch.request(i) for i in range(len(reqs))]
+    finally:
+        sch.close()
+        pool.close()
+
+
+@pytest.mark.parametrize("seed,blocks,mbt,chunk,max_running", [
+    (1, 400, 512, 128, 16),
+    (2, 1500, 2048, 256, 64),
+    (3, 250, 256, 64, 32),
+    (4, 3000, 4096, 512, 128),
+])
+def test_lockstep_streams(seed, blocks, mbt, chunk, max_running):
+    reqs = draw_request_trace(60, seed, rate=2.0, prompt_hi=1024, mean_output=120, max_output=400,
+                              prefix_len=128)
+    order = np.random.default_rng(seed).permutation(blocks).astype(np.int32)
+    st, states = run_lockstep(reqs, blocks, 96, mbt, chunk, max_running, order)
+    print(f"\nseed {seed}: {st}")
+    if blocks <= 400:
+        assert st["preemptions"] > 0
+    assert st["prefix_hit_tokens"] > 0
+    m = request_metrics(reqs, states)
+    assert sum(v["finished"] for v in m.values()) == st["finished"]
+
+
+def test_rejects_what_can_never_fit():
+    reqs = [dict(arrival=0, prompt_len=40, output_len=10, klass=0, prefix_id=-1, prefix_len=0),
+            dict(arrival=0, prompt_len=500, output_len=100, klass=1, prefix_id=-1, prefix_len=0),
+            dict(arrival=1, prompt_len=20, output_len=5, klass=0, prefix_id=-1, prefix_len=0)]
+    st, states = run_lockstep(reqs, 20, 20, 64, 32, 4)
+    assert st["rejected"] == 1 and states[1]["state"] == REJECTED
+    assert states[0]["state"] == states[2]["state"] == FINISHED
+
+
+def test_prefix_sharing_and_first_token():
+    # the second and third requests share the first one's 32-token prefix
+    reqs = [dict(arrival=0, prompt_len=50, output_len=3, klass=0, prefix_id=7, prefix_len=32),
+            dict(arrival=2, prompt_len=40, output_len=1, klass=0, prefix_id=7, prefix_len=32),
+            dict(arrival=2, prompt_len=33, output_len=2, klass=0, prefix_id=7, prefix_len=32)]
+    st, states = run_lockstep(reqs, 64, 16, 256, 256, 4)
+    assert [s["prefix_hit_tokens"] for s in states] == [0, 32, 32]
+    assert states[1]["first_token_at"] == states[1]["finished_at"] == 2  # output_len 1
+    assert st["prefix_hit_tokens"] == 64
+
+
+def test_bad_requests():
+    pool = Pool(8, 1, 8, "f16", 8, 16, host_only=True)
+    try:
+        with pytest.raises(PkvError):
+            Scheduler(pool, [dict(arrival=0, prompt_len=20, output_len=1, prefix_id=1, prefix_len=20)],
+                      64, 16, 2)
+        with pytest.raises(PkvError):
+            Scheduler(pool, [dict(arrival=0, prompt_len=0, output_len=1)], 64, 16, 2)
+    finally:
+        pool.close()
