@@ -106,7 +106,7 @@ def main(argv=None) -> int:
     ap.add_argument("--max-batch-tokens", type=int, default=4096)
     ap.add_argument("--chunk", type=int, default=512)
     ap.add_argument("--max-running", type=int, default=256)
-    ap.add_argument("--rate", type=float, default=4.0)
+    ap.add_argument("--rate", type=float, default=0.15, help="arrivals per iteration (6000 blocks serve ~0.19)")
     ap.add_argument("--seed", type=int, default=42)
     ap.add_argument("--json", action="store_true")
     a = ap.parse_args(argv)
