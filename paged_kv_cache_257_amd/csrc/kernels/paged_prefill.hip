@@ -108,8 +108,11 @@ __device__ __forceinline__ uint32_t round16<PKV_BF16>(float x, float* back) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Three waves per SIMD: the compiler then keeps the accumulators in the
+// arch registers (no spills) and a CU runs three workgroups, whose MFMA and
+// softmax phases overlap.
 template <int DT, int D, int GW>
-__global__ __launch_bounds__(kPfThreads) void paged_prefill_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const PrefillParams p) {
   constexpr int RG = kPfRowGroups;         // 16-row groups per wave
   constexpr int TPW = 16 * RG / GW;        // query tokens per wave
   constexpr int TQ = kPfWaves * TPW;       // query tokens per workgroup
@@ -403,6 +406,7 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, flo
   const pkv_pool_desc& d = pool->desc;
   if (!pool->k_cache || !pool->v_cache) return fail(PKV_E_BAD_ARG, "pool has no device K/V arrays");
   if (d.block_size != kBlockTokens) return fail(PKV_E_UNSUPPORTED, "device kernels take block_size 16 only");
+  if (d.num_blocks < 1) return fail(PKV_E_BAD_ARG, "pool has no blocks");
   if (d.dtype != PKV_F16 && d.dtype != PKV_BF16)
     return fail(PKV_E_UNSUPPORTED, "paged prefill takes fp16 or bf16 pools");
   if (d.head_dim != 64 && d.head_dim != 128)
