@@ -85,8 +85,21 @@ struct DecodeParams {
   float scale_log2;
 };
 
+// Occupancy hint (waves per SIMD) where the compiler fits the kernel in
+// the matching register budget without spilling (checked per instance):
+// 4 (128 registers) for bf16 x 128 with one head per workgroup, 3 (168) for
+// fp16 x 128 with one head and bf16 x 128 with two; else none.
+template <int DT, int D, int GW>
+constexpr int decode_waves_hint() {
+  if (D != 128) return 1;
+  if (DT == PKV_BF16) return GW == 1 ? 4 : GW == 2 ? 3 : 1;
+  if (DT == PKV_F16) return GW == 1 ? 3 : 1;
+  return 1;
+}
+
 template <int DT, int D, int GW, int NW>
-__global__ __launch_bounds__(kWave* NW) void paged_decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kWave* NW, (decode_waves_hint<DT, D, GW>())) void paged_decode_kernel(
+    const DecodeParams p) {
   constexpr int E = ElemBytes<DT>::value;
   constexpr int R = D * E;         // bytes per token row of one head
   constexpr int LPR = R / 16;      // lanes per token row
@@ -464,6 +477,24 @@ int waves_per_item() {
   return nw;
 }
 
+// Query heads of one KV head that one workgroup takes (GW).  All of them
+// (up to 8) by default: splitting a KV head's query heads over workgroups
+// makes each read the tiles (the nontemporal loads keep no copy in L2 for
+// the others; measured 1.45x slower for GQA-4 split in two).
+// PKV_DECODE_GW caps it for tuning sweeps.
+int heads_per_workgroup(int group, int32_t dtype, int32_t head_dim) {
+  static const int cap = [] {
+    const char* s = std::getenv("PKV_DECODE_GW");
+    const int v = s ? std::atoi(s) : 0;
+    return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 8;
+  }();
+  (void)dtype;
+  (void)head_dim;
+  int gw = 1;
+  while (gw < cap && group % (2 * gw) == 0) gw *= 2;
+  return gw;
+}
+
 // Validate the arguments shared by the decode entry points and fill the
 // kernel parameters.  Returns PKV_OK with *empty set when there is no work.
 pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, const void* v_new,
@@ -504,7 +535,7 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_E_BAD_ARG, "workspace too small: need " + std::to_string(need) + " bytes");
   const int group = num_q_heads / d.num_kv_heads;
-  gw = (group % 8 == 0) ? 8 : (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
+  gw = heads_per_workgroup(group, d.dtype, d.head_dim);
   prm.q = static_cast<const char*>(q);
   prm.k_new = static_cast<const char*>(k_new);
   prm.v_new = static_cast<const char*>(v_new);
