@@ -183,11 +183,14 @@ pkv_status pkv_build_batch(const pkv_pool* pool, const int32_t* seqs, int32_t n_
  * is prompt_len + generated - 1 once it has generated >= 1 tokens.  Each
  * pkv_sched_step(), at iteration t:
  *   1. requests arriving at t join the back of the waiting queue (id order);
- *   2. every running sequence past its prefill needs room for one token;
- *      while the blocks this needs exceed the free blocks, the most recently
- *      admitted running sequence is preempted: its blocks are freed and it
- *      goes to the front of the waiting queue, to be recomputed (prefilled
- *      again over prompt_len + generated - 1 tokens) when readmitted;
+ *   2. every running sequence past its prefill needs room for one token,
+ *      and the oldest running sequence still in prefill room for its next
+ *      slice; while the blocks this needs exceed the free blocks, the most
+ *      recently admitted running sequence is preempted (for that slice, only
+ *      sequences newer than the prefill; for the decodes, any): its blocks are freed and it goes to the front of the
+ *      waiting queue, to be recomputed (prefilled again over prompt_len +
+ *      generated - 1 tokens) when readmitted.  So the oldest running
+ *      request always advances and sliced prefills cannot deadlock;
  *   3. each of those sequences appends one token and generates one (DECODE
  *      item);
  *   4. budget = max_batch_tokens - decode tokens; running sequences still

@@ -11,10 +11,15 @@ to keep (the metrics paragraph).  The rules are readings, in this order
 per iteration t:
 
   1. requests arriving at t join the back of the waiting queue (id order);
-  2. each running sequence past its prefill needs room for one more token;
-     while those needs exceed the free blocks, preempt the most recently
-     admitted running sequence: free it, put it at the front of the queue;
-     when readmitted it prefills again over prompt + generated - 1 tokens;
+  2. each running sequence past its prefill needs room for one more token,
+     and the oldest running sequence still in prefill needs room for its
+     next slice; while those needs exceed the free blocks, preempt the most
+     recently admitted running sequence (for the slice, never that prefill
+     itself or an older one; for the decodes, whichever is newest): free
+     it, put it at the front of the queue; when readmitted it prefills
+     again over prompt + generated - 1 tokens.  The oldest running request
+     therefore always advances (slices of several prefills cannot hold all
+     blocks while waiting on each other);
   3. those sequences each append one token and generate one;
   4. with budget = max_batch_tokens - decode tokens, running prefills take
      min(rest, chunk, budget) tokens in admission order, stopping at the
@@ -138,9 +143,21 @@ class OracleScheduler:
             self.waiting.append(i)
 
         while self.running:
-            need = sum(self._need(self.reqs[i].seq, 1) for i in self.running
-                       if self._decoding(self.reqs[i]))
-            if need <= self._free_blocks():
+            dec = [i for i in self.running if self._decoding(self.reqs[i])]
+            dec_need = sum(self._need(self.reqs[i].seq, 1) for i in dec)
+            pf = [i for i in self.running
+                  if not self._decoding(self.reqs[i]) and self.reqs[i].prefilled < self.reqs[i].target]
+            first = pf[0] if pf else None
+            pf_need = 0
+            if first is not None:
+                r0 = self.reqs[first]
+                n = min(r0.target - r0.prefilled, self.chunk, self.max_batch_tokens - len(dec))
+                if n > 0:
+                    pf_need = self._need(r0.seq, n)
+            free = self._free_blocks()
+            # the decodes' room may displace any newest sequence; the oldest
+            # prefill's slice only sequences newer than it
+            if dec_need <= free and (dec_need + pf_need <= free or self.running[-1] == first):
                 break
             v = self.running[-1]
             r = self.reqs[v]

@@ -160,12 +160,33 @@ pkv_status pkv_sched_step(pkv_sched* s, pkv_sched_item* items, int32_t cap, pkv_
     s->waiting.push_back(id);
   }
 
-  // 2. room for one token per decoding sequence, preempting the newest
-  for (;;) {
-    int64_t need = 0;
-    for (int32_t id : s->running)
-      if (decoding(s->reqs[id])) need += append_need(p, s->reqs[id].st.seq, 1);
-    if (need <= free_blocks(p) || s->running.empty()) break;
+  // 2. room for one token per decoding sequence and for the next slice of
+  //    the oldest running prefill, preempting the newest running sequences
+  //    (never that prefill's own or older ones): the oldest running request
+  //    always advances, so sliced prefills cannot hold every block while
+  //    waiting on each other
+  while (!s->running.empty()) {
+    int64_t dec_need = 0, pf_need = 0, n_dec = 0;
+    int32_t first_pf = -1;
+    for (int32_t id : s->running) {
+      const Req& q = s->reqs[id];
+      if (decoding(q)) {
+        dec_need += append_need(p, q.st.seq, 1);
+        n_dec++;
+      } else if (first_pf < 0 && q.prefilled < q.target) {
+        first_pf = id;
+      }
+    }
+    if (first_pf >= 0) {
+      const Req& q = s->reqs[first_pf];
+      const int64_t n = std::min<int64_t>({q.target - q.prefilled, s->cfg.chunk_tokens,
+                                           int64_t(s->cfg.max_batch_tokens) - n_dec});
+      if (n > 0) pf_need = append_need(p, q.st.seq, int32_t(n));
+    }
+    const int64_t free_now = free_blocks(p);
+    // decodes come first (any newest sequence may go); the prefill's slice
+    // only displaces sequences newer than it
+    if (dec_need <= free_now && (dec_need + pf_need <= free_now || s->running.back() == first_pf)) break;
     const int32_t v = s->running.back();
     Req& q = s->reqs[v];
     drop_holder(s, v);

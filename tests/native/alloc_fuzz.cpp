@@ -2,8 +2,10 @@
 // the properties of a paged pool: free blocks are distinct and exactly the
 // blocks with refcount 0; a refcount equals the number of live tables
 // holding the block; a table holds ceil(length / block) blocks; tail waste is
-// below one block; a failed call changes nothing.  Built with address and
-// undefined-behaviour sanitizers by the CPU test suite.
+// below one block; a failed call changes nothing.  Then, per seed, the
+// hybrid manager, a whole scheduler run and the plan helpers on random
+// inputs.  Built with address and undefined-behaviour sanitizers by the CPU
+// test suite.
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
@@ -74,6 +76,135 @@ static void check_invariants(const Snapshot& s, const pkv_pool_desc& d) {
   }
 }
 
+// Hybrid manager: slots held == sequences held, refusals change nothing.
+static void fuzz_hybrid(std::mt19937& rng) {
+  pkv_pool_desc d{};
+  d.num_blocks = 4 + int(rng() % 40);
+  d.block_size = 16;
+  d.num_kv_heads = 1;
+  d.head_dim = 8;
+  d.max_blocks_per_seq = 1 + int(rng() % 8);
+  d.dtype = PKV_BF16;
+  pkv_pool* p = nullptr;
+  CHECK(pkv_pool_create(&d, nullptr, nullptr, nullptr, &p) == PKV_OK);
+  const int32_t ns = 1 + int32_t(rng() % 10);
+  pkv_hybrid* h = nullptr;
+  CHECK(pkv_hybrid_create(p, ns, 64, nullptr, nullptr, &h) == PKV_OK);
+  std::vector<int32_t> held;
+  std::vector<int32_t> pairs(2 * 1024);
+  for (int op = 0; op < 500; ++op) {
+    pkv_hybrid_stats_t a{}, b{};
+    CHECK(pkv_hybrid_stats(h, &a) == PKV_OK);
+    const int kind = int(rng() % 4);
+    int32_t seq = -1, slot = -1, n = 0;
+    pkv_status st = PKV_OK;
+    if (kind == 0) {
+      st = pkv_hybrid_admit(h, int32_t(rng() % 80), &seq, &slot, nullptr);
+      if (st == PKV_OK) held.push_back(seq);
+    } else if (kind == 1 && !held.empty()) {
+      st = pkv_hybrid_fork(h, held[rng() % held.size()], &seq, &slot);
+      if (st == PKV_OK) held.push_back(seq);
+    } else if (kind == 2 && !held.empty()) {
+      const size_t i = rng() % held.size();
+      CHECK(pkv_hybrid_free(h, held[i]) == PKV_OK);
+      held.erase(held.begin() + i);
+    } else {
+      CHECK(pkv_hybrid_take_copies(h, pairs.data(), 1024, &n) == PKV_OK);
+      for (int32_t i = 0; i < 2 * n; ++i) CHECK(pairs[i] >= 0 && pairs[i] < ns);
+    }
+    CHECK(pkv_hybrid_stats(h, &b) == PKV_OK);
+    CHECK(b.free_slots + b.used_slots == ns);
+    CHECK(b.used_slots == int64_t(held.size()));
+    if (st != PKV_OK) CHECK(b.used_slots == a.used_slots && b.refusals >= a.refusals);
+  }
+  for (int32_t s : held) CHECK(pkv_hybrid_free(h, s) == PKV_OK);
+  pkv_stats_t ps{};
+  CHECK(pkv_stats(p, &ps) == PKV_OK);
+  CHECK(ps.used_blocks == 0);
+  CHECK(pkv_hybrid_destroy(h) == PKV_OK);
+  CHECK(pkv_pool_destroy(p) == PKV_OK);
+}
+
+// Scheduler: runs a random request stream to the end; every request ends
+// finished with all its tokens or rejected, and the pool ends empty.
+static void fuzz_scheduler(std::mt19937& rng) {
+  pkv_pool_desc d{};
+  d.num_blocks = 16 + int(rng() % 200);
+  d.block_size = 16;
+  d.num_kv_heads = 1;
+  d.head_dim = 8;
+  d.max_blocks_per_seq = 4 + int(rng() % 40);
+  d.dtype = PKV_F16;
+  pkv_pool* p = nullptr;
+  CHECK(pkv_pool_create(&d, nullptr, nullptr, nullptr, &p) == PKV_OK);
+  const int32_t n = 1 + int32_t(rng() % 40);
+  std::vector<pkv_request> reqs(n);
+  for (int32_t i = 0; i < n; ++i) {
+    pkv_request& r = reqs[i];
+    r.arrival = int32_t(rng() % 50);
+    r.prompt_len = 1 + int32_t(rng() % 400);
+    r.output_len = 1 + int32_t(rng() % 60);
+    r.klass = int32_t(rng() % 2);
+    r.prefix_id = rng() % 3 == 0 ? int32_t(rng() % 2) : -1;
+    r.prefix_len = r.prefix_id >= 0 ? 16 * int32_t(rng() % 4) : 0;
+    if (r.prefix_id >= 0 && r.prompt_len <= r.prefix_len) r.prompt_len = r.prefix_len + 1;
+  }
+  pkv_sched_config cfg{};
+  cfg.max_batch_tokens = 8 + int32_t(rng() % 512);
+  cfg.chunk_tokens = 1 + int32_t(rng() % 256);
+  cfg.max_running = 1 + int32_t(rng() % 16);
+  pkv_sched* s = nullptr;
+  CHECK(pkv_sched_create(p, &cfg, reqs.data(), n, &s) == PKV_OK);
+  std::vector<pkv_sched_item> items(cfg.max_running);
+  pkv_sched_stats_t st{};
+  int steps = 0;
+  do {
+    pkv_sched_step_info info{};
+    CHECK(pkv_sched_step(s, items.data(), cfg.max_running, &info) == PKV_OK);
+    CHECK(info.n_items <= cfg.max_running);
+    CHECK(info.prefill_tokens + info.decode_tokens <= cfg.max_batch_tokens);
+    CHECK(pkv_sched_stats(s, &st) == PKV_OK);
+    CHECK(++steps < 200000);
+  } while (st.finished + st.rejected < n);
+  pkv_sched_step_info info{};
+  CHECK(pkv_sched_step(s, items.data(), cfg.max_running, &info) == PKV_OK && info.n_items == 0);
+  for (int32_t i = 0; i < n; ++i) {
+    pkv_request_state rs{};
+    CHECK(pkv_sched_request(s, i, &rs) == PKV_OK);
+    CHECK(rs.state == PKV_REQ_REJECTED || (rs.state == PKV_REQ_FINISHED && rs.generated == reqs[i].output_len));
+  }
+  pkv_stats_t ps{};
+  CHECK(pkv_stats(p, &ps) == PKV_OK);
+  CHECK(ps.used_blocks == 0 && ps.free_blocks == d.num_blocks);
+  CHECK(pkv_sched_destroy(s) == PKV_OK);
+  CHECK(pkv_pool_destroy(p) == PKV_OK);
+}
+
+// Plans and the utilisation count on random inputs (bounds of the outputs).
+static void fuzz_plans(std::mt19937& rng) {
+  const int32_t b = 1 + int32_t(rng() % 20);
+  std::vector<int32_t> ql(b), cl(b);
+  for (int32_t i = 0; i < b; ++i) {
+    ql[i] = 1 + int32_t(rng() % 300);
+    cl[i] = ql[i] + int32_t(rng() % 2000);
+  }
+  const int32_t hkv = 1 + int32_t(rng() % 4), hq = hkv * (1 + int32_t(rng() % 20));
+  int32_t need = 0;
+  CHECK(pkv_prefill_plan_ints(ql.data(), b, hq, hkv, &need) == PKV_OK);
+  std::vector<int32_t> plan(need);
+  pkv_prefill_plan_info info{};
+  CHECK(pkv_prefill_plan(ql.data(), cl.data(), b, hq, hkv, plan.data(), need, &info) == PKV_OK);
+  CHECK(info.plan_ints == need);
+  for (int32_t w = 0; w < info.n_work; ++w) {
+    CHECK(plan[2 * w] >= 0 && plan[2 * w] < b);
+    CHECK(plan[2 * w + 1] >= 0 && plan[2 * w + 1] * info.tile_tokens < ql[plan[2 * w]]);
+  }
+  CHECK(pkv_prefill_plan(ql.data(), cl.data(), b, hq, hkv, plan.data(), need - 1, &info) == PKV_E_BAD_ARG);
+  pkv_utilisation_t u{};
+  CHECK(pkv_utilisation(ql.data(), b, 300, 16, &u) == PKV_OK);
+  CHECK(u.paged_waste_tokens >= 0 && u.paged_waste_tokens < 16 * b);
+}
+
 int main(int argc, char** argv) {
   const int seeds = argc > 1 ? std::atoi(argv[1]) : 20;
   for (int seed = 0; seed < seeds; ++seed) {
@@ -95,7 +226,7 @@ int main(int argc, char** argv) {
     for (int op = 0; op < 2000; ++op) {
       Snapshot before = snap(p, d);
       pkv_status st = PKV_OK;
-      int kind = int(rng() % 7);
+      int kind = int(rng() % 8);
       int32_t any = before.live.empty() ? 12345 : before.live[rng() % before.live.size()];
       if (rng() % 50 == 0) any = 99999;  // unknown id
       int32_t out = 0;
@@ -114,6 +245,14 @@ int main(int argc, char** argv) {
         case 3: st = pkv_seq_fork(p, any, &out); break;
         case 4: st = pkv_seq_free(p, any); break;
         case 5: st = pkv_take_cow(p, pairs.data(), 4096, &out); break;
+        case 7: {
+          int32_t len = 0;
+          const bool known = pkv_seq_length(p, any, &len) == PKV_OK;
+          const int32_t n = known ? int32_t(rng() % (len + 2)) : 3;  // len + 1: refused
+          st = pkv_seq_fork_prefix(p, any, n, &out);
+          if (known && n > len) CHECK(st == PKV_E_BAD_ARG);
+          break;
+        }
         case 6: {
           std::vector<int32_t> tab(before.live.size() * d.max_blocks_per_seq + 1), lens(before.live.size() + 1);
           st = pkv_build_batch(p, before.live.data(), int32_t(before.live.size()), tab.data(),
@@ -130,6 +269,9 @@ int main(int argc, char** argv) {
     CHECK(pkv_stats(p, &s) == PKV_OK);
     CHECK(s.free_blocks + s.used_blocks == d.num_blocks);
     CHECK(pkv_pool_destroy(p) == PKV_OK);
+    fuzz_hybrid(rng);
+    fuzz_scheduler(rng);
+    fuzz_plans(rng);
   }
   std::printf("alloc_fuzz ok (%d seeds)\n", seeds);
   return 0;

@@ -1,7 +1,8 @@
-"""The host allocator under AddressSanitizer and UBSan (CPU, g++ only).
+"""The host library under AddressSanitizer and UBSan (CPU, g++ only).
 
-Builds tests/native/alloc_fuzz.cpp together with the allocator sources
-(no GPU code) and runs seeded random operations with invariant checks.
+Builds tests/native/alloc_fuzz.cpp together with every host source (no GPU
+code): allocator, plans, staging, scheduler, hybrid manager, utilisation;
+runs seeded random operations with invariant checks.
 """
 
 import os
@@ -21,7 +22,8 @@ def test_allocator_fuzz_under_sanitizers(tmp_path):
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-I" + os.path.join(ROOT, "include"),
            os.path.join(ROOT, "tests", "native", "alloc_fuzz.cpp"),
-           os.path.join(SRC, "pool.cpp"), os.path.join(SRC, "plan.cpp"), "-o", exe]
+           *[os.path.join(SRC, f) for f in ("pool.cpp", "plan.cpp", "prepare.cpp", "prefill_plan.cpp",
+                                            "utilisation.cpp", "hybrid.cpp", "sched.cpp")], "-o", exe]
     b = subprocess.run(cmd, capture_output=True, text=True)
     assert b.returncode == 0, b.stderr
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")

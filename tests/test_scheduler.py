@@ -123,3 +123,14 @@ def test_bad_requests():
             Scheduler(pool, [dict(arrival=0, prompt_len=0, output_len=1)], 64, 16, 2)
     finally:
         pool.close()
+
+
+def test_sliced_prefills_do_not_deadlock():
+    # two 200-token prompts in 32-token slices in a 16-block pool: both partial
+    # prefills would fill the pool and wait on each other; the newer one is
+    # preempted so that the older completes, then the newer runs
+    reqs = [dict(arrival=0, prompt_len=200, output_len=3, klass=0, prefix_id=-1, prefix_len=0),
+            dict(arrival=0, prompt_len=200, output_len=3, klass=0, prefix_id=-1, prefix_len=0)]
+    st, states = run_lockstep(reqs, 16, 16, 64, 32, 4, max_steps=200)
+    assert st["finished"] == 2 and st["preemptions"] >= 1
+    assert states[0]["finished_at"] < states[1]["finished_at"]
