@@ -81,6 +81,9 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="gpt_f16")
     ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = library default)")
+    ap.add_argument("--max-keys", type=int, default=None,
+                    help="prefill workloads: split tiles attending more keys (0 = never, -1 = the "
+                         "library's rule for under-filled launches; default -1)")
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -320,6 +323,7 @@ def bench_prefix_shared(args, cfg):
 
 
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix-core peak
+PREFILL_MAX_KEYS = -1      # prefill key split: -1 = the library's rule (only under-filled launches)
 
 
 def prefill_flops(q_len: int, ctx_len: int, num_q_heads: int, head_dim: int) -> int:
@@ -340,9 +344,11 @@ def bench_prefill(args, cfg):
     import numpy as np
     import torch
 
-    from paged_kv_cache_257_amd import Pool, prefill_plan
+    from paged_kv_cache_257_amd import Pool, prefill_plan, prefill_workspace_bytes
     from workloads import draw_normal_storage
     from workloads.prefill import draw_prefill_shapes
+
+    max_keys = PREFILL_MAX_KEYS if args.max_keys is None else args.max_keys
 
     sh = draw_prefill_shapes(cfg)
     H, Hq, d, dt = cfg.num_kv_heads, cfg.num_q_heads, cfg.head_dim, cfg.dtype
@@ -376,7 +382,7 @@ def bench_prefill(args, cfg):
         sl = slots[o:o + chunk]
         pool.write_kv(ck[:sl.numel()], cv[:sl.numel()], sl)
     del ck, cv
-    launches, flops = [], []
+    launches, flops, ws_bytes = [], [], 0
     max_q = max(sum(n for _, _, n in step) for step in sh.steps)
     q_all = dev(draw_normal_storage((cfg.seed, 62), (max_q, Hq, d), dt))
     out = torch.empty((max_q, Hq, d), dtype=torch.float32, device="cuda")
@@ -385,18 +391,21 @@ def bench_prefill(args, cfg):
         q_lens = np.array([n for _, _, n in step])
         lens = np.array([t0 + n for _, t0, n in step], dtype=np.int32)
         tables, _ = pool.build_batch(seqs, width)
-        plan, info = prefill_plan(q_lens, lens, Hq, H)
+        plan, info = prefill_plan(q_lens, lens, Hq, H, max_keys)
         launches.append((torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
                          torch.from_numpy(plan).cuda(), info, int(q_lens.sum())))
+        ws_bytes = max(ws_bytes, prefill_workspace_bytes(info, d))
         flops.append(sum(prefill_flops(int(n), int(L), Hq, d) for n, L in zip(q_lens, lens)))
     total_tokens = int(sh.prompts.sum())
+    # zeroed once: every launch leaves the split tiles' tickets at zero
+    workspace = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in launches] for _ in range(args.warmup + args.steps)]
 
     def schedule(r):
         for k, (tb, ln, pl, info, nq) in enumerate(launches):
             ev[r][k][0].record()
-            pool.paged_prefill(q_all[:nq], out[:nq], tb, ln, cfg.scale, pl, info)
+            pool.paged_prefill(q_all[:nq], out[:nq], tb, ln, cfg.scale, pl, info, workspace)
             ev[r][k][1].record()
 
     for r in range(args.warmup):
@@ -424,6 +433,8 @@ def bench_prefill(args, cfg):
         "data": "synthetic",
         "config": {"workload": cfg.name, "prompts": len(sh.prompts), "prompt_tokens": total_tokens,
                    "chunk_tokens": cfg.chunk_tokens, "launches_per_step": len(launches),
+                   "max_keys_per_item": max_keys,
+                   "split_tiles_per_step": int(sum(l[3].n_split for l in launches)),
                    "num_q_heads": Hq, "num_kv_heads": H, "head_dim": d, "block_size": 16,
                    "accumulate": "f32", "output": "f32"},
         "prompt_tokens_per_s": round(total_tokens * args.steps / wall, 1),

@@ -401,8 +401,13 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
                            int32_t partition_tokens, int32_t* plan, int32_t cap,
                            pkv_decode_plan_info* info);
 
-/* Device workspace bytes pkv_paged_decode needs for this plan: completion
- * tickets for num_seqs x num_q_heads, then the split-K partials. */
+/* Device workspace bytes pkv_paged_decode needs for this plan: the split-K
+ * partial records (from the workspace's start) and completion tickets for
+ * num_seqs x num_q_heads (at its end; they must be zero before the first
+ * launch and every launch leaves them zero).  A workspace reused by
+ * launches of different shapes must be sized for the largest of them
+ * (pkv_decode_workspace_bound does that), so that no launch's records
+ * overlap another's tickets. */
 size_t pkv_decode_workspace_bytes(const pkv_decode_plan_info* info, int32_t num_q_heads,
                                   int32_t head_dim);
 
@@ -423,16 +428,24 @@ int32_t pkv_default_partition_tokens(void);
  * batching", 01 · Conceito, the scheduler paragraph: long prefills are cut
  * into slices).  Sequence i brings q_lens[i] >= 1 new tokens that are the
  * last q_lens[i] of its context_lens[i] tokens (already appended and
- * written).  A work item is one tile of tile_tokens consecutive query
- * tokens of one sequence; the kernel runs every item for every KV head.
- * tile_tokens is 128 / Gw with Gw the largest power of two <= 16 dividing
- * H_q / H_kv (Gw query heads of one KV head share a tile).  Items are
- * ordered by decreasing number of keys they attend.
+ * written).  A tile is tile_tokens consecutive query tokens of one
+ * sequence; tile_tokens is 128 / Gw with Gw the largest power of two <= 16
+ * dividing H_q / H_kv (Gw query heads of one KV head share a tile).  A tile
+ * whose last query attends more than max_keys keys (max_keys > 0) is split
+ * into parts of at most max_keys keys (whole 32-key stages); max_keys = 0
+ * never splits; max_keys < 0 splits only a launch that would have fewer
+ * than 512 workgroups, with a limit that brings it to about 512 (at least
+ * 1024 keys per part).  Each part is a work item, and the parts' partial softmax states are merged in the same
+ * launch (workspace: pkv_prefill_workspace_bytes).  The kernel runs every
+ * item for every KV head.  Items are ordered by decreasing number of keys.
  *
  * plan (host int32, cap >= pkv_prefill_plan_ints(...)) receives
- *   [0, 2*n_work)                      items (sequence, tile index)
- *   [2*n_work, 2*n_work + num_seqs + 1) q_start: first query row of each
+ *   [0, 6*n_work)                      items (sequence, tile, first stage,
+ *                                       end stage, split tile index or -1,
+ *                                       part index)
+ *   [6*n_work, .. + num_seqs + 1)      q_start: first query row of each
  *                                       sequence in q / out (prefix sums)
+ *   [.., + 2*n_split)                  per split tile (first partial, parts)
  * Upload it unchanged and pass the device copy to pkv_paged_prefill. */
 typedef struct {
   int32_t num_seqs;
@@ -443,13 +456,24 @@ typedef struct {
   int32_t total_q;
   int32_t max_context_len;
   int32_t plan_ints;
+  int32_t n_split;     /* tiles split into several parts                 */
+  int32_t n_partials;  /* parts of split tiles, summed                   */
 } pkv_prefill_plan_info;
 
-pkv_status pkv_prefill_plan_ints(const int32_t* q_lens, int32_t num_seqs, int32_t num_q_heads,
-                                 int32_t num_kv_heads, int32_t* plan_ints);
+pkv_status pkv_prefill_plan_ints(const int32_t* q_lens, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t max_keys, int32_t* plan_ints);
 pkv_status pkv_prefill_plan(const int32_t* q_lens, const int32_t* context_lens, int32_t num_seqs,
-                            int32_t num_q_heads, int32_t num_kv_heads, int32_t* plan, int32_t cap,
-                            pkv_prefill_plan_info* info);
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t max_keys,
+                            int32_t* plan, int32_t cap, pkv_prefill_plan_info* info);
+/* Device workspace bytes pkv_paged_prefill needs for this plan (0 when no
+ * tile is split): one record per (part, head group, tile row): o[head_dim],
+ * m, l as fp32 padded to whole 128-byte lines, from the workspace's start;
+ * completion tickets [n_split][H_q / Gw] int32 at its end.  The tickets
+ * must be zero before the first launch; every launch leaves them zero.  A
+ * workspace reused by launches of different shapes must be sized for the
+ * largest records plus the largest tickets. */
+size_t pkv_prefill_workspace_bytes(const pkv_prefill_plan_info* info, int32_t head_dim);
 
 /* ---------------------------------------------------------------------------
  * Host: one decode iteration's metadata in one staging buffer
@@ -618,13 +642,16 @@ pkv_status pkv_paged_decode_reduce(const pkv_pool* pool, const void* q, const vo
  * pool (pkv_seq_append / pkv_write_kv).  q: device [total_q][H_q][head_dim]
  * in the pool dtype; out: device fp32 [total_q][H_q][head_dim]; block_tables
  * / context_lens as for decode; plan / info from pkv_prefill_plan (plan
- * uploaded).  fp16 and bf16 pools, head_dim 64 or 128 (else
- * PKV_E_UNSUPPORTED); the products run on the matrix cores with fp32
- * accumulation.  Asynchronous on `stream`; allocates nothing. */
+ * uploaded); workspace (device, zeroed once, every launch leaves its
+ * tickets zero) of at least pkv_prefill_workspace_bytes(info, head_dim)
+ * bytes, may be NULL when no tile is split.  fp16 and bf16 pools, head_dim
+ * 64 or 128 (else PKV_E_UNSUPPORTED); the products run on the matrix cores
+ * with fp32 accumulation.  Asynchronous on `stream`; allocates nothing. */
 pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, float* out, int32_t num_seqs,
                              int32_t num_q_heads, const int32_t* block_tables, int32_t table_stride,
                              const int32_t* context_lens, float scale, const int32_t* plan,
-                             const pkv_prefill_plan_info* info, void* stream);
+                             const pkv_prefill_plan_info* info, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -40,7 +40,8 @@ class PlanInfo(C.Structure):
 
 class PrefillPlanInfo(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("num_seqs", "num_q_heads", "num_kv_heads", "tile_tokens",
-                                         "n_work", "total_q", "max_context_len", "plan_ints")]
+                                         "n_work", "total_q", "max_context_len", "plan_ints",
+                                         "n_split", "n_partials")]
 
 
 class Utilisation(C.Structure):
@@ -162,8 +163,9 @@ SIGNATURES = {
     "pkv_decode_workspace_bytes": [C.POINTER(PlanInfo), I32, I32],
     "pkv_decode_workspace_bound": [I32, I32, I32, I32, I32, I32],
     "pkv_default_partition_tokens": [],
-    "pkv_prefill_plan_ints": [PI32, I32, I32, I32, PI32],
-    "pkv_prefill_plan": [PI32, PI32, I32, I32, I32, PI32, I32, C.POINTER(PrefillPlanInfo)],
+    "pkv_prefill_plan_ints": [PI32, PI32, I32, I32, I32, I32, PI32],
+    "pkv_prefill_plan": [PI32, PI32, I32, I32, I32, I32, PI32, I32, C.POINTER(PrefillPlanInfo)],
+    "pkv_prefill_workspace_bytes": [C.POINTER(PrefillPlanInfo), I32],
     "pkv_prepare_decode_bytes": [I32, I32, I32, I32, I32],
     "pkv_prepare_decode": [P, PI32, I32, I32, I32, I32, P, C.c_size_t, C.POINTER(BatchLayout)],
     "pkv_stepper_slot_bytes": [I32, I32, I32, I32],
@@ -176,11 +178,13 @@ SIGNATURES = {
     "pkv_paged_decode": DECODE_ARGS,
     "pkv_paged_decode_partitions": DECODE_ARGS,
     "pkv_paged_decode_reduce": DECODE_ARGS,
-    "pkv_paged_prefill": [P, P, P, I32, I32, P, I32, P, C.c_float, P, C.POINTER(PrefillPlanInfo), P],
+    "pkv_paged_prefill": [P, P, P, I32, I32, P, I32, P, C.c_float, P, C.POINTER(PrefillPlanInfo), P,
+                          C.c_size_t, P],
     "pkv_last_error": [],
 }
 RESTYPES = {"pkv_last_error": C.c_char_p, "pkv_decode_workspace_bytes": C.c_size_t,
             "pkv_decode_workspace_bound": C.c_size_t, "pkv_default_partition_tokens": C.c_int32,
+            "pkv_prefill_workspace_bytes": C.c_size_t,
             "pkv_prepare_decode_bytes": C.c_size_t, "pkv_stepper_slot_bytes": C.c_size_t}
 DEVICE_FUNCS = ("pkv_copy_blocks", "pkv_write_kv", "pkv_paged_decode", "pkv_paged_decode_partitions",
                 "pkv_paged_decode_reduce", "pkv_paged_prefill", "pkv_hybrid_copy_states",

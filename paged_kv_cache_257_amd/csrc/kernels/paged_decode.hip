@@ -546,12 +546,16 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
   prm.context_lens = context_lens;
   prm.work = plan;
   prm.part_offset = plan + 2 * int64_t(info->n_work);
-  // workspace: completion tickets [num_seqs][H_q] (256-byte aligned), then
-  // one record per (partial, query head): o[D], m, l, padded to 128 bytes
+  // workspace: records from its start, one per (partial, query head):
+  // o[D], m, l padded to 128 bytes; completion tickets [num_seqs][H_q] at
+  // its end (128-byte aligned).  A workspace shared by launches of
+  // different shapes and sized for the largest (pkv_decode_workspace_bound)
+  // therefore never has one launch's records where another's tickets are.
   char* ws = static_cast<char*>(workspace);
   const int64_t ticket_bytes = (int64_t(num_seqs) * num_q_heads * 4 + 255) / 256 * 256;
-  prm.counters = reinterpret_cast<int32_t*>(ws);
-  prm.part = reinterpret_cast<float*>(ws + ticket_bytes);
+  prm.part = reinterpret_cast<float*>(ws);
+  prm.counters = reinterpret_cast<int32_t*>(
+      ws + ((int64_t(workspace_bytes) - ticket_bytes) & ~int64_t(127)));
   prm.rec_floats = int32_t(((int64_t(d.head_dim) + 2) * 4 + 127) / 128 * 32);
   prm.num_q_heads = num_q_heads;
   prm.num_kv_heads = d.num_kv_heads;

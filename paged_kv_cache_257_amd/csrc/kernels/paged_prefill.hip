@@ -63,8 +63,14 @@ struct PrefillParams {
   const char* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  const int32_t* work;       // [n_work][2] (sequence, tile)
+  const int32_t* work;       // [n_work][6] (sequence, tile, stage begin, stage end, split, part)
   const int32_t* q_start;    // [num_seqs + 1]
+  const int32_t* split_tab;  // [n_split][2] (first partial, parts)
+  int32_t* counters;         // [n_split][hgroups] completion tickets
+  float* part;               // [n_partials][hgroups][tile rows] records of rec_floats
+  int32_t rec_floats;        // o[D], m, l padded to whole 128-byte lines
+  int32_t n_split;
+  int32_t n_partials;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;             // H_q / H_kv
@@ -111,7 +117,10 @@ __device__ __forceinline__ uint32_t round16<PKV_BF16>(float x, float* back) {
 // Three waves per SIMD: the compiler then keeps the accumulators in the
 // arch registers (no spills) and a CU runs three workgroups, whose MFMA and
 // softmax phases overlap.
-template <int DT, int D, int GW>
+// SPLIT: the plan splits some tiles' keys into parts; without it the kernel
+// carries no code for partial records (the main loop then keeps its
+// registers: that code alone cost 13% on unsplit launches).
+template <int DT, int D, int GW, bool SPLIT>
 __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const PrefillParams p) {
   constexpr int RG = kPfRowGroups;         // 16-row groups per wave
   constexpr int TPW = 16 * RG / GW;        // query tokens per wave
@@ -143,8 +152,10 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
   const int hgroups = p.num_kv_heads * p.hgroups_per_kv;
   const int wi = blockIdx.x / hgroups;
   const int hg = blockIdx.x - wi * hgroups;
-  const int seq = p.work[2 * wi];
-  const int tile = p.work[2 * wi + 1];
+  const int32_t* item = p.work + 6 * int64_t(wi);
+  const int seq = item[0];
+  const int tile = item[1];
+  const int split = SPLIT ? item[4] : -1;
   const int kvh = hg / p.hgroups_per_kv;
   const int qh0 = kvh * p.group + (hg - kvh * p.hgroups_per_kv) * GW;
   const int L = p.context_lens[seq];
@@ -173,6 +184,8 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
   const int wave_last = min(wave_first + TPW, T) - 1;  // < wave_first: no rows
   const int wg_last = min(t0 + TQ, T) - 1;
   const int wg_stages = (C + wg_last) / kStage + 1;
+  const int s_begin = SPLIT ? item[2] : 0;
+  const int s_end = SPLIT ? min(item[3], wg_stages) : wg_stages;
   const int wave_stages = wave_last >= wave_first ? (C + wave_last) / kStage + 1 : 0;
   const int mask_from = (C + wave_first) / kStage;  // first stage with a masked key
 
@@ -341,53 +354,150 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
     }
   };
 
-  load_stage(0);
-  store_stage(0, 0);
-  __syncthreads();
-  for (int st = 0; st < wg_stages; ++st) {
-    const int buf = st & 1;
-    const bool more = st + 1 < wg_stages;
-    if (more) load_stage(st + 1);
-    if (st < wave_stages) compute(buf, st);
-    if (more) store_stage(buf ^ 1, st + 1);
+  if constexpr (!SPLIT) {
+    // the whole tile, from stage 0 (kept apart from the stage-range loop
+    // below: the compiler schedules this form better)
+    load_stage(0);
+    store_stage(0, 0);
     __syncthreads();
+    for (int st = 0; st < wg_stages; ++st) {
+      const int buf = st & 1;
+      const bool more = st + 1 < wg_stages;
+      if (more) load_stage(st + 1);
+      if (st < wave_stages) compute(buf, st);
+      if (more) store_stage(buf ^ 1, st + 1);
+      __syncthreads();
+    }
+  } else {
+    if (s_begin < s_end) {
+      load_stage(s_begin);
+      store_stage(0, s_begin);
+      __syncthreads();
+    }
+    for (int st = s_begin; st < s_end; ++st) {
+      const int buf = (st - s_begin) & 1;
+      const bool more = st + 1 < s_end;
+      if (more) load_stage(st + 1);
+      if (st < wave_stages) compute(buf, st);
+      if (more) store_stage(buf ^ 1, st + 1);
+      __syncthreads();
+    }
   }
 
+  float lt[RG];
 #pragma unroll
   for (int j = 0; j < RG; ++j) {
-    float lt = lsum[j] + __shfl_xor(lsum[j], 16);
-    lt += __shfl_xor(lt, 32);
-    if (row_ok[j]) {
-      const float inv = 1.f / lt;
-      float* orow = p.out + (int64_t(qs + tq[j]) * p.num_q_heads + h) * D;
+    lt[j] = lsum[j] + __shfl_xor(lsum[j], 16);
+    lt[j] += __shfl_xor(lt[j], 32);
+  }
+  if (!SPLIT || split < 0) {
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      if (row_ok[j]) {
+        const float inv = 1.f / lt[j];
+        float* orow = p.out + (int64_t(qs + tq[j]) * p.num_q_heads + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          *reinterpret_cast<f4*>(orow + dt * 16 + 4 * g) = o[j][dt] * inv;
+      }
+    }
+    return;
+  }
+
+  if constexpr (SPLIT) {
+  // A part of a split tile: its (o, m, l) per row go to a record through
+  // device-scope atomic stores (visible to any XCD without cache flushes);
+  // the part that takes the last ticket merges all parts:
+  //   M = max m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+  if (split >= p.n_split) return;
+  const int base = p.split_tab[2 * split];
+  const int parts = p.split_tab[2 * split + 1];
+  if (base < 0 || parts < 1 || base + parts > p.n_partials || item[5] >= parts) return;
+  const int hgroups_total = hgroups;
+  auto record = [&](int prt, int j) -> float* {
+    const int row = wave * 16 * RG + 16 * j + n;
+    return p.part + ((int64_t(base + prt) * hgroups_total + hg) * kPrefillTileRows + row) * p.rec_floats;
+  };
+#pragma unroll
+  for (int j = 0; j < RG; ++j) {
+    float* rec = record(item[5], j);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        __hip_atomic_store(rec + dt * 16 + 4 * g + v, o[j][dt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (g == 0) {
+      __hip_atomic_store(rec + D, m[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(rec + D + 1, lt[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __shared__ int sm_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int32_t* ticket = p.counters + int64_t(split) * hgroups_total + hg;
+  if (tid == 0)
+    sm_last = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == parts - 1);
+  __syncthreads();
+  if (!sm_last) return;
+#pragma unroll
+  for (int j = 0; j < RG; ++j) {
+    float M = kNegBig;
+    for (int prt = 0; prt < parts; ++prt)
+      M = fmaxf(M, __hip_atomic_load(record(prt, j) + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    f4 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f4{0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    for (int prt = 0; prt < parts; ++prt) {
+      const float* rec = record(prt, j);
+      const float w = __builtin_amdgcn_exp2f(
+          __hip_atomic_load(rec + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
+      den = __builtin_fmaf(w, __hip_atomic_load(rec + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), den);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        *reinterpret_cast<f4*>(orow + dt * 16 + 4 * g) = o[j][dt] * inv;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          acc[dt][v] = __builtin_fmaf(
+              w, __hip_atomic_load(rec + dt * 16 + 4 * g + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+              acc[dt][v]);
     }
+    if (row_ok[j]) {
+      const float inv = 1.f / den;
+      float* orow = p.out + (int64_t(qs + tq[j]) * p.num_q_heads + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f4*>(orow + dt * 16 + 4 * g) = acc[dt] * inv;
+    }
+  }
+    if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 typedef void (*PrefillFn)(const PrefillParams);
 
-template <int DT, int D>
+template <int DT, int D, bool SPLIT>
 PrefillFn pick_gw(int gw) {
   switch (gw) {
-    case 1: return paged_prefill_kernel<DT, D, 1>;
-    case 2: return paged_prefill_kernel<DT, D, 2>;
-    case 4: return paged_prefill_kernel<DT, D, 4>;
-    case 8: return paged_prefill_kernel<DT, D, 8>;
-    case 16: return paged_prefill_kernel<DT, D, 16>;
+    case 1: return paged_prefill_kernel<DT, D, 1, SPLIT>;
+    case 2: return paged_prefill_kernel<DT, D, 2, SPLIT>;
+    case 4: return paged_prefill_kernel<DT, D, 4, SPLIT>;
+    case 8: return paged_prefill_kernel<DT, D, 8, SPLIT>;
+    case 16: return paged_prefill_kernel<DT, D, 16, SPLIT>;
   }
   return nullptr;
 }
 
-PrefillFn pick_prefill(int32_t dtype, int32_t head_dim, int gw) {
+template <int DT, int D>
+PrefillFn pick_split(int gw, bool split) {
+  return split ? pick_gw<DT, D, true>(gw) : pick_gw<DT, D, false>(gw);
+}
+
+PrefillFn pick_prefill(int32_t dtype, int32_t head_dim, int gw, bool split) {
   if (dtype == PKV_F16) {
-    if (head_dim == 64) return pick_gw<PKV_F16, 64>(gw);
-    if (head_dim == 128) return pick_gw<PKV_F16, 128>(gw);
+    if (head_dim == 64) return pick_split<PKV_F16, 64>(gw, split);
+    if (head_dim == 128) return pick_split<PKV_F16, 128>(gw, split);
   } else if (dtype == PKV_BF16) {
-    if (head_dim == 64) return pick_gw<PKV_BF16, 64>(gw);
-    if (head_dim == 128) return pick_gw<PKV_BF16, 128>(gw);
+    if (head_dim == 64) return pick_split<PKV_BF16, 64>(gw, split);
+    if (head_dim == 128) return pick_split<PKV_BF16, 128>(gw, split);
   }
   return nullptr;
 }
@@ -401,7 +511,8 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, flo
                                         int32_t num_seqs, int32_t num_q_heads,
                                         const int32_t* block_tables, int32_t table_stride,
                                         const int32_t* context_lens, float scale, const int32_t* plan,
-                                        const pkv_prefill_plan_info* info, void* stream) {
+                                        const pkv_prefill_plan_info* info, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
   if (!pool) return fail(PKV_E_BAD_ARG, "null pool");
   const pkv_pool_desc& d = pool->desc;
   if (!pool->k_cache || !pool->v_cache) return fail(PKV_E_BAD_ARG, "pool has no device K/V arrays");
@@ -419,7 +530,7 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, flo
   while (gw < 16 && group % (2 * gw) == 0) gw *= 2;
   if (info->num_seqs != num_seqs || info->num_q_heads != num_q_heads ||
       info->num_kv_heads != d.num_kv_heads || info->tile_tokens != kPrefillTileRows / gw ||
-      info->n_work < 0)
+      info->n_work < 0 || info->n_split < 0 || info->n_partials < 0)
     return fail(PKV_E_BAD_ARG, "plan info does not match this batch");
   if (table_stride < 1) return fail(PKV_E_BAD_ARG, "table_stride must be >= 1");
   if (int64_t(info->max_context_len) > int64_t(table_stride) * kBlockTokens)
@@ -434,8 +545,24 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, flo
   prm.v_cache = static_cast<const char*>(pool->v_cache);
   prm.block_tables = block_tables;
   prm.context_lens = context_lens;
+  const size_t need = pkv_prefill_workspace_bytes(info, d.head_dim);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_E_BAD_ARG, "workspace too small: need " + std::to_string(need) + " bytes");
   prm.work = plan;
-  prm.q_start = plan + 2 * int64_t(info->n_work);
+  prm.q_start = plan + 6 * int64_t(info->n_work);
+  prm.split_tab = prm.q_start + num_seqs + 1;
+  // records from the workspace's start, tickets at its end (as for decode:
+  // launches of different shapes sharing one workspace sized for the
+  // largest never put records where another launch's tickets are)
+  const int64_t ticket_bytes =
+      (int64_t(info->n_split) * d.num_kv_heads * (group / gw) * 4 + 255) / 256 * 256;
+  prm.part = static_cast<float*>(workspace);
+  prm.counters = need > 0 ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                                       ((int64_t(workspace_bytes) - ticket_bytes) & ~int64_t(127)))
+                          : nullptr;
+  prm.rec_floats = int32_t(((int64_t(d.head_dim) + 2) * 4 + 127) / 128 * 32);
+  prm.n_split = info->n_split;
+  prm.n_partials = info->n_partials;
   prm.num_q_heads = num_q_heads;
   prm.num_kv_heads = d.num_kv_heads;
   prm.group = group;
@@ -445,7 +572,7 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, flo
   prm.scale_log2 = scale * kLog2eF;
   const int64_t grid = int64_t(info->n_work) * d.num_kv_heads * (group / gw);
   if (grid > INT32_MAX) return fail(PKV_E_BAD_ARG, "batch too large for one launch");
-  PrefillFn fn = pick_prefill(d.dtype, d.head_dim, gw);
+  PrefillFn fn = pick_prefill(d.dtype, d.head_dim, gw, info->n_split > 0);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no prefill kernel for this dtype / head_dim / group");
   hipLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kPfThreads), 0, static_cast<hipStream_t>(stream), prm);
   return launch_status("paged_prefill launch");

@@ -183,31 +183,41 @@ class Pool:
 
 
     def paged_prefill(self, q, out, block_tables, context_lens, scale: float, plan,
-                      info: PrefillPlanInfo, stream=None) -> None:
+                      info: PrefillPlanInfo, workspace=None, stream=None) -> None:
         """Causal attention of chunked-prefill queries (see pkv_paged_prefill).
 
         q: device [total_q][H_q][d] (pool dtype); out: device fp32, same
-        shape; ``plan``/``info`` from ``prefill_plan`` (plan on the device)."""
+        shape; ``plan``/``info`` from ``prefill_plan`` (plan on the device);
+        ``workspace``: zeroed device tensor of ``prefill_workspace_bytes``
+        bytes when the plan splits tiles."""
         Hq = int(q.shape[1])
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
         check(self.lib, self.lib.pkv_paged_prefill(
             self.handle, _dptr(q), _dptr(out), int(info.num_seqs), Hq, _dptr(block_tables),
             int(block_tables.shape[1]), _dptr(context_lens), float(scale), _dptr(plan),
-            C.byref(info), _stream_ptr(stream)))
+            C.byref(info), _dptr(workspace), ws_bytes, _stream_ptr(stream)))
 
 
-def prefill_plan(q_lens, context_lens, num_q_heads: int, num_kv_heads: int,
+def prefill_plan(q_lens, context_lens, num_q_heads: int, num_kv_heads: int, max_keys: int = 0,
                  host_only: bool = False) -> Tuple[np.ndarray, PrefillPlanInfo]:
-    """Host work list of a chunked-prefill launch (see pkv_prefill_plan)."""
+    """Host work list of a chunked-prefill launch (see pkv_prefill_plan);
+    tiles attending more than ``max_keys`` keys (> 0) are split."""
     lib = _capi.load(host_only=host_only)
     ql = np.ascontiguousarray(q_lens, dtype=np.int32)
     cl = np.ascontiguousarray(context_lens, dtype=np.int32)
     n = C.c_int32()
-    check(lib, lib.pkv_prefill_plan_ints(i32p(ql), len(ql), num_q_heads, num_kv_heads, C.byref(n)))
+    check(lib, lib.pkv_prefill_plan_ints(i32p(ql), i32p(cl), len(ql), num_q_heads, num_kv_heads,
+                                         int(max_keys), C.byref(n)))
     plan = np.empty(max(n.value, 1), dtype=np.int32)
     info = PrefillPlanInfo()
     check(lib, lib.pkv_prefill_plan(i32p(ql), i32p(cl), len(ql), num_q_heads, num_kv_heads,
-                                    i32p(plan), len(plan), C.byref(info)))
+                                    int(max_keys), i32p(plan), len(plan), C.byref(info)))
     return plan[:info.plan_ints], info
+
+
+def prefill_workspace_bytes(info: PrefillPlanInfo, head_dim: int, host_only: bool = False) -> int:
+    lib = _capi.load(host_only=host_only)
+    return int(lib.pkv_prefill_workspace_bytes(C.byref(info), head_dim))
 
 
 def decode_plan(context_lens: np.ndarray, partition_tokens: int = 0, block_size: int = 16,

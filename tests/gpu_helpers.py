@@ -90,17 +90,19 @@ class DecodeCase:
         sync()
         del k, v
 
-    def decode(self, partition_tokens=0, split=False, append=False):
+    def decode(self, partition_tokens=0, split=False, append=False, workspace=None):
         """Decode the batch; ``append`` passes each sequence's newest token as
-        k_new/v_new (fused store + decode)."""
+        k_new/v_new (fused store + decode); ``workspace`` (optional, zeroed
+        once by the caller) is reused instead of a fresh one."""
         cfg = self.cfg
         tables, lens = self.pool.build_batch(self.seqs, self.stride)
         plan, info = decode_plan(lens, partition_tokens)
         q = to_device(self.vals["q"], cfg.dtype)
         out = torch.full((len(self.lens), cfg.num_q_heads, cfg.head_dim), float("nan"),
                          dtype=torch.float32, device="cuda")
-        ws = decode_workspace_bytes(info, cfg.num_q_heads, cfg.head_dim)
-        workspace = torch.zeros(max(ws // 4, 1), dtype=torch.float32, device="cuda")
+        if workspace is None:
+            ws = decode_workspace_bytes(info, cfg.num_q_heads, cfg.head_dim)
+            workspace = torch.zeros(max(ws // 4, 1), dtype=torch.float32, device="cuda")
         k_new = v_new = None
         if append:
             rows = self.last_rows()
@@ -110,8 +112,8 @@ class DecodeCase:
                                cfg.scale, torch.from_numpy(plan).cuda(), info, workspace,
                                k_new=k_new, v_new=v_new, split=split)
         sync()
-        ntickets = -(-len(self.lens) * cfg.num_q_heads * 4 // 256) * 64
-        tickets_zero = bool((workspace[:ntickets].view(torch.int32) == 0).all().item())
+        ntickets = -(-len(self.lens) * cfg.num_q_heads * 4 // 256) * 64  # at the workspace's end
+        tickets_zero = bool((workspace[workspace.numel() - ntickets:].view(torch.int32) == 0).all().item())
         self.last_tickets_zero = tickets_zero
         return out.cpu().numpy().astype(np.float64), info
 

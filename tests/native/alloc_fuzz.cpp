@@ -189,17 +189,22 @@ static void fuzz_plans(std::mt19937& rng) {
     cl[i] = ql[i] + int32_t(rng() % 2000);
   }
   const int32_t hkv = 1 + int32_t(rng() % 4), hq = hkv * (1 + int32_t(rng() % 20));
+  const int32_t max_keys = rng() % 2 ? 0 : 32 * (1 + int32_t(rng() % 40));
   int32_t need = 0;
-  CHECK(pkv_prefill_plan_ints(ql.data(), b, hq, hkv, &need) == PKV_OK);
+  CHECK(pkv_prefill_plan_ints(ql.data(), cl.data(), b, hq, hkv, max_keys, &need) == PKV_OK);
   std::vector<int32_t> plan(need);
   pkv_prefill_plan_info info{};
-  CHECK(pkv_prefill_plan(ql.data(), cl.data(), b, hq, hkv, plan.data(), need, &info) == PKV_OK);
+  CHECK(pkv_prefill_plan(ql.data(), cl.data(), b, hq, hkv, max_keys, plan.data(), need, &info) == PKV_OK);
   CHECK(info.plan_ints == need);
   for (int32_t w = 0; w < info.n_work; ++w) {
-    CHECK(plan[2 * w] >= 0 && plan[2 * w] < b);
-    CHECK(plan[2 * w + 1] >= 0 && plan[2 * w + 1] * info.tile_tokens < ql[plan[2 * w]]);
+    const int32_t* e = plan.data() + 6 * w;
+    CHECK(e[0] >= 0 && e[0] < b);
+    CHECK(e[1] >= 0 && e[1] * info.tile_tokens < ql[e[0]]);
+    CHECK(0 <= e[2] && e[2] < e[3]);
+    CHECK(e[4] < info.n_split && e[5] >= 0);
   }
-  CHECK(pkv_prefill_plan(ql.data(), cl.data(), b, hq, hkv, plan.data(), need - 1, &info) == PKV_E_BAD_ARG);
+  CHECK(pkv_prefill_plan(ql.data(), cl.data(), b, hq, hkv, max_keys, plan.data(), need - 1, &info) ==
+        PKV_E_BAD_ARG);
   pkv_utilisation_t u{};
   CHECK(pkv_utilisation(ql.data(), b, 300, 16, &u) == PKV_OK);
   CHECK(u.paged_waste_tokens >= 0 && u.paged_waste_tokens < 16 * b);

@@ -201,3 +201,37 @@ def test_write_kv_skips_negative_and_out_of_pool_slots():
         assert np.array_equal(device_bits(case.v_cache), host_bits(case.oracle.mirror.v))
     finally:
         case.close()
+
+
+def test_workspace_shared_by_launches_of_different_shapes():
+    """One workspace sized by pkv_decode_workspace_bound serves, in turn, a
+    batch of 2 long sequences (many split-K records) and a batch of 40
+    shorter ones (more completion tickets), twice: records grow from the
+    workspace's start and tickets sit at its end, so neither launch sees the
+    other's leftovers."""
+    from paged_kv_cache_257_amd import decode_workspace_bound
+    base = dataclasses.replace(CONFIGS[1], name="shared_ws", index=60, dtype="bf16", num_kv_heads=8,
+                               num_q_heads=32)
+    long_lens = [3000, 2500]
+    short_lens = [int(x) for x in np.random.default_rng(60).integers(100, 2500, size=40)]
+    cases = []
+    for lens in (long_lens, short_lens):
+        cfg = dataclasses.replace(base, num_seqs=len(lens))
+        nb = sum(-(-L // 16) for L in lens) + 3
+        cases.append(DecodeCase(cfg, lens=lens, num_blocks=nb,
+                                free_order=np.random.default_rng(len(lens)).permutation(nb)))
+        cases[-1].write_context()
+    try:
+        ws_bytes = decode_workspace_bound(40, 3000, 32, 128, 512)
+        workspace = torch.zeros(ws_bytes // 4, dtype=torch.float32, device="cuda")
+        for rnd in range(2):
+            for case in cases:
+                got, info = case.decode(512, workspace=workspace)
+                assert info.n_partials > 0
+                err = max(float(np.max(np.abs(got[i] - case.oracle_out(i)))) for i in range(len(case.lens)))
+                print(f"[gpu] shared workspace round {rnd} batch {len(case.lens)}: max_err={err:.3e}", flush=True)
+                assert err <= TOL["bf16"], err
+                assert case.last_tickets_zero
+    finally:
+        for case in cases:
+            case.close()

@@ -8,8 +8,10 @@ workloads compare every output; the 30,000-token prompt and the 16-prompt
 GQA batch run at their full size and compare a seeded sample of rows of
 every step (first, last and random tokens of each chunk), which the oracle
 computes one query at a time.  Tolerance: 2e-3 max-abs for 16-bit inputs.
-Also: NaN-filled pools (stale slots must not leak), a sweep of cached
-lengths / chunk lengths / head groupings, and the unsupported dtype.
+Also: tiles split into parts of at most 32 / 64 / 4096 keys (merged in
+the same launch; the completion tickets must be back at zero), NaN-filled
+pools (stale slots must not leak), a sweep of cached lengths / chunk
+lengths / head groupings, and the unsupported dtype.
 """
 
 import dataclasses
@@ -19,7 +21,7 @@ import pytest
 import torch
 
 from oracle.runs import PrefillRun
-from paged_kv_cache_257_amd import PkvError, Pool, prefill_plan
+from paged_kv_cache_257_amd import PkvError, Pool, prefill_plan, prefill_workspace_bytes
 from tests.gpu_helpers import TOL, TORCH_DTYPE, sync, to_device
 from workloads.prefill import (PrefillConfig, draw_prefill_shapes, draw_prefill_values,
                                prefill_config_by_name, prompt_offsets)
@@ -31,8 +33,10 @@ pytestmark = [pytest.mark.gpu,
 class PrefillCase:
     """A prefill schedule on the HIP path and on the oracle, step by step."""
 
-    def __init__(self, cfg, shapes=None, fill=0.0, values=None):
+    def __init__(self, cfg, shapes=None, fill=0.0, values=None, max_keys=0):
         self.cfg = cfg
+        self.max_keys = max_keys
+        self.workspace = None
         self.sh = shapes or draw_prefill_shapes(cfg)
         self.vals = values or draw_prefill_values(cfg, self.sh.prompts)
         self.width = -(-int(self.sh.prompts.max()) // 16)
@@ -68,25 +72,31 @@ class PrefillCase:
         self.pool.write_kv(self.k_dev.index_select(0, rows), self.v_dev.index_select(0, rows), slot_t)
         tables, lens = self.pool.build_batch(seqs, self.width)
         q_lens = np.array([n for _, _, n, _ in items])
-        plan, info = prefill_plan(q_lens, lens, self.cfg.num_q_heads, self.cfg.num_kv_heads)
+        plan, info = prefill_plan(q_lens, lens, self.cfg.num_q_heads, self.cfg.num_kv_heads, self.max_keys)
+        ws = prefill_workspace_bytes(info, self.cfg.head_dim)
+        if ws and (self.workspace is None or self.workspace.numel() < ws):
+            # zeroed once per size: every launch leaves the tickets at zero
+            self.workspace = torch.zeros(ws, dtype=torch.uint8, device="cuda")
         out = torch.full((int(q_lens.sum()), self.cfg.num_q_heads, self.cfg.head_dim), float("nan"),
                          dtype=torch.float32, device="cuda")
         self.pool.paged_prefill(self.q_dev.index_select(0, rows), out, torch.from_numpy(tables).cuda(),
                                 torch.from_numpy(lens).cuda(), self.cfg.scale,
-                                torch.from_numpy(plan).cuda(), info)
+                                torch.from_numpy(plan).cuda(), info, self.workspace)
+        self.last_info = info
         return items, out
 
     def close(self):
         self.pool.close()
 
 
-def run_full(cfg, fill=0.0):
-    case = PrefillCase(cfg, fill=fill)
+def run_full(cfg, fill=0.0, max_keys=0):
+    case = PrefillCase(cfg, fill=fill, max_keys=max_keys)
     try:
-        worst = 0.0
+        worst, splits = 0.0, 0
         for k in range(len(case.sh.steps)):
             items, out = case.step()
             sync()
+            splits += case.last_info.n_split
             got = out.cpu().numpy().astype(np.float64)
             pos = 0
             for seq, t0, n, _ in items:
@@ -95,6 +105,10 @@ def run_full(cfg, fill=0.0):
                 worst = max(worst, err)
                 assert err <= TOL[cfg.dtype], (cfg.name, k, seq, t0, n, err)
                 pos += n
+        if max_keys > 0:
+            assert splits > 0
+            if case.workspace is not None:  # tickets (at the end) back at zero
+                assert int(case.workspace[-256:].view(torch.int32).abs().sum()) == 0
         return worst
     finally:
         case.close()
@@ -107,6 +121,15 @@ def test_tiny_workloads_every_output(name):
     print(f"\n[gpu] prefill {name}: max_err={worst:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("name,max_keys", [("pf_tiny_f16", 32), ("pf_tiny_f16", 64),
+                                           ("pf_tiny_gqa_bf16", 32)])
+def test_tiny_workloads_split_keys(name, max_keys):
+    """Tiles split into parts of at most max_keys keys, merged in-launch."""
+    cfg = prefill_config_by_name(name)
+    worst = run_full(cfg, max_keys=max_keys)
+    print(f"\n[gpu] prefill {name} max_keys={max_keys}: max_err={worst:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("name", ["pf_tiny_f16", "pf_tiny_gqa_bf16"])
 def test_nan_filled_pool(name):
     cfg = prefill_config_by_name(name)
@@ -114,15 +137,16 @@ def test_nan_filled_pool(name):
     print(f"\n[gpu] prefill {name} NaN pool: max_err={worst:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["pf_batch_bf16", "pf_long_f16"])
-def test_full_size_sampled_rows(name):
+@pytest.mark.parametrize("name,max_keys", [("pf_batch_bf16", 0), ("pf_long_f16", 0),
+                                           ("pf_long_f16", 4096), ("pf_slice_f16", -1)])
+def test_full_size_sampled_rows(name, max_keys):
     cfg = prefill_config_by_name(name)
-    case = PrefillCase(cfg)
+    case = PrefillCase(cfg, max_keys=max_keys)
     rng = np.random.default_rng(cfg.seed + 5)
     try:
         worst = 0.0
         for k in range(len(case.sh.steps)):
-            print(f"[gpu] prefill {name} step {k}", flush=True)
+            print(f"[gpu] prefill {name} max_keys={max_keys} step {k}", flush=True)
             items, out = case.step()
             sync()
             pos = 0
@@ -130,15 +154,16 @@ def test_full_size_sampled_rows(name):
                 if len(items) > 4 and idx % 4 != k % 4:  # a quarter of the sequences per step
                     pos += n
                     continue
-                rows = sorted({0, n - 1, *rng.integers(0, n, size=3).tolist()})
+                extra = 1 if len(case.sh.steps) > 50 else 3
+                rows = sorted({0, n - 1, *rng.integers(0, n, size=extra).tolist()})
                 got = out[pos:pos + n].cpu().numpy().astype(np.float64)[rows]
                 ref = case.ora.attend(seq, t0, n, rows=rows)
                 err = float(np.max(np.abs(got - ref)))
                 worst = max(worst, err)
                 assert err <= TOL[cfg.dtype], (name, k, seq, t0, n, err)
                 pos += n
-        print(f"[gpu] prefill {name}: {len(case.sh.steps)} steps, sampled max_err={worst:.3e}",
-              flush=True)
+        print(f"[gpu] prefill {name} max_keys={max_keys}: {len(case.sh.steps)} steps, "
+              f"sampled max_err={worst:.3e}", flush=True)
     finally:
         case.close()
 
@@ -160,6 +185,7 @@ def test_shape_sweep(dt, Hq, Hkv, d, prompts, chunk):
     cfg = PrefillConfig(name="sweep", index=20, dtype=dt, num_q_heads=Hq, num_kv_heads=Hkv,
                         head_dim=d, chunk_tokens=chunk, fixed_prompts=tuple(prompts))
     worst = run_full(cfg)
+    worst = max(worst, run_full(cfg, max_keys=64) if max(prompts) > 64 else 0.0)
     print(f"\n[gpu] prefill sweep {dt} {Hq}/{Hkv} d={d} {prompts} chunk={chunk}: max_err={worst:.3e}",
           flush=True)
 

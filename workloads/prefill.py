@@ -14,7 +14,11 @@ gives no other size.  The workloads below are readings of that sentence:
     (32 x 128, fp16);
   * ``pf_batch_bf16``: sixteen prompts of U[512, 4096] tokens prefilled
     together in 1024-token slices, with the long-context workload's
-    grouped-query heads (32 query / 8 KV, bf16).
+    grouped-query heads (32 query / 8 KV, bf16);
+  * ``pf_slice_f16``: the same 30,000-token newcomer in 256-token slices,
+    the thin slices a scheduler takes when it guards the decoding
+    sequences' next token (each launch is then a few tiles deep in a long
+    context).
 
 Schedule: step k takes, from every prompt that still has tokens left, its
 next ``min(chunk, remaining)`` tokens; the first chunk allocates the
@@ -78,6 +82,9 @@ PREFILL_CONFIGS = (
     PrefillConfig(name="pf_batch_bf16", index=13, dtype="bf16", num_q_heads=32, num_kv_heads=8,
                   head_dim=128, chunk_tokens=1024, num_seqs=16, prompt_lo=512, prompt_hi=4096,
                   description="16 prompts of U[512, 4096] tokens in 1024-token slices, GQA 32/8"),
+    PrefillConfig(name="pf_slice_f16", index=14, dtype="f16", num_q_heads=32, num_kv_heads=32,
+                  head_dim=128, chunk_tokens=256, fixed_prompts=(30000,),
+                  description="one 30,000-token prompt in 256-token slices"),
 )
 
 
