@@ -369,13 +369,13 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
       __syncthreads();
     }
   } else {
-    if (s_begin < s_end) {
-      load_stage(s_begin);
-      store_stage(0, s_begin);
-      __syncthreads();
-    }
+    // a part: stages [s_begin, s_end) (never empty; the buffer parity is
+    // the stage's own, so the loop has the same form as above)
+    load_stage(s_begin);
+    store_stage(s_begin & 1, s_begin);
+    __syncthreads();
     for (int st = s_begin; st < s_end; ++st) {
-      const int buf = (st - s_begin) & 1;
+      const int buf = st & 1;
       const bool more = st + 1 < s_end;
       if (more) load_stage(st + 1);
       if (st < wave_stages) compute(buf, st);
