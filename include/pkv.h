@@ -145,6 +145,13 @@ pkv_status pkv_seq_length(const pkv_pool* pool, int32_t seq, int32_t* length);
 /* Copy the sequence's block table to table[0..cap); *n = its length. */
 pkv_status pkv_seq_table(const pkv_pool* pool, int32_t seq, int32_t* table, int32_t cap,
                          int32_t* n);
+/* Slots of positions [first, first + n) of the sequence, slots[i] =
+ * table[p / block_size] * block_size + p % block_size for p = first + i: the
+ * gather list through which the paged cache is read ([preview] "La idea de
+ * PagedAttention", step 5).  Fails (nothing written) unless
+ * 0 <= first, 0 <= n and first + n <= the sequence's length. */
+pkv_status pkv_seq_slots(const pkv_pool* pool, int32_t seq, int32_t first, int32_t n,
+                         int64_t* slots);
 /* Live sequence ids in ascending order. */
 pkv_status pkv_live_seqs(const pkv_pool* pool, int32_t* ids, int32_t cap, int32_t* n);
 /* Free blocks in the order they will be handed out next. */
@@ -577,6 +584,18 @@ pkv_status pkv_copy_blocks(const pkv_pool* pool, const int32_t* pairs, int32_t n
  * the pool.  Bit-exact copy. */
 pkv_status pkv_write_kv(const pkv_pool* pool, const void* k_new, const void* v_new,
                         const int64_t* slot_mapping, int32_t n_tokens, void* stream);
+
+/* Read tokens' K and V rows back out of the pool into dense arrays: the
+ * "read" of the cache surface (append, read, reset) that the paged cache
+ * keeps from the dense one ([preview] "Lo que la Fase 22 construye hacia la
+ * Fase 27", first item).  k_out, v_out: device [n_tokens][num_kv_heads]
+ * [head_dim] of the pool dtype, 16-byte aligned, written by the call;
+ * slot_mapping: device int64 [n_tokens] (pkv_seq_slots gives a sequence's).
+ * The inverse of pkv_write_kv: row t of k_out / v_out is the pool's row at
+ * slot_mapping[t], bit for bit; a negative slot, or one outside the pool,
+ * gives a row of zeros. */
+pkv_status pkv_read_kv(const pkv_pool* pool, const int64_t* slot_mapping, int32_t n_tokens,
+                       void* k_out, void* v_out, void* stream);
 
 /* PagedAttention decode ([lesson] paragraph 5, [preview] step 5): for every
  * sequence i and query head h,

@@ -3,7 +3,8 @@
 The product is the C-ABI library ``lib/libpkv.so`` (include/pkv.h): a C++
 block allocator and HIP kernels for gfx950.  This package is its thin Python
 binding: ``Pool`` mirrors the pkv_* calls, ``DecodeIteration`` strings them
-into one decode iteration.  Importing it does not load the library; the
+into one decode iteration, ``PagedKVCache`` and ``attention`` give one
+sequence the dense cache's append / read / reset surface.  Importing it does not load the library; the
 first call does, and raises if it is not built (there is no fallback).
 """
 
@@ -13,11 +14,14 @@ from .pool import (Pool, decode_plan, decode_workspace_bound, decode_workspace_b
 
 __all__ = ["Pool", "PkvError", "decode_plan", "decode_workspace_bound", "decode_workspace_bytes",
            "default_partition_tokens", "prefill_plan", "prefill_workspace_bytes", "load",
-           "DecodeIteration"]
+           "DecodeIteration", "PagedKVCache", "attention"]
 
 
 def __getattr__(name):
     if name == "DecodeIteration":
         from .step import DecodeIteration
         return DecodeIteration
+    if name in ("PagedKVCache", "attention"):
+        from . import cache
+        return getattr(cache, name)
     raise AttributeError(name)

@@ -141,6 +141,7 @@ SIGNATURES = {
     "pkv_seq_free": [P, I32],
     "pkv_seq_length": [P, I32, PI32],
     "pkv_seq_table": [P, I32, PI32, I32, PI32],
+    "pkv_seq_slots": [P, I32, I32, I32, PI64],
     "pkv_live_seqs": [P, PI32, I32, PI32],
     "pkv_free_list": [P, PI32, I32, PI32],
     "pkv_refcounts": [P, PI32],
@@ -175,6 +176,7 @@ SIGNATURES = {
                          PI32],
     "pkv_copy_blocks": [P, P, I32, P],
     "pkv_write_kv": [P, P, P, P, I32, P],
+    "pkv_read_kv": [P, P, I32, P, P, P],
     "pkv_paged_decode": DECODE_ARGS,
     "pkv_paged_decode_partitions": DECODE_ARGS,
     "pkv_paged_decode_reduce": DECODE_ARGS,
@@ -186,7 +188,7 @@ RESTYPES = {"pkv_last_error": C.c_char_p, "pkv_decode_workspace_bytes": C.c_size
             "pkv_decode_workspace_bound": C.c_size_t, "pkv_default_partition_tokens": C.c_int32,
             "pkv_prefill_workspace_bytes": C.c_size_t,
             "pkv_prepare_decode_bytes": C.c_size_t, "pkv_stepper_slot_bytes": C.c_size_t}
-DEVICE_FUNCS = ("pkv_copy_blocks", "pkv_write_kv", "pkv_paged_decode", "pkv_paged_decode_partitions",
+DEVICE_FUNCS = ("pkv_copy_blocks", "pkv_write_kv", "pkv_read_kv", "pkv_paged_decode", "pkv_paged_decode_partitions",
                 "pkv_paged_decode_reduce", "pkv_paged_prefill", "pkv_hybrid_copy_states",
                 "pkv_stepper_slot_bytes", "pkv_stepper_create",
                 "pkv_stepper_destroy", "pkv_stepper_step")

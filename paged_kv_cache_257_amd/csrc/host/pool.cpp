@@ -350,6 +350,21 @@ pkv_status pkv_seq_table(const pkv_pool* p, int32_t seq, int32_t* table, int32_t
   return PKV_OK;
 }
 
+pkv_status pkv_seq_slots(const pkv_pool* p, int32_t seq, int32_t first, int32_t n, int64_t* slots) {
+  if (pkv_status st = check_pool(p)) return st;
+  const pkv_seq_state* s = find_seq(p, seq);
+  if (!s) return fail(PKV_E_BAD_SEQ, unknown(seq));
+  if (first < 0 || n < 0 || int64_t(first) + n > s->length)
+    return fail(PKV_E_BAD_ARG, "positions outside the sequence");
+  if (n > 0 && !slots) return fail(PKV_E_BAD_ARG, "null slots");
+  const int32_t bs = p->desc.block_size;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t pos = first + i;
+    slots[i] = int64_t(s->table[size_t(pos / bs)]) * bs + pos % bs;
+  }
+  return PKV_OK;
+}
+
 pkv_status pkv_live_seqs(const pkv_pool* p, int32_t* ids, int32_t cap, int32_t* n) {
   if (pkv_status st = check_pool(p)) return st;
   if (!n || cap < 0 || (cap > 0 && !ids)) return fail(PKV_E_BAD_ARG, "bad id buffer");

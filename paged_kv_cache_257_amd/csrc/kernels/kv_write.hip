@@ -1,5 +1,5 @@
-// write_kv and copy_blocks: the device half of appending tokens to a paged
-// KV cache.
+// write_kv, read_kv and copy_blocks: the device half of appending tokens
+// to a paged KV cache and of reading them back.
 //
 // write_kv stores each new token's K and V rows at the slot the allocator
 // handed out ("04 — Hacia PagedAttention", La idea de PagedAttention, step 3:
@@ -42,6 +42,36 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const char* __restrict__ 
   const int64_t dst = ((blk * heads + h) * kBlockTokens + row) * row_bytes + c * 16;
   *reinterpret_cast<u32x4*>(k_cache + dst) = *reinterpret_cast<const u32x4*>(k_new + src);
   *reinterpret_cast<u32x4*>(v_cache + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
+}
+
+// The inverse of write_kv: row t of the dense output is the pool row at
+// slot t (zeros for a slot outside the pool).  Same thread-to-chunk map.
+__global__ __launch_bounds__(256) void read_kv_kernel(const int64_t* __restrict__ slots,
+                                                      const char* __restrict__ k_cache,
+                                                      const char* __restrict__ v_cache,
+                                                      char* __restrict__ k_out,
+                                                      char* __restrict__ v_out, int64_t n_chunks,
+                                                      int32_t heads, int32_t chunks_per_row,
+                                                      int64_t num_slots) {
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= n_chunks) return;
+  const int64_t per_token = int64_t(heads) * chunks_per_row;
+  const int64_t t = idx / per_token;
+  const int64_t rem = idx - t * per_token;
+  const int64_t slot = slots[t];
+  const int64_t dst = idx * 16;
+  if (slot < 0 || slot >= num_slots) {
+    *reinterpret_cast<u32x4*>(k_out + dst) = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(v_out + dst) = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const int64_t h = rem / chunks_per_row;
+  const int64_t c = rem - h * chunks_per_row;
+  const int64_t blk = slot / kBlockTokens;
+  const int64_t row = slot - blk * kBlockTokens;
+  const int64_t src = ((blk * heads + h) * kBlockTokens + row) * (int64_t(chunks_per_row) * 16) + c * 16;
+  *reinterpret_cast<u32x4*>(k_out + dst) = *reinterpret_cast<const u32x4*>(k_cache + src);
+  *reinterpret_cast<u32x4*>(v_out + dst) = *reinterpret_cast<const u32x4*>(v_cache + src);
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(const int32_t* __restrict__ pairs,
@@ -116,6 +146,27 @@ extern "C" pkv_status pkv_write_kv(const pkv_pool* pool, const void* k_new, cons
                      static_cast<char*>(pool->k_cache), static_cast<char*>(pool->v_cache), n_chunks,
                      d.num_kv_heads, cpr, int64_t(d.num_blocks) * kBlockTokens);
   return launch_status("write_kv launch");
+}
+
+extern "C" pkv_status pkv_read_kv(const pkv_pool* pool, const int64_t* slot_mapping,
+                                  int32_t n_tokens, void* k_out, void* v_out, void* stream) {
+  if (pkv_status st = check_device_pool(pool)) return st;
+  if (n_tokens < 0) return fail(PKV_E_BAD_ARG, "negative n_tokens");
+  if (n_tokens == 0) return PKV_OK;
+  if (!k_out || !v_out || !slot_mapping) return fail(PKV_E_BAD_ARG, "null k_out, v_out or slot_mapping");
+  if ((reinterpret_cast<uintptr_t>(k_out) | reinterpret_cast<uintptr_t>(v_out)) & 15)
+    return fail(PKV_E_BAD_ARG, "k_out and v_out must be 16-byte aligned");
+  const pkv_pool_desc& d = pool->desc;
+  const int32_t cpr = int32_t(int64_t(d.head_dim) * dtype_bytes(d.dtype) / 16);
+  const int64_t n_chunks = int64_t(n_tokens) * d.num_kv_heads * cpr;
+  const int64_t grid = (n_chunks + 255) / 256;
+  if (grid > INT32_MAX) return fail(PKV_E_BAD_ARG, "read too large for one launch");
+  hipLaunchKernelGGL(read_kv_kernel, dim3(uint32_t(grid)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), slot_mapping,
+                     static_cast<const char*>(pool->k_cache), static_cast<const char*>(pool->v_cache),
+                     static_cast<char*>(k_out), static_cast<char*>(v_out), n_chunks, d.num_kv_heads,
+                     cpr, int64_t(d.num_blocks) * kBlockTokens);
+  return launch_status("read_kv launch");
 }
 
 extern "C" pkv_status pkv_copy_blocks(const pkv_pool* pool, const int32_t* pairs, int32_t n_pairs,

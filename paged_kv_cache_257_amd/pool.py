@@ -109,6 +109,14 @@ class Pool:
         check(self.lib, self.lib.pkv_seq_table(self.handle, seq, i32p(buf), cap, C.byref(n)))
         return buf[:n.value].tolist()
 
+    def slots(self, seq: int, first: int = 0, n: Optional[int] = None) -> np.ndarray:
+        """int64 slots of positions [first, first + n) (n defaults to the rest)."""
+        if n is None:
+            n = self.length(seq) - first
+        buf = np.empty(max(n, 1), dtype=np.int64)
+        check(self.lib, self.lib.pkv_seq_slots(self.handle, seq, first, n, i64p(buf)))
+        return buf[:n]
+
     def live(self) -> List[int]:
         n = C.c_int32()
         self.lib.pkv_live_seqs(self.handle, None, 0, C.byref(n))
@@ -156,6 +164,12 @@ class Pool:
         n = int(slot_mapping.shape[0])
         check(self.lib, self.lib.pkv_write_kv(self.handle, _dptr(k_new), _dptr(v_new),
                                               _dptr(slot_mapping), n, _stream_ptr(stream)))
+
+    def read_kv(self, slot_mapping, k_out, v_out, stream=None) -> None:
+        """k_out, v_out: device [T][H_kv][d] filled from the pool rows at slot_mapping (int64 [T])."""
+        n = int(slot_mapping.shape[0])
+        check(self.lib, self.lib.pkv_read_kv(self.handle, _dptr(slot_mapping), n, _dptr(k_out),
+                                             _dptr(v_out), _stream_ptr(stream)))
 
     def copy_blocks(self, pairs, stream=None) -> None:
         """pairs: device int32 [n][2] (src, dst)."""

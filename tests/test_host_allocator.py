@@ -237,3 +237,56 @@ def test_prepare_decode_matches_separate_calls():
                                 buf.ctypes.data, 64, C.byref(lay))
     assert st == _capi.E_BAD_ARG
     assert (a.live(), a.free_list(), a.refcounts()) == before
+
+
+def test_seq_slots_read_back_each_sequences_dense_history():
+    """pkv_seq_slots against the dense shadow: every token gets a unique id
+    written at the slot the append handed out (copy-on-write pairs copied
+    first, as the device does); reading the cells at a sequence's slots must
+    give its history in position order, forks included."""
+    rng = np.random.default_rng(31)
+    nb, bs = 48, 16
+    pool = host_pool(nb, bs, 12, rng.permutation(nb).astype(np.int32))
+    cells = np.full(nb * bs, -1, np.int64)
+    shadow, tok = {}, 0
+    for _ in range(400):
+        live = pool.live()
+        op = str(rng.choice(["alloc", "append", "fork", "free"], p=[.2, .5, .15, .15]))
+        try:
+            if op == "alloc" or not live:
+                seq, slots = pool.alloc(int(rng.integers(0, 40)))
+                shadow[seq] = []
+            elif op == "append":
+                seq = int(rng.choice(live))
+                slots = pool.append(seq, int(rng.integers(1, 20)))
+            elif op == "fork":
+                p = int(rng.choice(live))
+                shadow[pool.fork(p)] = list(shadow[p])
+                continue
+            else:
+                s = int(rng.choice(live))
+                pool.free(s)
+                del shadow[s]
+                continue
+        except PkvError:
+            continue
+        for a, b in pool.take_cow().tolist():
+            cells[b * bs:(b + 1) * bs] = cells[a * bs:(a + 1) * bs]
+        ids = np.arange(tok, tok + len(slots))
+        tok += len(slots)
+        cells[slots] = ids
+        shadow[seq].extend(ids.tolist())
+        for s in pool.live():
+            assert cells[pool.slots(s)].tolist() == shadow[s], s
+    s = max(pool.live(), key=pool.length)
+    L = pool.length(s)
+    full = pool.slots(s)
+    assert L > 20 and pool.slots(s, 7, 9).tolist() == full[7:16].tolist()
+    assert len(pool.slots(s, L, 0)) == 0
+    for first, n in ((L - 3, 4), (-1, 2), (0, -1)):
+        with pytest.raises(PkvError) as e:
+            pool.slots(s, first, n)
+        assert e.value.kind == "bad_arg"
+    with pytest.raises(PkvError) as e:
+        pool.slots(10_000, 0, 0)
+    assert e.value.kind == "bad_seq"
