@@ -34,6 +34,7 @@ import math
 import os
 import sys
 import time
+from typing import Optional
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -47,17 +48,30 @@ COUNTER_SUMMARY = "profiles/paged_decode_gpt_f16_counters.txt"
 
 
 def kernel_source_sha() -> str:
+    return _sources_sha(KERNEL_SOURCES)
+
+
+PREFILL_SOURCES = ("paged_kv_cache_257_amd/csrc/kernels/paged_prefill.hip",
+                   "paged_kv_cache_257_amd/csrc/kernels/device_common.h")
+
+
+def _sources_sha(paths) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic():
-    """Per-launch HBM bytes from the committed counter summary, if it was
-    taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, COUNTER_SUMMARY)
+def prefill_source_sha() -> str:
+    return _sources_sha(PREFILL_SOURCES)
+
+
+def committed_traffic(summary: str = COUNTER_SUMMARY, sha: Optional[str] = None,
+                      key: str = "hbm_bytes_per_launch"):
+    """HBM bytes from a committed counter summary, if it was taken on the
+    current kernel source (else None)."""
+    path = os.path.join(ROOT, summary)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -66,10 +80,10 @@ def committed_traffic():
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha") != kernel_source_sha():
+    if kv.get("kernel_source_sha") != (sha or kernel_source_sha()):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
@@ -441,7 +455,10 @@ def bench_prefill(args, cfg):
         "roofline": {"bound": "mfma", "achieved": round(total_flops / kern_total_s / 1e12, 2),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(total_flops / kern_total_s / 1e12 / MFMA_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "paged_prefill_kernel",
+                     "traffic": committed_traffic(f"profiles/paged_prefill_{cfg.name}_counters.txt",
+                                                  prefill_source_sha(), "hbm_bytes_per_step")
+                     if max_keys == PREFILL_MAX_KEYS else None,
+                     "traffic_unit": "HBM bytes per step", "kernel": "paged_prefill_kernel",
                      "kernel_ms_per_step": round(float(per_launch_ms.sum()), 4),
                      "largest_launch": {"flops": flops[k_big], "ms": round(float(per_launch_ms[k_big]), 4),
                                         "TFLOPs": round(flops[k_big] / per_launch_ms[k_big] / 1e9, 1)},

@@ -95,6 +95,19 @@ __device__ __forceinline__ f4 mfma32<PKV_BF16>(const u32x4& a, const u32x4& b, c
                                                  c, 0, 0, 0);
 }
 
+// 16-byte store / load at device scope: cache policy sc1, the coherence
+// level the compiler gives relaxed agent-scope atomics (which it emits as
+// 4-byte sc1 accesses), so records written this way are read by a
+// workgroup on any XCD with no cache maintenance, in a quarter of the
+// transactions.
+constexpr int kCachePolicyDevice = 16;  // sc1
+__device__ __forceinline__ void store_device(__amdgpu_buffer_rsrc_t r, int offset, const f4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, offset, 0, kCachePolicyDevice);
+}
+__device__ __forceinline__ f4 load_device(__amdgpu_buffer_rsrc_t r, int offset) {
+  return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, kCachePolicyDevice));
+}
+
 // Round an fp32 value to the 16-bit type (nearest even): returns the bits
 // and, in *back, the rounded value as fp32.
 template <int DT>
@@ -406,7 +419,8 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
 
   if constexpr (SPLIT) {
   // A part of a split tile: its (o, m, l) per row go to a record through
-  // device-scope atomic stores (visible to any XCD without cache flushes);
+  // device-scope stores (visible to any XCD without cache flushes: o in
+  // 16-byte sc1 stores, m and l as relaxed agent-scope atomics);
   // the part that takes the last ticket merges all parts:
   //   M = max m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
   if (split >= p.n_split) return;
@@ -418,14 +432,24 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
     const int row = wave * 16 * RG + 16 * j + n;
     return p.part + ((int64_t(base + prt) * hgroups_total + hg) * kPrefillTileRows + row) * p.rec_floats;
   };
+  // the records of part prt of this (tile, head group): 128 rows, as a
+  // buffer resource for the 16-byte device-scope accesses of o
+  const int rec_bytes = p.rec_floats * 4;
+  auto records = [&](int prt) -> __amdgpu_buffer_rsrc_t {
+    return make_rsrc(p.part + (int64_t(base + prt) * hgroups_total + hg) * kPrefillTileRows * p.rec_floats,
+                     kPrefillTileRows * rec_bytes);
+  };
+  const int row_off = (wave * 16 * RG + n) * rec_bytes + 16 * g;  // + 16 j rows + 64 dt
+  {
+    const __amdgpu_buffer_rsrc_t rs = records(item[5]);
+#pragma unroll
+    for (int j = 0; j < RG; ++j)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) store_device(rs, row_off + 16 * j * rec_bytes + 64 * dt, o[j][dt]);
+  }
 #pragma unroll
   for (int j = 0; j < RG; ++j) {
     float* rec = record(item[5], j);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        __hip_atomic_store(rec + dt * 16 + 4 * g + v, o[j][dt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (g == 0) {
       __hip_atomic_store(rec + D, m[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(rec + D + 1, lt[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -453,13 +477,10 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
       const float w = __builtin_amdgcn_exp2f(
           __hip_atomic_load(rec + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
       den = __builtin_fmaf(w, __hip_atomic_load(rec + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), den);
+      const __amdgpu_buffer_rsrc_t rs = records(prt);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          acc[dt][v] = __builtin_fmaf(
-              w, __hip_atomic_load(rec + dt * 16 + 4 * g + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-              acc[dt][v]);
+        acc[dt] += w * load_device(rs, row_off + 16 * j * rec_bytes + 64 * dt);
     }
     if (row_ok[j]) {
       const float inv = 1.f / den;
