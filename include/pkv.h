@@ -22,7 +22,8 @@
  *
  * Conventions
  *   - Every function returns a pkv_status.  On any error nothing changes
- *     (admission is refused early with a clear error, [lesson] paragraph 8);
+ *     (a request that does not fit is turned away when admitted, with a
+ *     status, instead of failing later: [lesson] paragraph 8);
  *     pkv_last_error() gives a message for the calling thread.
  *   - The caller owns all device memory: the K/V pools, q, out, tables,
  *     context lengths, plans and workspaces.  The library never allocates
@@ -181,8 +182,8 @@ pkv_status pkv_build_batch(const pkv_pool* pool, const int32_t* seqs, int32_t n_
  * batching", 01 · Conceito: composition revisited at every iteration
  * boundary, finished sequences leave, waiting ones enter, running ones
  * advance one token; the scheduler weighs free blocks, tokens per batch and
- * the prefill/decode mix, slicing long prefills; admission reasons in
- * blocks and refuses early; paragraph 9 names the metrics kept here).
+ * the prefill/decode mix, slicing long prefills; admission is decided in
+ * blocks; paragraph 9 names the metrics kept here).
  * The pages give the goals, not the rules; the rules below are readings.
  *
  * Requests are known up front with an arrival iteration; the policy does
@@ -307,7 +308,7 @@ pkv_status pkv_sched_stats(const pkv_sched* s, pkv_sched_stats_t* out);
  * slot; a fork shares the parent's blocks (refcounts) but takes its own
  * slot and queues a (parent slot, child slot) copy, since the state changes
  * every step; free returns both.  Admission and fork are all-or-nothing
- * across the two pools and refuse early ([lesson] paragraph 8) with
+ * across the two pools and fail up front ([lesson] paragraph 8) with
  * PKV_E_NO_SLOTS or PKV_E_NO_BLOCKS.  The slot free list is a stack seeded
  * by slot_order (NULL = 0..num_slots-1; slot_order[0] is handed out first).
  * Sequences admitted here must be forked and freed here; appends go to the

@@ -11,7 +11,8 @@ and [lesson] paragraph 7: sequences may point at the same read-only blocks
 (forks, shared prefixes); when one of them diverges, copy-on-write gives the
 writer a new block for the altered positions, and reference counts decide
 when a shared block goes back to the pool.  [lesson] paragraph 8: admission
-is counted in blocks and refused early with a clear error.
+is decided in blocks, and a request that cannot fit is turned away at once
+with an explicit error.
 
 Readings (the pages leave these open):
   * free list = LIFO stack; its initial content is ``free_order`` and the

@@ -4,8 +4,8 @@
 revisited at every iteration boundary (finished sequences leave, waiting
 ones enter, running ones advance one token); the scheduler weighs free
 blocks, the tokens of a batch and the prefill/decode mix, slicing long
-prefills; admission reasons in blocks and refuses early rather than fail
-mid-generation (the scheduler paragraph); preemptions, prefix hits, queue
+prefills; admission is decided in blocks, so a request that cannot fit is
+turned away before it starts (the scheduler paragraph); preemptions, prefix hits, queue
 delay, time to first token and inter-token latency are among the metrics
 to keep (the metrics paragraph).  The rules are readings, in this order
 per iteration t:

@@ -6,7 +6,7 @@
 // free list) and "PagedAttention e continuous batching", 01 · Conceito,
 // paragraph 7 (shared read-only blocks, copy-on-write for the writer of a
 // diverging branch, reference counts deciding when a block returns to the
-// pool) and paragraph 8 (admission counted in blocks, refused early).
+// pool) and paragraph 8 (admission decided in blocks, failing up front).
 //
 // Policy choices the pages leave open, fixed so that tables are
 // reproducible bit for bit:
