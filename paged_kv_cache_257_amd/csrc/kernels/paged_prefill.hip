@@ -36,7 +36,8 @@
 // weights must become 16-bit MFMA operands: for fp16 they are rounded to
 // fp16 (11-bit significand); for bf16 they are split into a bf16 head and a
 // bf16 remainder (two MFMAs, ~16 bits), since bf16 weights alone put the
-// error of short contexts above 2e-3.  The normaliser sums the fp32 weights.
+// error of short contexts above 2e-3.  Both round to nearest even, two
+// weights per conversion instruction.  The normaliser sums the fp32 weights.
 // The accumulators are rescaled only in stages where some row's running
 // maximum grew (a wave-wide vote); otherwise the factor is exactly 1.
 #include "device_common.h"
@@ -48,6 +49,9 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPfWaves = 4;
 constexpr int kPfRowGroups = kPrefillTileRows / (16 * kPfWaves);  // 16-row groups per wave
@@ -108,23 +112,18 @@ __device__ __forceinline__ f4 load_device(__amdgpu_buffer_rsrc_t r, int offset) 
   return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, kCachePolicyDevice));
 }
 
-// Round an fp32 value to the 16-bit type (nearest even): returns the bits
-// and, in *back, the rounded value as fp32.
-template <int DT>
-__device__ __forceinline__ uint32_t round16(float x, float* back);
-
-template <>
-__device__ __forceinline__ uint32_t round16<PKV_F16>(float x, float* back) {
-  const _Float16 h = static_cast<_Float16>(x);
-  *back = static_cast<float>(h);
-  return __builtin_bit_cast(uint16_t, h);
-}
-
-template <>
-__device__ __forceinline__ uint32_t round16<PKV_BF16>(float x, float* back) {
-  const __bf16 h = static_cast<__bf16>(x);
-  *back = static_cast<float>(h);
-  return __builtin_bit_cast(uint16_t, h);
+// Maximum over the four lanes n, n + 16, n + 32, n + 48 (one query row's
+// accumulator lanes), with gfx950's lane swaps instead of LDS permutes: a
+// swap of a register with itself leaves, in the two results, each lane's
+// own value and its partner's (16 lanes away for permlane16, 32 for
+// permlane32).
+__device__ __forceinline__ float max_over_columns(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  x = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
 }
 
 // Three waves per SIMD: the compiler then keeps the accumulators in the
@@ -322,8 +321,7 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
       float mx = s[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_over_columns(mx);
       const float mn = fmaxf(m[j], mx * c2);
       alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
       rescale |= mn > m[j];
@@ -335,11 +333,13 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
         const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q2], c2, -mn));
         const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q2 + 1], c2, -mn));
         psum += x0 + x1;
-        float r0, r1;
-        ph[q2] = round16<DT>(x0, &r0) | (round16<DT>(x1, &r1) << 16);
-        if constexpr (DT == PKV_BF16) {
-          float e0, e1;
-          plo[q2] = round16<DT>(x0 - r0, &e0) | (round16<DT>(x1 - r1, &e1) << 16);
+        const f2 xx = {x0, x1};
+        if constexpr (DT == PKV_F16) {
+          ph[q2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(xx, h2));
+        } else {
+          const b2 hi = __builtin_convertvector(xx, b2);
+          ph[q2] = __builtin_bit_cast(uint32_t, hi);
+          plo[q2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(xx - __builtin_convertvector(hi, f2), b2));
         }
       }
       lsum[j] = lsum[j] * alpha[j] + psum;
