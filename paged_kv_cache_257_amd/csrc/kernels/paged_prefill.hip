@@ -19,7 +19,8 @@
 //
 // Per stage.  All 256 threads stage the two K tiles into LDS as they are
 // (rows padded by 16 bytes against bank conflicts) and the two V tiles
-// transposed (V^T, d-major), while the previous stage is computed.  A wave
+// transposed (V^T, d-major, 4-token column blocks swizzled per row against
+// bank conflicts), while the previous stage is computed.  A wave
 // then forms S^T = K Q^T with v_mfma_f32_16x16x32_{f16,bf16}: K from LDS is
 // the A operand (lane = 16 g + n holds token n, d-chunk 8 g), Q^T from
 // registers the B operand (query row n, d-chunk 8 g), and the accumulator
@@ -153,6 +154,14 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
   static_assert(kBlockTokens % KTOK_PER_WAVE == 0 && kBlockTokens % VTOK_PER_WAVE == 0,
                 "a wave's staged rows lie in one block");
 
+  // V^T column of stage token tok in row r (a dim): 4-token column blocks
+  // XOR-swizzled by bits 5-6 of the row, so that the staging stores (a wave
+  // writes 16 rows 8 apart x 8 tokens) hit 64 distinct banks; 8-byte reads
+  // of 4 consecutive tokens stay contiguous, and for the rows one d-tile
+  // reads (r < 32 apart, same bits 5-6) the swizzle is a single constant.
+  auto vt_col = [](int r, int tok) __attribute__((always_inline)) {
+    return (((tok >> 2) ^ (2 * ((r >> 5) & 3))) << 2) | (tok & 3);
+  };
   __shared__ __attribute__((aligned(16))) uint16_t lk[2][kStage * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t lv[2][D * VROW];
 
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
       for (int e = 0; e < 8; ++e) {
         const uint32_t ea = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
         const uint32_t eb = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        *reinterpret_cast<uint32_t*>(&lv[buf][(ch * 8 + e) * VROW + tok]) = ea | (eb << 16);
+        *reinterpret_cast<uint32_t*>(&lv[buf][(ch * 8 + e) * VROW + vt_col(ch * 8 + e, tok)]) = ea | (eb << 16);
       }
     }
   };
@@ -356,8 +365,8 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const uint16_t* vrow = &lv[buf][(dt * 16 + n) * VROW];
-      const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + 4 * g);
-      const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + 16 + 4 * g);
+      const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + vt_col(dt * 16, 4 * g));
+      const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + vt_col(dt * 16, 16 + 4 * g));
       const u32x4 a = {a0.x, a0.y, a1.x, a1.y};
 #pragma unroll
       for (int j = 0; j < RG; ++j) {
