@@ -47,6 +47,20 @@ KERNEL_SOURCES = ("paged_kv_cache_257_amd/csrc/kernels/paged_decode.hip",
 COUNTER_SUMMARY = "profiles/paged_decode_gpt_f16_counters.txt"
 
 
+def counter_summary(workload: str) -> str:
+    """The committed HBM-counter summary of a decode workload."""
+    return f"profiles/paged_decode_{workload}_counters.txt"
+
+
+def decode_kernel_name(dtype: str, head_dim: int, group: int) -> str:
+    """The kernel that runs a decode launch: grouped-query fp16/bf16 batches
+    of head_dim 128 go to the matrix-core kernel unless PKV_DECODE_MFMA=0."""
+    if group >= 2 and head_dim == 128 and dtype in ("f16", "bf16") and \
+            os.environ.get("PKV_DECODE_MFMA", "1")[:1] != "0":
+        return "paged_decode_mfma_kernel"
+    return "paged_decode_kernel"
+
+
 def kernel_source_sha() -> str:
     return _sources_sha(KERNEL_SOURCES)
 
@@ -618,7 +632,7 @@ def main(argv=None):
     timed_ctx = float(np.mean([step_bytes[s] for s in timed])) / per_tok / B
     value = kbytes / wall / 1e9
     info = infos[-1]
-    traffic = committed_traffic()
+    traffic = committed_traffic(counter_summary(cfg.name))
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -649,8 +663,8 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "paged_decode_kernel" + (" (partition kernel of two launches)"
-                                                        if args.two_launch else ""),
+                     "kernel": decode_kernel_name(dt, d, Hq // H) + (" (partition kernel of two launches)"
+                                                                     if args.two_launch else ""),
                      "kernel_ms_mean": round(float(np.mean(kern_ms)), 5),
                      "kernel_ms_median": round(float(np.median(kern_ms)), 5),
                      "kernel_ms_p10": round(float(np.percentile(kern_ms, 10)), 5),

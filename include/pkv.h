@@ -626,7 +626,13 @@ pkv_status pkv_read_kv(const pkv_pool* pool, const int64_t* slot_mapping, int32_
  * One kernel launch: multi-partition sequences are combined by the last
  * workgroup of each sequence and head group to finish.
  * Arithmetic: fp32 accumulation and an online (running max) softmax; the
- * output is float32.  Table entries outside the pool read nothing. */
+ * output is float32.  Table entries outside the pool read nothing.
+ * Kernels: grouped-query batches (num_q_heads / num_kv_heads >= 2) of fp16 or
+ * bf16 with head_dim 128 run the two products on the matrix cores (the
+ * softmax weights enter them as fp16, or as a bf16 head plus a bf16
+ * remainder); every other shape runs on the vector ALUs.  The environment
+ * variable PKV_DECODE_MFMA=0, read at every call, selects the vector kernel
+ * for all shapes. */
 pkv_status pkv_paged_decode(const pkv_pool* pool, const void* q, const void* k_new,
                             const void* v_new, float* out, int32_t num_seqs, int32_t num_q_heads,
                             const int32_t* block_tables, int32_t table_stride,

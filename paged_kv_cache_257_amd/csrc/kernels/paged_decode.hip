@@ -50,6 +50,7 @@
 // treated as fully masked blocks (nothing is read through them).
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <cstdlib>
 
 #include "decode_launch.h"
@@ -84,6 +85,89 @@ struct DecodeParams {
   int32_t n_partials;
   float scale_log2;
 };
+
+// The end of a work item, shared by both decode kernels.  sm_m, sm_l
+// ([NSUB][GW]) and sm_o ([NSUB][GW][D]) hold the workgroup's NSUB partial
+// softmax states per query head (base-2 maxima in scaled units), written
+// before a barrier.  They are merged; a single-partition sequence writes
+// o / l, otherwise the partition's (o, m, l) becomes a record and the last
+// partition to finish combines all records of the (sequence, head group).
+template <int D, int GW, int NSUB, int NT>
+__device__ __forceinline__ void finish_item(const DecodeParams& p, const float* sm_m, const float* sm_l,
+                                            const float* sm_o, int seq, int part, int n_parts, int hg,
+                                            int hgroups, int qh0) {
+  const bool single = (n_parts <= 1);
+  const int pidx = single ? -1 : p.part_offset[seq] + part;
+  if (!single && (pidx < 0 || pidx >= p.n_partials)) return;
+  for (int idx = threadIdx.x; idx < GW * D; idx += NT) {
+    const int g = idx / D;
+    const int dd = idx - g * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) M = fmaxf(M, sm_m[s * GW + g]);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const float w = __builtin_amdgcn_exp2f(sm_m[s * GW + g] - M_use);
+      num = __builtin_fmaf(w, sm_o[(s * GW + g) * D + dd], num);
+      den = __builtin_fmaf(w, sm_l[s * GW + g], den);
+    }
+    const int qh = qh0 + g;
+    if (single) {
+      p.out[(int64_t(seq) * p.num_q_heads + qh) * D + dd] = num / den;
+    } else {
+      // partial record of (partition, query head): agent-scope stores, so
+      // the combining workgroup on any XCD reads them without cache flushes
+      float* rec = p.part + (int64_t(pidx) * p.num_q_heads + qh) * p.rec_floats;
+      __hip_atomic_store(rec + dd, num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (dd == 0) {
+        __hip_atomic_store(rec + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(rec + D + 1, den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if (single || p.counters == nullptr) return;
+
+  // Split-K combine in the same launch.  Each workgroup of a (sequence, head
+  // group) waits until its partial stores have completed, takes a ticket, and
+  // the one taking the last ticket combines every partition's record and
+  // resets the ticket for the next launch.  Records and tickets are only
+  // touched through agent-scope atomics and every record owns whole cache
+  // lines, so no cache writeback or invalidate is needed.
+  __shared__ int sm_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int32_t* ticket = p.counters + int64_t(seq) * hgroups + hg;
+  if (threadIdx.x == 0)
+    sm_last = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               n_parts - 1);
+  __syncthreads();
+  if (!sm_last) return;
+  const int base = p.part_offset[seq];
+  if (base < 0 || base + n_parts > p.n_partials) return;
+  for (int idx = threadIdx.x; idx < GW * D; idx += NT) {
+    const int g = idx / D;
+    const int dd = idx - g * D;
+    const int qh = qh0 + g;
+    const float* rec0 = p.part + (int64_t(base) * p.num_q_heads + qh) * p.rec_floats;
+    const int64_t step = int64_t(p.num_q_heads) * p.rec_floats;
+    float M = -INFINITY;
+    for (int q = 0; q < n_parts; ++q)
+      M = fmaxf(M, __hip_atomic_load(rec0 + q * step + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    float num = 0.f, den = 0.f;
+    for (int q = 0; q < n_parts; ++q) {
+      const float* rec = rec0 + q * step;
+      const float w = __builtin_amdgcn_exp2f(
+          __hip_atomic_load(rec + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M_use);
+      num = __builtin_fmaf(w, __hip_atomic_load(rec + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), num);
+      den = __builtin_fmaf(w, __hip_atomic_load(rec + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), den);
+    }
+    p.out[(int64_t(seq) * p.num_q_heads + qh) * D + dd] = num / den;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Occupancy hint (waves per SIMD) where the compiler fits the kernel in
 // the matching register budget without spilling (checked per instance):
@@ -306,77 +390,288 @@ __global__ __launch_bounds__(kWave* NW, (decode_waves_hint<DT, D, GW>())) void p
   }
   __syncthreads();
 
-  const bool single = (n_parts <= 1);
-  const int pidx = single ? -1 : p.part_offset[seq] + part;
-  if (!single && (pidx < 0 || pidx >= p.n_partials)) return;
-  for (int idx = threadIdx.x; idx < GW * D; idx += kWave * NW) {
-    const int g = idx / D;
-    const int dd = idx - g * D;
-    float M = -INFINITY;
+  finish_item<D, GW, NW * RPI, kWave * NW>(p, sm_m, sm_l, sm_o, seq, part, n_parts, hg, hgroups, qh0);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped-query decode on the matrix cores (fp16 / bf16, head_dim 128).
+//
+// With GQA the GW query heads of a KV head share every K/V tile, so per
+// block S^T = K Q^T is a 16-token x GW-head product and O^T += V^T P^T a
+// 128-dim x GW-head one: small dense contractions that the VALU path spends
+// about 400 instructions per tile on (dot products, row sums, per-head
+// softmax, per-head V products).  Here they run as MFMA, with GW heads in
+// the 16 columns (column n serves head n mod GW; the copies cost nothing
+// on the matrix cores, and every lane then holds a real head).
+//
+// Lane (g, n) = lane (16 g + n).  Per block and wave:
+//  * K tile: load kc (kc = 0..3) gives lane (g, n) 16 bytes of token n at
+//    dims 32 kc + 8 g .. + 7, which is the A operand of
+//    v_mfma_f32_16x16x32 (row n, k-slice 8 g); each load reads 64
+//    contiguous bytes of all 16 rows.  Q^T is the B operand (column n, the
+//    same dims), loaded once.
+//  * The accumulator leaves lane (g, n) with the scores of tokens
+//    4 g .. 4 g + 3 for column n: the B-operand layout of the 16x16x16
+//    product that follows, so the weights never move between lanes.  The
+//    online softmax keeps one running maximum per column (the four lanes of
+//    a column agree after an exchange through gfx950's lane swaps) and a
+//    per-lane partial sum.
+//  * V tile: load j (j = 0..3) gives lane (g, n) dims 8 n .. 8 n + 7 of
+//    token 4 g + j, four full 256-byte rows per load.  The lane then holds
+//    its four tokens at eight dims; pairing halves gives, for each dim
+//    8 n + t (t = 0..7), the A operand of O^T += V^T P^T (row n, tokens
+//    4 g .. 4 g + 3), so d-tile t of O^T covers dims 8 r + t for rows r and
+//    lane (g, n) ends with dims 32 g .. 32 g + 31 of its column: no LDS
+//    transpose.
+//  * Weights: fp16 inputs round them to fp16; bf16 inputs split them into a
+//    bf16 head and a bf16 remainder (two products), since bf16 weights
+//    alone put short contexts above the 2e-3 tolerance.  The normaliser
+//    sums the fp32 weights.
+//  * Masking: the tile's buffer resources cover only the rows that hold
+//    tokens (zeros beyond, so V rows past the length contribute 0 even if
+//    the pool holds NaN there) and scores of rows past the length are -inf.
+//  * With k_new / v_new, the newest token's row is taken from those arrays
+//    into the registers of the tile (the pool slot may still be being
+//    written by this launch), and the first head group stores it.
+// The partition's states then merge and combine as in the VALU kernel.
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegBig = -3.0e38f;  // finite "no token yet" running maximum
+
+template <int DT>
+__device__ __forceinline__ f4 mfma_k32(const u32x4& a, const u32x4& b, const f4& c) {
+  if constexpr (DT == PKV_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c,
+                                                   0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ f4 mfma_k16(const u32x2& a, const u32x2& b, const f4& c) {
+  if constexpr (DT == PKV_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, b), c, 0, 0,
+                                                 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c,
+                                                     0, 0, 0);
+}
+
+// A streamed 16-byte tile load (nontemporal, as load_stream) whose
+// wave-uniform part of the offset sits in a scalar register, so that one
+// vector offset serves all loads of a tile.
+__device__ __forceinline__ u32x4 load_stream_s(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, kCachePolicyNT));
+}
+
+// Maximum over the four lanes n, n + 16, n + 32, n + 48 of a column: a
+// swap of a register with itself leaves each lane its own value and its
+// partner's (16 lanes away for permlane16, 32 for permlane32).
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(f_bits(x), f_bits(x), false, false);
+  x = fmaxf(bits_f(a[0]), bits_f(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
+  return fmaxf(bits_f(b[0]), bits_f(b[1]));
+}
+
+template <int DT, int GW, int NW>
+__global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const DecodeParams p) {
+  constexpr int D = 128;
+  constexpr int R = D * 2;                // bytes per token row of one head
+  constexpr int TILE = kBlockTokens * R;  // one (block, KV head) tile
+  static_assert(GW >= 2 && GW <= 16 && (GW & (GW - 1)) == 0, "2 to 16 heads per workgroup");
+  static_assert(DT == PKV_F16 || DT == PKV_BF16, "16-bit inputs");
+
+  __shared__ float sm_m[NW * GW];
+  __shared__ float sm_l[NW * GW];
+  __shared__ __attribute__((aligned(16))) float sm_o[NW * GW * D];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int hgroups = p.num_kv_heads * p.hgroups_per_kv;
+  const int wi = blockIdx.x / hgroups;
+  const int hg = blockIdx.x - wi * hgroups;
+  const int seq = p.work[2 * wi];
+  const int part = p.work[2 * wi + 1];
+  const int kvh = hg / p.hgroups_per_kv;
+  const int qh0 = kvh * p.group + (hg - kvh * p.hgroups_per_kv) * GW;
+  const int L = p.context_lens[seq];
+  const int nblk = min((L + kBlockTokens - 1) / kBlockTokens, p.table_stride);
+  const int n_parts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  const int b0 = part * p.partition_blocks;
+  const int b1 = min(b0 + p.partition_blocks, nblk);
+  const bool writes_new = (hg - kvh * p.hgroups_per_kv) == 0;
+  const float c2 = p.scale_log2;
+
+  // Q^T (B operand): column n = head qh0 + n mod GW, dims 32 kc + 8 g .. + 7
+  u32x4 qb[4];
+  {
+    const char* qrow = p.q + (int64_t(seq) * p.num_q_heads + qh0 + (n & (GW - 1))) * R;
 #pragma unroll
-    for (int s = 0; s < NW * RPI; ++s) M = fmaxf(M, sm_m[s * GW + g]);
-    const float M_use = (M == -INFINITY) ? 0.f : M;
-    float num = 0.f, den = 0.f;
+    for (int kc = 0; kc < 4; ++kc) qb[kc] = *reinterpret_cast<const u32x4*>(qrow + 64 * kc + 16 * g);
+  }
+
+  float m = kNegBig, lsum = 0.f;
+  f4 o[8];
 #pragma unroll
-    for (int s = 0; s < NW * RPI; ++s) {
-      const float w = __builtin_amdgcn_exp2f(sm_m[s * GW + g] - M_use);
-      num = __builtin_fmaf(w, sm_o[(s * GW + g) * D + dd], num);
-      den = __builtin_fmaf(w, sm_l[s * GW + g], den);
-    }
-    const int qh = qh0 + g;
-    if (single) {
-      p.out[(int64_t(seq) * p.num_q_heads + qh) * D + dd] = num / den;
+  for (int t = 0; t < 8; ++t) o[t] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* trow = p.block_tables + int64_t(seq) * p.table_stride;
+  const int64_t blk_stride = int64_t(p.num_kv_heads) * TILE;
+
+  // Issue the K/V loads of block j of the current chunk into kk / vv.  The
+  // loads are always issued (same loads on every path, exact vmcnt waits);
+  // the resources cover the rows that hold tokens, none past the chunk's
+  // end or for a table entry outside the pool.  Returns the block id.
+  int cb = 0, ce = 0, tbl = -1;
+  const int koff = n * R + 16 * g;      // + 64 kc
+  const int voff = 4 * g * R + 16 * n;  // + t R
+  auto issue = [&](int j, u32x4* kk, u32x4* vv) __attribute__((always_inline)) -> int {
+    const int blk = __builtin_amdgcn_readlane(tbl, min(j - cb, kWave - 1));
+    const bool ok = j < ce && unsigned(blk) < unsigned(p.num_blocks);
+    const int rows = ok ? min(kBlockTokens, L - j * kBlockTokens) : 0;
+    const int64_t tile = int64_t(ok ? blk : 0) * blk_stride + int64_t(kvh) * TILE;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_cache + tile, rows * R);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_cache + tile, rows * R);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) kk[kc] = load_stream_s(rk, koff, 64 * kc);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) vv[t] = load_stream_s(rv, voff, t * R);
+    return j < ce ? blk : -1;
+  };
+
+  // One block: `valid` rows hold tokens (16 except in the last block).
+  auto process = [&](const u32x4* kk, const u32x4* vv, int valid) __attribute__((always_inline)) {
+    f4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) sacc = mfma_k32<DT>(kk[kc], qb[kc], sacc);
+    float s[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * g + r >= valid) s[r] = -INFINITY;
+    const float mx = max_over_lane_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+    const float mn = fmaxf(m, mx * c2);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -mn));
+    lsum = lsum * alpha + ((x[0] + x[1]) + (x[2] + x[3]));
+    const f2 x01 = {x[0], x[1]}, x23 = {x[2], x[3]};
+    u32x2 pb, pl;
+    if constexpr (DT == PKV_F16) {
+      pb = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01, h2)),
+                 __builtin_bit_cast(uint32_t, __builtin_convertvector(x23, h2))};
     } else {
-      // partial record of (partition, query head): agent-scope stores, so
-      // the combining workgroup on any XCD reads them without cache flushes
-      float* rec = p.part + (int64_t(pidx) * p.num_q_heads + qh) * p.rec_floats;
-      __hip_atomic_store(rec + dd, num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (dd == 0) {
-        __hip_atomic_store(rec + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(rec + D + 1, den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const b2 h01 = __builtin_convertvector(x01, b2), h23 = __builtin_convertvector(x23, b2);
+      pb = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+      pl = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01 - __builtin_convertvector(h01, f2), b2)),
+                 __builtin_bit_cast(uint32_t, __builtin_convertvector(x23 - __builtin_convertvector(h23, f2), b2))};
+    }
+    // every block rescales (alpha = 1 when no maximum moved): a branch on a
+    // vote makes the compiler keep a second copy of the accumulators
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[t] *= alpha;
+    // vv[j] word w holds dims 8 n + 2 w (low half) and 8 n + 2 w + 1 (high
+    // half) of token 4 g + j
+    const uint32_t v0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
+    const uint32_t v1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+    const uint32_t v2[4] = {vv[2].x, vv[2].y, vv[2].z, vv[2].w};
+    const uint32_t v3[4] = {vv[3].x, vv[3].y, vv[3].z, vv[3].w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u32x2 lo = {(v0[w] & 0xFFFFu) | (v1[w] << 16), (v2[w] & 0xFFFFu) | (v3[w] << 16)};
+      const u32x2 hi = {(v0[w] >> 16) | (v1[w] & 0xFFFF0000u), (v2[w] >> 16) | (v3[w] & 0xFFFF0000u)};
+      o[2 * w] = mfma_k16<DT>(lo, pb, o[2 * w]);
+      o[2 * w + 1] = mfma_k16<DT>(hi, pb, o[2 * w + 1]);
+      if constexpr (DT == PKV_BF16) {
+        o[2 * w] = mfma_k16<DT>(lo, pl, o[2 * w]);
+        o[2 * w + 1] = mfma_k16<DT>(hi, pl, o[2 * w + 1]);
       }
     }
-  }
-  if (single || p.counters == nullptr) return;
+  };
 
-  // Split-K combine in the same launch.  Each workgroup of a (sequence, head
-  // group) waits until its partial stores have completed, takes a ticket, and
-  // the one taking the last ticket combines every partition's record and
-  // resets the ticket for the next launch.  Records and tickets are only
-  // touched through agent-scope atomics and every record owns whole cache
-  // lines, so no cache writeback or invalidate is needed.
-  __shared__ int sm_last;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int32_t* ticket = p.counters + int64_t(seq) * hgroups + hg;
-  if (threadIdx.x == 0)
-    sm_last = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               n_parts - 1);
-  __syncthreads();
-  if (!sm_last) return;
-  const int base = p.part_offset[seq];
-  if (base < 0 || base + n_parts > p.n_partials) return;
-  for (int idx = threadIdx.x; idx < GW * D; idx += kWave * NW) {
-    const int g = idx / D;
-    const int dd = idx - g * D;
-    const int qh = qh0 + g;
-    const float* rec0 = p.part + (int64_t(base) * p.num_q_heads + qh) * p.rec_floats;
-    const int64_t step = int64_t(p.num_q_heads) * p.rec_floats;
-    float M = -INFINITY;
-    for (int q = 0; q < n_parts; ++q)
-      M = fmaxf(M, __hip_atomic_load(rec0 + q * step + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    const float M_use = (M == -INFINITY) ? 0.f : M;
-    float num = 0.f, den = 0.f;
-    for (int q = 0; q < n_parts; ++q) {
-      const float* rec = rec0 + q * step;
-      const float w = __builtin_amdgcn_exp2f(
-          __hip_atomic_load(rec + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M_use);
-      num = __builtin_fmaf(w, __hip_atomic_load(rec + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), num);
-      den = __builtin_fmaf(w, __hip_atomic_load(rec + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), den);
+  // One block.  Rows past the sequence length (in its last block) or in a
+  // table entry outside the pool are masked; every block takes the same
+  // masked step (a few compares), which keeps one copy of the step per
+  // register buffer.  With k_new given, the newest row (position L - 1)
+  // replaces row r_new of the tile: K in the lanes of column r_new, V in
+  // lane group r_new / 4, load r_new mod 4; the first head group stores it.
+  auto consume = [&](u32x4* kk, u32x4* vv, int j, int blk) __attribute__((always_inline)) {
+    const bool in_pool = unsigned(blk) < unsigned(p.num_blocks);
+    const int valid = in_pool ? min(kBlockTokens, L - j * kBlockTokens) : 0;
+    const int r_new = L - 1 - j * kBlockTokens;
+    if (p.k_new != nullptr && in_pool && r_new < kBlockTokens) {
+      const int64_t src = (int64_t(seq) * p.num_kv_heads + kvh) * R;
+      const u32x4 nv = *reinterpret_cast<const u32x4*>(p.v_new + src + 16 * n);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const u32x4 nk = *reinterpret_cast<const u32x4*>(p.k_new + src + 64 * kc + 16 * g);
+        kk[kc] = n == r_new ? nk : kk[kc];
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) vv[t] = (g == (r_new >> 2) && t == (r_new & 3)) ? nv : vv[t];
+      if (writes_new && g == 0) {
+        const int64_t dst = int64_t(blk) * blk_stride + int64_t(kvh) * TILE + int64_t(r_new) * R + 16 * n;
+        *reinterpret_cast<u32x4*>(p.k_cache + dst) = *reinterpret_cast<const u32x4*>(p.k_new + src + 16 * n);
+        *reinterpret_cast<u32x4*>(p.v_cache + dst) = nv;
+      }
     }
-    p.out[(int64_t(seq) * p.num_q_heads + qh) * D + dd] = num / den;
+    process(kk, vv, valid);
+  };
+
+  // Wave `wave` takes blocks b0 + wave, b0 + wave + NW, ... (table entries in
+  // chunks of 64, one per lane; two register buffers alternate, as in the
+  // VALU kernel).
+  u32x4 ka[4], va[4], kb[4], vb[4];
+  for (cb = b0; cb < b1; cb += kWave) {
+    ce = min(cb + kWave, b1);
+    tbl = (cb + lane < ce) ? trow[cb + lane] : -1;
+    int j = cb + wave;
+    if (j >= ce) break;
+    int blk_a = issue(j, ka, va), blk_b;
+    while (true) {
+      blk_b = issue(j + NW, kb, vb);
+      consume(ka, va, j, blk_a);
+      j += NW;
+      if (j >= ce) break;
+      blk_a = issue(j + NW, ka, va);
+      consume(kb, vb, j, blk_b);
+      j += NW;
+      if (j >= ce) break;
+    }
   }
-  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // this wave's state per column: the sum over the four lane groups, dims
+  // 32 g + 8 r + t in o[t][r]
+  float lt = lsum + __shfl_xor(lsum, 16);
+  lt += __shfl_xor(lt, 32);
+  if (n < GW) {
+    if (g == 0) {
+      sm_m[wave * GW + n] = m;
+      sm_l[wave * GW + n] = lt;
+    }
+    float* orow = sm_o + (wave * GW + n) * D + 32 * g;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<f4*>(orow + 8 * r) = f4{o[0][r], o[1][r], o[2][r], o[3][r]};
+      *reinterpret_cast<f4*>(orow + 8 * r + 4) = f4{o[4][r], o[5][r], o[6][r], o[7][r]};
+    }
+  }
+  __syncthreads();
+
+  finish_item<D, GW, NW, kWave * NW>(p, sm_m, sm_l, sm_o, seq, part, n_parts, hg, hgroups, qh0);
 }
 
 struct ReduceParams {
@@ -465,6 +760,38 @@ DecodeFn pick_decode(int dt, int d, int gw, int nw) {
   }
 }
 
+template <int DT, int GW>
+DecodeFn pick_mfma_waves(int nw) {
+  switch (nw) {
+    case 1: return paged_decode_mfma_kernel<DT, GW, 1>;
+    case 2: return paged_decode_mfma_kernel<DT, GW, 2>;
+    case 4: return paged_decode_mfma_kernel<DT, GW, 4>;
+    case 8:  // its LDS merge area fits 32 KiB for GW <= 8
+      if constexpr (GW <= 8) return paged_decode_mfma_kernel<DT, GW, 8>;
+      return paged_decode_mfma_kernel<DT, GW, 4>;
+    default: return nullptr;
+  }
+}
+
+template <int DT>
+DecodeFn pick_mfma_gw(int gw, int nw) {
+  switch (gw) {
+    case 2: return pick_mfma_waves<DT, 2>(nw);
+    case 4: return pick_mfma_waves<DT, 4>(nw);
+    case 8: return pick_mfma_waves<DT, 8>(nw);
+    case 16: return pick_mfma_waves<DT, 16>(nw);
+    default: return nullptr;
+  }
+}
+
+DecodeFn pick_mfma(int dt, int gw, int nw) {
+  switch (dt) {
+    case PKV_F16: return pick_mfma_gw<PKV_F16>(gw, nw);
+    case PKV_BF16: return pick_mfma_gw<PKV_BF16>(gw, nw);
+    default: return nullptr;
+  }
+}
+
 // Waves per workgroup (they split a partition's blocks): 4 by default, the
 // best of {1, 2, 4} x partition {128, 256, 512} on the GPT-style fp16 batch;
 // PKV_DECODE_WAVES overrides it for tuning sweeps.
@@ -477,22 +804,31 @@ int waves_per_item() {
   return nw;
 }
 
-// Query heads of one KV head that one workgroup takes (GW).  All of them
-// (up to 8) by default: splitting a KV head's query heads over workgroups
-// makes each read the tiles (the nontemporal loads keep no copy in L2 for
-// the others; measured 1.45x slower for GQA-4 split in two).
-// PKV_DECODE_GW caps it for tuning sweeps.
-int heads_per_workgroup(int group, int32_t dtype, int32_t head_dim) {
+// Query heads of one KV head that one workgroup takes (GW): all of them,
+// up to 8 on the VALU kernel and 16 on the matrix-core one.  Splitting a KV
+// head's query heads over workgroups makes each read the tiles (the
+// nontemporal loads keep no copy in L2 for the others; measured 1.45x
+// slower for GQA-4 split in two).  PKV_DECODE_GW caps it for tuning sweeps.
+int heads_per_workgroup(int group, int limit) {
   static const int cap = [] {
     const char* s = std::getenv("PKV_DECODE_GW");
     const int v = s ? std::atoi(s) : 0;
-    return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 8;
+    return (v == 1 || v == 2 || v == 4 || v == 8 || v == 16) ? v : 16;
   }();
-  (void)dtype;
-  (void)head_dim;
+  limit = std::min(limit, cap);
   int gw = 1;
-  while (gw < cap && group % (2 * gw) == 0) gw *= 2;
+  while (gw < limit && group % (2 * gw) == 0) gw *= 2;
   return gw;
+}
+
+// Grouped-query batches of fp16 / bf16 with head_dim 128 run on the
+// matrix-core kernel when at least two query heads share a workgroup.
+// PKV_DECODE_MFMA=0 selects the VALU kernel instead; it is read at every
+// launch, so one process can run and compare both.
+bool mfma_eligible(int group, int32_t dtype, int32_t head_dim) {
+  if (group < 2 || head_dim != 128 || (dtype != PKV_F16 && dtype != PKV_BF16)) return false;
+  const char* s = std::getenv("PKV_DECODE_MFMA");
+  return !(s && s[0] == '0');
 }
 
 // Validate the arguments shared by the decode entry points and fill the
@@ -502,7 +838,7 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
                         const int32_t* block_tables, int32_t table_stride,
                         const int32_t* context_lens, float scale, const int32_t* plan,
                         const pkv_decode_plan_info* info, void* workspace, size_t workspace_bytes,
-                        DecodeParams& prm, int& gw, bool& empty) {
+                        DecodeParams& prm, int& gw, bool& mfma, bool& empty) {
   empty = false;
   if (!pool) return fail(PKV_E_BAD_ARG, "null pool");
   const pkv_pool_desc& d = pool->desc;
@@ -535,7 +871,9 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_E_BAD_ARG, "workspace too small: need " + std::to_string(need) + " bytes");
   const int group = num_q_heads / d.num_kv_heads;
-  gw = heads_per_workgroup(group, d.dtype, d.head_dim);
+  mfma = mfma_eligible(group, d.dtype, d.head_dim);
+  gw = heads_per_workgroup(group, mfma ? 16 : 8);
+  if (gw < 2) mfma = false;
   prm.q = static_cast<const char*>(q);
   prm.k_new = static_cast<const char*>(k_new);
   prm.v_new = static_cast<const char*>(v_new);
@@ -575,11 +913,11 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
 // ev_start / ev_stop (optional) are attached to the dispatch itself
 // (hipExtLaunchKernel), so their interval is the kernel's execution, without
 // the queueing of separate marker packets.
-pkv_status launch_partitions(const pkv_pool* pool, const DecodeParams& prm, int gw,
+pkv_status launch_partitions(const pkv_pool* pool, const DecodeParams& prm, int gw, bool mfma,
                              const pkv_decode_plan_info* info, hipStream_t s,
                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
   const int nw = waves_per_item();
-  DecodeFn fn = pick_decode(pool->desc.dtype, pool->desc.head_dim, gw, nw);
+  DecodeFn fn = mfma ? pick_mfma(pool->desc.dtype, gw, nw) : pick_decode(pool->desc.dtype, pool->desc.head_dim, gw, nw);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group");
   const int64_t grid = int64_t(info->n_work) * prm.num_kv_heads * prm.hgroups_per_kv;
   if (ev_start || ev_stop)
@@ -622,32 +960,33 @@ using namespace pkv;
 #define PKV_SETUP                                                                                \
   DecodeParams prm;                                                                              \
   int gw = 1;                                                                                    \
-  bool empty = false;                                                                            \
+  bool mfma = false, empty = false;                                                              \
   if (pkv_status st = setup_decode(pool, q, k_new, v_new, out, num_seqs, num_q_heads,           \
                                    block_tables, table_stride, context_lens, scale, plan, info, \
-                                   workspace, workspace_bytes, prm, gw, empty))                 \
+                                   workspace, workspace_bytes, prm, gw, mfma, empty))           \
     return st;                                                                                   \
   if (empty) return PKV_OK;                                                                      \
   hipStream_t s = static_cast<hipStream_t>(stream);
 
 extern "C" pkv_status pkv_paged_decode(PKV_DECODE_ARGS) {
   PKV_SETUP
-  return launch_partitions(pool, prm, gw, info, s);  // combine fused in
+  return launch_partitions(pool, prm, gw, mfma, info, s);  // combine fused in
 }
 
 pkv_status pkv::paged_decode_timed(PKV_DECODE_ARGS, hipEvent_t ev_start, hipEvent_t ev_stop) {
   PKV_SETUP
-  return launch_partitions(pool, prm, gw, info, s, ev_start, ev_stop);
+  return launch_partitions(pool, prm, gw, mfma, info, s, ev_start, ev_stop);
 }
 
 extern "C" pkv_status pkv_paged_decode_partitions(PKV_DECODE_ARGS) {
   PKV_SETUP
   prm.counters = nullptr;  // partials only; pkv_paged_decode_reduce combines
-  return launch_partitions(pool, prm, gw, info, s);
+  return launch_partitions(pool, prm, gw, mfma, info, s);
 }
 
 extern "C" pkv_status pkv_paged_decode_reduce(PKV_DECODE_ARGS) {
   PKV_SETUP
   (void)gw;
+  (void)mfma;
   return launch_reduce(pool, prm, num_seqs, info, s);
 }

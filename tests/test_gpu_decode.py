@@ -235,3 +235,33 @@ def test_workspace_shared_by_launches_of_different_shapes():
     finally:
         for case in cases:
             case.close()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("group", [2, 4, 8, 16])
+def test_gqa_both_kernels(dtype, group, monkeypatch):
+    """Grouped-query decode of head_dim 128 runs on the matrix-core kernel by
+    default; PKV_DECODE_MFMA=0 selects the VALU kernel.  Both against the
+    oracle, with and without the fused append, split and unsplit."""
+    idx = 300 + 10 * group + (dtype == "bf16")
+    cfg = dataclasses.replace(CONFIGS[0], name="gqa_kernels", index=idx, dtype=dtype, head_dim=128,
+                              num_kv_heads=2, num_q_heads=2 * group, num_seqs=10)
+    lens = [1, 2, 15, 16, 17, 33, 100, 257, 600, 1111]
+    nb = sum(-(-L // 16) for L in lens) + 3
+    order = np.random.default_rng(idx).permutation(nb)
+    case = DecodeCase(cfg, lens=lens, num_blocks=nb, free_order=order, fill=float("nan"))
+    try:
+        case.write_context(skip_last=True)
+        for mode in ("1", "0"):
+            monkeypatch.setenv("PKV_DECODE_MFMA", mode)
+            for P in (16, 256, 0):
+                for split in (False, True):
+                    out, _ = case.decode(P, split=split, append=True)
+                    err = max_err(case, out, range(len(lens)))
+                    print(f"[gpu] gqa {dtype} group={group} mfma={mode} P={P} split={split} "
+                          f"max_err={err:.3e}", flush=True)
+                    assert np.isfinite(out).all()
+                    assert err <= TOL[dtype], (mode, P, split, err)
+                    assert case.last_tickets_zero
+    finally:
+        case.close()
