@@ -108,7 +108,9 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="gpt_f16")
-    ap.add_argument("--partition", type=int, default=0, help="split-K partition tokens (0 = library default)")
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="split-K partition tokens (0 = library default; -1 = fill mode: per step, the "
+                         "smallest partition whose workgroups are all resident at once, else the default)")
     ap.add_argument("--max-keys", type=int, default=None,
                     help="prefill workloads: split tiles attending more keys (0 = never, -1 = the "
                          "library's rule for under-filled launches; default -1)")
@@ -569,6 +571,10 @@ def main(argv=None):
     k_ctx, v_ctx, q_dev = dev_tensor(vals["k"]), dev_tensor(vals["v"]), dev_tensor(vals["q"])
     new_k = dev_tensor(draw_normal_storage((cfg.seed, 50), (total, B, H, d), dt))
     new_v = dev_tensor(draw_normal_storage((cfg.seed, 51), (total, B, H, d), dt))
+    native = not (args.two_launch or args.separate_write or args.no_overlap)
+    # fill mode is chosen inside the native stepper; the Python-driven paths
+    # take the library default instead
+    partition = args.partition if (native or args.partition >= 0) else 0
     reps = []
     for r in range(args.replicas):
         kc = torch.zeros((nb, H, 16, d), dtype=tdt, device="cuda")
@@ -576,7 +582,7 @@ def main(argv=None):
         pool = Pool(nb, H, d, dt, stride, 16, order, kc, vc)
         slots = np.concatenate([pool.alloc(int(L))[1] for L in sh.lens])
         pool.write_kv(k_ctx, v_ctx, torch.from_numpy(slots).cuda())
-        it = DecodeIteration(pool, B, stride, Hq, args.partition, pipelined=not args.no_overlap)
+        it = DecodeIteration(pool, B, stride, Hq, partition, pipelined=not args.no_overlap)
         out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
         reps.append((pool, it, out, kc, vc))
     del k_ctx, v_ctx
@@ -588,7 +594,6 @@ def main(argv=None):
           for _ in range(total)]
     step_bytes, infos = [], []
 
-    native = not (args.two_launch or args.separate_write or args.no_overlap)
     seqs_np = np.arange(B, dtype=np.int32)
     ctx_tokens = [int(sh.lens.sum())] * args.replicas  # tokens in each replica before a step
 
@@ -650,6 +655,7 @@ def main(argv=None):
                    "head_dim": d, "block_size": 16, "mean_context": round(float(sh.lens.mean()), 1),
                    "mean_context_timed": round(timed_ctx, 1),
                    "max_context": int(sh.lens.max()), "partition_tokens": info.partition_tokens,
+                   "partition_mode": {-1: "fill", 0: "default"}.get(partition, "fixed"),
                    "work_items": info.n_work, "replicas": args.replicas,
                    "decode_launches": 2 if args.two_launch else 1,
                    "new_kv_store": "write_kv" if args.separate_write else "in decode",

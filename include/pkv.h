@@ -428,6 +428,25 @@ size_t pkv_decode_workspace_bound(int32_t max_seqs, int32_t max_context_len, int
 /* Partition length that partition_tokens = 0 selects. */
 int32_t pkv_default_partition_tokens(void);
 
+/* Fill mode: a stepper created with partition_tokens = PKV_PARTITION_FILL
+ * picks, at every iteration, the smallest partition that lets all of the
+ * launch's workgroups be resident on the GPU at once
+ * (pkv_decode_fill_partition over pkv_decode_occupancy), else the default.
+ * pkv_prepare_decode_bytes, pkv_stepper_slot_bytes and
+ * pkv_decode_workspace_bound size buffers for it as for PKV_FILL_MIN_TOKENS;
+ * the plan functions themselves take concrete sizes only. */
+#define PKV_PARTITION_FILL (-1)
+#define PKV_FILL_MIN_TOKENS 512
+
+/* Smallest multiple of block_size P >= min_tokens for which
+ * workgroups_per_item * sum_i ceil(context_lens[i] / P) <= resident, i.e. a
+ * split-K plan whose workgroups all fit on the GPU at once (one dispatch
+ * round: no tail of a partly filled second round, and the finest split that
+ * does so).  0 when even one partition per sequence needs more; the caller
+ * then keeps its partition size.  Host only. */
+int32_t pkv_decode_fill_partition(const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                                  int32_t workgroups_per_item, int64_t resident, int32_t min_tokens);
+
 /* ---------------------------------------------------------------------------
  * Host: chunked-prefill plan
  * ------------------------------------------------------------------------ */
@@ -536,7 +555,10 @@ pkv_status pkv_prepare_decode(pkv_pool* pool, const int32_t* seqs, int32_t n_seq
  * else.  The compute stream never waits on another stream; the host waits
  * for each upload before launching, and for the iterations that last used a
  * slot before rewriting it (one completion event per group of four slots).
- * All calls on one stepper must use the same compute stream. */
+ * All calls on one stepper must use the same compute stream.
+ * partition_tokens: a concrete size, 0 (the default) or PKV_PARTITION_FILL
+ * (re-chosen at every iteration from the batch's lengths after the append;
+ * size slots and workspace with the same value). */
 #define PKV_STEPPER_SLOTS 8
 typedef struct pkv_stepper pkv_stepper;
 
@@ -571,6 +593,14 @@ pkv_status pkv_stepper_step(pkv_stepper* stepper, const int32_t* seqs, int32_t n
 /* ---------------------------------------------------------------------------
  * Device (HIP, gfx950): asynchronous on `stream`
  * ------------------------------------------------------------------------ */
+
+/* Workgroups pkv_paged_decode launches per work item (KV heads x query-head
+ * groups) and how many of its workgroups the current device holds resident
+ * at once (the occupancy of the kernel this pool and head count select,
+ * times the number of compute units): the inputs of
+ * pkv_decode_fill_partition.  Makes no launch. */
+pkv_status pkv_decode_occupancy(const pkv_pool* pool, int32_t num_q_heads, int32_t* workgroups_per_item,
+                                int64_t* resident);
 
 /* Copy-on-write copies ([lesson] paragraph 7): for each pair, K[dst] = K[src]
  * and V[dst] = V[src] over all heads and rows.  pairs: device int32

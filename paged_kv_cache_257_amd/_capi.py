@@ -164,6 +164,8 @@ SIGNATURES = {
     "pkv_decode_workspace_bytes": [C.POINTER(PlanInfo), I32, I32],
     "pkv_decode_workspace_bound": [I32, I32, I32, I32, I32, I32],
     "pkv_default_partition_tokens": [],
+    "pkv_decode_fill_partition": [PI32, I32, I32, I32, C.c_int64, I32],
+    "pkv_decode_occupancy": [P, I32, PI32, PI64],
     "pkv_prefill_plan_ints": [PI32, PI32, I32, I32, I32, I32, PI32],
     "pkv_prefill_plan": [PI32, PI32, I32, I32, I32, I32, PI32, I32, C.POINTER(PrefillPlanInfo)],
     "pkv_prefill_workspace_bytes": [C.POINTER(PrefillPlanInfo), I32],
@@ -186,9 +188,11 @@ SIGNATURES = {
 }
 RESTYPES = {"pkv_last_error": C.c_char_p, "pkv_decode_workspace_bytes": C.c_size_t,
             "pkv_decode_workspace_bound": C.c_size_t, "pkv_default_partition_tokens": C.c_int32,
+            "pkv_decode_fill_partition": C.c_int32,
             "pkv_prefill_workspace_bytes": C.c_size_t,
             "pkv_prepare_decode_bytes": C.c_size_t, "pkv_stepper_slot_bytes": C.c_size_t}
 DEVICE_FUNCS = ("pkv_copy_blocks", "pkv_write_kv", "pkv_read_kv", "pkv_paged_decode", "pkv_paged_decode_partitions",
+                "pkv_decode_occupancy",
                 "pkv_paged_decode_reduce", "pkv_paged_prefill", "pkv_hybrid_copy_states",
                 "pkv_stepper_slot_bytes", "pkv_stepper_create",
                 "pkv_stepper_destroy", "pkv_stepper_step")

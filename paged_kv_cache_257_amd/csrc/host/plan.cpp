@@ -131,10 +131,40 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
 
 int32_t pkv_default_partition_tokens(void) { return pkv::kDefaultPartitionTokens; }
 
+int32_t pkv_decode_fill_partition(const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                                  int32_t workgroups_per_item, int64_t resident, int32_t min_tokens) {
+  if (num_seqs < 0 || (num_seqs > 0 && !context_lens) || block_size < 1 || workgroups_per_item < 1 ||
+      resident < 1 || min_tokens < 1)
+    return 0;
+  int32_t max_len = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    if (context_lens[i] < 1) return 0;
+    max_len = std::max(max_len, context_lens[i]);
+  }
+  // workgroups of a plan with partitions of P tokens (non-increasing in P)
+  auto workgroups = [&](int64_t P) {
+    int64_t items = 0;
+    for (int32_t i = 0; i < num_seqs; ++i) items += (context_lens[i] + P - 1) / P;
+    return items * workgroups_per_item;
+  };
+  // candidates: multiples of block_size from the first >= min_tokens up to
+  // the first that holds the longest sequence whole
+  const int64_t lo = (int64_t(min_tokens) + block_size - 1) / block_size;
+  const int64_t hi = std::max(lo, (int64_t(max_len) + block_size - 1) / block_size);
+  if (workgroups(hi * block_size) > resident) return 0;
+  int64_t a = lo, b = hi;  // smallest m in [a, b] with workgroups(m * bs) <= resident
+  while (a < b) {
+    const int64_t m = (a + b) / 2;
+    if (workgroups(m * block_size) <= resident) b = m;
+    else a = m + 1;
+  }
+  return a * block_size > INT32_MAX ? 0 : int32_t(a * block_size);
+}
+
 size_t pkv_decode_workspace_bound(int32_t max_seqs, int32_t max_context_len, int32_t block_size,
                                   int32_t partition_tokens, int32_t num_q_heads, int32_t head_dim) {
   if (max_seqs < 0 || max_context_len < 1 || block_size < 1) return 0;
-  const int32_t P = partition_tokens ? partition_tokens : pkv::kDefaultPartitionTokens;
+  const int32_t P = pkv::sizing_partition(partition_tokens);
   if (P < block_size || P % block_size != 0) return 0;
   const int64_t parts = (int64_t(max_context_len) + P - 1) / P;
   pkv_decode_plan_info worst{};

@@ -110,6 +110,12 @@ inline int dtype_bytes(int32_t dt) { return dt == PKV_F32 ? 4 : 2; }
 // partitions add combine work and more workgroups than the chip needs.
 constexpr int32_t kDefaultPartitionTokens = 2048;
 
+// A partition_tokens argument as the size buffers are dimensioned for: 0 is
+// the default, PKV_PARTITION_FILL the smallest size fill mode picks.
+inline int32_t sizing_partition(int32_t P) {
+  return P == 0 ? kDefaultPartitionTokens : P == PKV_PARTITION_FILL ? PKV_FILL_MIN_TOKENS : P;
+}
+
 // Query rows (token, head pairs) of one chunked-prefill workgroup: four
 // waves of two 16-row groups each.
 constexpr int32_t kPrefillTileRows = 128;

@@ -41,7 +41,7 @@ extern "C" {
 size_t pkv_prepare_decode_bytes(int32_t max_seqs, int32_t append_tokens, int32_t table_stride,
                                 int32_t block_size, int32_t partition_tokens) {
   if (max_seqs < 0 || append_tokens < 0 || table_stride < 1 || block_size < 1) return 0;
-  const int32_t P = partition_tokens ? partition_tokens : pkv::kDefaultPartitionTokens;
+  const int32_t P = pkv::sizing_partition(partition_tokens);
   if (P < block_size) return 0;
   const Offsets o = layout_for(max_seqs, append_tokens, max_seqs, table_stride,
                                plan_cap_for(max_seqs, table_stride, block_size, P));

@@ -16,7 +16,9 @@
 // only these events; every buffer is the caller's.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <string>
+#include <vector>
 
 #include "../host/pool_internal.h"
 #include "decode_launch.h"
@@ -43,6 +45,11 @@ struct pkv_stepper {
   int next = 0;
   hipStream_t last_stream = nullptr;  // compute stream of the latest launch
   bool pending = false;               // launches since the last group event
+  // fill mode (partition_tokens == PKV_PARTITION_FILL): the decode's
+  // workgroups per work item and resident workgroups, and length scratch
+  int32_t fill_wpi = 0;
+  int64_t fill_resident = 0;
+  std::vector<int32_t> fill_lens;
 };
 
 namespace {
@@ -75,8 +82,15 @@ pkv_status pkv_stepper_create(pkv_pool* pool, int32_t max_seqs, int32_t table_st
   if (need == 0 || slot_bytes < need)
     return fail(PKV_E_BAD_ARG, "staging slot too small: need " + std::to_string(need) + " bytes");
   if (slot_bytes % 256 != 0) return fail(PKV_E_BAD_ARG, "slot_bytes must be a multiple of 256");
+  int32_t wpi = 0;
+  int64_t resident = 0;
+  if (partition_tokens == PKV_PARTITION_FILL) {
+    if (pkv_status st = pkv_decode_occupancy(pool, num_q_heads, &wpi, &resident)) return st;
+  }
   pkv_stepper* s = new pkv_stepper();
   s->pool = pool;
+  s->fill_wpi = wpi;
+  s->fill_resident = resident;
   s->max_seqs = max_seqs;
   s->stride = table_stride;
   s->num_q_heads = num_q_heads;
@@ -135,9 +149,20 @@ pkv_status pkv_stepper_step(pkv_stepper* s, const int32_t* seqs, int32_t n_seqs,
     if (pkv_status st = hip_status(hipEventSynchronize(s->compute_done[k / kGroup]), "hipEventSynchronize"))
       return st;
   }
+  int32_t P = s->partition_tokens;
+  if (P == PKV_PARTITION_FILL) {
+    // the batch's lengths after this iteration's append
+    s->fill_lens.resize(size_t(std::max(n_seqs, 0)));
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      if (pkv_status st = pkv_seq_length(s->pool, seqs[i], &s->fill_lens[i])) return st;
+      s->fill_lens[i] += 1;
+    }
+    P = pkv_decode_fill_partition(s->fill_lens.data(), n_seqs, s->pool->desc.block_size, s->fill_wpi,
+                                  s->fill_resident, PKV_FILL_MIN_TOKENS);
+    if (P == 0) P = pkv::kDefaultPartitionTokens;
+  }
   pkv_batch_layout lay{};
-  if (pkv_status st = pkv_prepare_decode(s->pool, seqs, n_seqs, 1, s->stride, s->partition_tokens,
-                                         host, s->slot_bytes, &lay))
+  if (pkv_status st = pkv_prepare_decode(s->pool, seqs, n_seqs, 1, s->stride, P, host, s->slot_bytes, &lay))
     return st;  // the pool is unchanged
   s->next = (k + 1) % kSlots;
   if (layout_out) *layout_out = lay;

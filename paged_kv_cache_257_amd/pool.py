@@ -176,6 +176,12 @@ class Pool:
         n = int(pairs.shape[0])
         check(self.lib, self.lib.pkv_copy_blocks(self.handle, _dptr(pairs), n, _stream_ptr(stream)))
 
+    def decode_occupancy(self, num_q_heads: int) -> Tuple[int, int]:
+        """(workgroups per decode work item, resident workgroups on the device)."""
+        wpi, res = C.c_int32(), C.c_int64()
+        check(self.lib, self.lib.pkv_decode_occupancy(self.handle, num_q_heads, C.byref(wpi), C.byref(res)))
+        return wpi.value, res.value
+
     def paged_decode(self, q, out, block_tables, context_lens, scale: float, plan, info: PlanInfo,
                      workspace, stream=None, k_new=None, v_new=None, split: bool = False) -> None:
         """Decode attention of every sequence of the batch through its table.
@@ -265,6 +271,16 @@ def decode_workspace_bound(max_seqs: int, max_context_len: int, num_q_heads: int
     if n == 0:
         raise ValueError("bad decode geometry")
     return n
+
+
+def fill_partition(context_lens, workgroups_per_item: int, resident: int, min_tokens: int = 512,
+                   block_size: int = 16, host_only: bool = False) -> int:
+    """Smallest multiple of block_size >= min_tokens whose split-K plan puts
+    at most `resident` workgroups in flight (0 if none does)."""
+    lib = _capi.load(host_only=host_only)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    return int(lib.pkv_decode_fill_partition(i32p(lens), len(lens), block_size, workgroups_per_item,
+                                             int(resident), min_tokens))
 
 
 def default_partition_tokens(host_only: bool = False) -> int:

@@ -32,6 +32,7 @@ from .pool import Pool, _dptr, _stream_ptr
 
 NBUF = 3
 STEPPER_SLOTS = 8  # PKV_STEPPER_SLOTS in include/pkv.h
+PARTITION_FILL = -1  # PKV_PARTITION_FILL in include/pkv.h
 
 
 class DecodeIteration:
@@ -139,6 +140,9 @@ class DecodeIteration:
         host, dev = self.host[k], self.dev[k]
         lay = BatchLayout()
         a = self.append_tokens if append else 0
+        if self.P == PARTITION_FILL:
+            raise ValueError("fill-mode partitioning is chosen by the native stepper (step()); "
+                             "prepare() takes a concrete partition size or 0")
         check(self.lib, self.lib.pkv_prepare_decode(self.pool.handle, i32p(seqs_np), n, a, self.stride,
                                                     self.P, host.data_ptr(), self.nbytes, C.byref(lay)))
         compute = torch.cuda.current_stream() if stream is None else stream

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from paged_kv_cache_257_amd import (PkvError, decode_plan, decode_workspace_bound,
-                                    decode_workspace_bytes, default_partition_tokens)
+                                    decode_workspace_bytes, default_partition_tokens, fill_partition)
 from workloads import CONFIGS
 from workloads.configs import draw_decode_shapes
 
@@ -80,3 +80,51 @@ def test_default_partition_and_workspace_bound():
         decode_workspace_bytes(info, 8, 128, host_only=True)
     with pytest.raises(ValueError):
         decode_workspace_bound(4, 100, 8, 128, 24, host_only=True)
+
+
+def _fill_brute(lens, wpi, resident, min_tokens, bs=16):
+    """The rule restated by enumeration: the first multiple of bs >= min_tokens
+    (up to the one holding the longest sequence whole) whose plan has at most
+    `resident` workgroups, else 0."""
+    lo = -(-min_tokens // bs)
+    hi = max(lo, -(-max(lens) // bs)) if len(lens) else lo
+    for m in range(lo, hi + 1):
+        if wpi * sum(-(-int(L) // (m * bs)) for L in lens) <= resident:
+            return m * bs
+    return 0
+
+
+def test_fill_partition_matches_enumeration():
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        B = int(rng.integers(1, 40))
+        lens = rng.integers(1, 40000, size=B).astype(np.int32)
+        wpi = int(rng.choice([1, 2, 8, 32]))
+        resident = int(rng.integers(1, 4000))
+        mn = int(rng.choice([16, 256, 512, 1000]))
+        assert fill_partition(lens, wpi, resident, mn, host_only=True) == _fill_brute(lens, wpi, resident, mn)
+
+
+def test_fill_partition_cases():
+    # 10 x 32,786 tokens, 8 workgroups per item, 768 resident (3 per CU on
+    # 256 CUs): 9 partitions per sequence fit (720), 10 do not (800)
+    lens = np.full(10, 32786, np.int32)
+    P = fill_partition(lens, 8, 768, 512, host_only=True)
+    assert P == 3648 and 8 * 10 * -(-32786 // P) <= 768 and 8 * 10 * -(-32786 // (P - 16)) > 768
+    # 64 sequences x 32 heads cannot fit 768 at one partition each: 0
+    assert fill_partition(np.full(64, 500, np.int32), 32, 768, 512, host_only=True) == 0
+    # plenty of room: the minimum size
+    assert fill_partition(np.array([5000], np.int32), 1, 10 ** 6, 512, host_only=True) == 512
+    # a result is never below min_tokens, always a multiple of 16
+    assert fill_partition(np.array([17], np.int32), 1, 1, 100, host_only=True) == 112
+    # bad arguments -> 0
+    assert fill_partition(np.array([0], np.int32), 1, 10, 512, host_only=True) == 0
+    assert fill_partition(np.array([10], np.int32), 0, 10, 512, host_only=True) == 0
+
+
+def test_fill_mode_sizes_buffers_for_its_minimum():
+    from paged_kv_cache_257_amd import _capi
+    lib = _capi.load(host_only=True)
+    assert lib.pkv_prepare_decode_bytes(64, 1, 128, 16, -1) == lib.pkv_prepare_decode_bytes(64, 1, 128, 16, 512)
+    assert decode_workspace_bound(10, 33000, 32, 128, partition_tokens=-1, host_only=True) == \
+        decode_workspace_bound(10, 33000, 32, 128, partition_tokens=512, host_only=True)
