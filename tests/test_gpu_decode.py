@@ -5,8 +5,9 @@
   of sequences (all of them for the tiny workload) within the tolerance the
   workload states: max |err| <= 1e-5 for fp32 inputs, <= 2e-3 for fp16/bf16
   (fp32 accumulation, fp32 output);
-* each at the partition size the benchmark uses and at a second one, so both
-  the single-partition and the split-K + reduce paths are compared;
+* each at the partition size the benchmark uses, at a second one and at the
+  one fill mode picks, so both the single-partition and the split-K + reduce
+  paths are compared;
 * masking: pools pre-filled with NaN must not leak into outputs;
 * a sweep over dtypes, head dims 64/128/256, GQA groups 1-8 and ragged
   lengths around block boundaries (1, 15, 16, 17, ...);
@@ -19,6 +20,7 @@ import numpy as np
 import pytest
 import torch
 
+from paged_kv_cache_257_amd import default_partition_tokens, fill_partition
 from tests.gpu_helpers import TOL, DecodeCase, device_bits, host_bits, sync, to_device
 from workloads import CONFIGS, draw_normal_storage
 
@@ -64,7 +66,10 @@ def test_workload_parity(cfg):
         assert np.array_equal(device_bits(case.v_cache), host_bits(case.oracle.mirror.v))
         seqs = sample_seqs(case.lens, 12, cfg.seed)
         ref = {i: case.oracle_out(i) for i in seqs}
-        for P in PARTITIONS[cfg.name]:
+        # and the partition fill mode picks for this batch (the bench's default)
+        wpi, resident = case.pool.decode_occupancy(cfg.num_q_heads)
+        p_fill = fill_partition(case.lens, wpi, resident, 512) or default_partition_tokens()
+        for P in PARTITIONS[cfg.name] + (p_fill,):
             for split in (False, True):
                 out, info = case.decode(P, split=split)
                 err = max(float(np.max(np.abs(out[i] - ref[i]))) for i in seqs)
