@@ -39,8 +39,10 @@
 // bf16 remainder (two MFMAs, ~16 bits), since bf16 weights alone put the
 // error of short contexts above 2e-3.  Both round to nearest even, two
 // weights per conversion instruction.  The normaliser sums the fp32 weights.
-// The accumulators are rescaled only in stages where some row's running
-// maximum grew (a wave-wide vote); otherwise the factor is exactly 1.
+// A row's running maximum is raised only when a score exceeds it by more
+// than 2^8 in weight, and the accumulators are rescaled only in stages where
+// some row's maximum moved (a wave-wide vote); otherwise the factor is
+// exactly 1.
 #include "device_common.h"
 
 namespace pkv {
@@ -60,6 +62,13 @@ constexpr int kPfThreads = kWave * kPfWaves;
 constexpr int kStage = 32;  // key tokens per stage (two blocks)
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr float kNegBig = -3.0e38f;  // finite "no key yet" running max
+// Slack of the running maximum, in base-2 units: a row's maximum is raised
+// (and its accumulators rescaled) only when a score exceeds it by more than
+// this, so after the first keys of a long context the rescale almost never
+// runs.  Weights are then at most 2^8: exact enough as fp16 (11-bit
+// significand at any magnitude) or as a bf16 head + remainder, and row sums
+// of up to 2^8 times the key count stay far inside fp32.
+constexpr float kRescaleSlack = 8.f;
 
 struct PrefillParams {
   const char* q;             // [total_q][H_q][D]
@@ -259,11 +268,18 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
     }
     if (wave * kWave < VPAIRS) {
       const int ch = tid % CH, tok = 2 * (tid / CH);
-      const int kp = st * kStage + tok;
-      const uint32_t z0 = kp < L ? 0xFFFFFFFFu : 0u;  // rows past the context -> 0
-      const uint32_t z1 = kp + 1 < L ? 0xFFFFFFFFu : 0u;
-      const uint32_t a[4] = {vr0.x & z0, vr0.y & z0, vr0.z & z0, vr0.w & z0};
-      const uint32_t b[4] = {vr1.x & z1, vr1.y & z1, vr1.z & z1, vr1.w & z1};
+      uint32_t a[4] = {vr0.x, vr0.y, vr0.z, vr0.w};
+      uint32_t b[4] = {vr1.x, vr1.y, vr1.z, vr1.w};
+      if ((st + 1) * kStage > L) {  // the stage reaches past the context: those rows -> 0
+        const int kp = st * kStage + tok;
+        const uint32_t z0 = kp < L ? 0xFFFFFFFFu : 0u;
+        const uint32_t z1 = kp + 1 < L ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[i] &= z0;
+          b[i] &= z1;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t ea = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
@@ -331,7 +347,10 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
       mx = max_over_columns(mx);
-      const float mn = fmaxf(m[j], mx * c2);
+      // the running maximum moves only when a score exceeds it by more than
+      // kRescaleSlack (weights stay <= 2^kRescaleSlack in between)
+      const float mxs = mx * c2;
+      const float mn = mxs > m[j] + kRescaleSlack ? mxs : m[j];
       alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
       rescale |= mn > m[j];
       m[j] = mn;
