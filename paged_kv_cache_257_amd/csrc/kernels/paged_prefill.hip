@@ -231,29 +231,46 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
 
   // ---- staging: global -> registers -> LDS ----------------------------------
   // Every wave's staged rows lie in one block, so the block index and the
-  // buffer resource are wave-uniform (scalar registers, one table read).
+  // buffer resource are wave-uniform.  The table entries come in chunks of
+  // 64, one per lane of a register, read with v_readlane: a scalar load per
+  // entry put a memory round trip (and a full wait) on every stage's path.
   u32x4 kr[KL];
   u32x4 vr0 = {0u, 0u, 0u, 0u}, vr1 = {0u, 0u, 0u, 0u};
-  auto tile_rsrc = [&](const char* base, int b) __attribute__((always_inline)) {
+  int tbl = -1, tbl_base = -kWave;  // entries tbl_base .. tbl_base + 63 (-1 past the sequence)
+  auto table_entry = [&](int b) __attribute__((always_inline)) -> int {
     b = __builtin_amdgcn_readfirstlane(b);
-    const int blk = b < nblk ? trow[b] : -1;
+    const int base = b & ~(kWave - 1);
+    if (base != tbl_base) {  // wave-uniform; stages advance monotonically
+      tbl_base = base;
+      tbl = base + lane < nblk ? trow[base + lane] : -1;
+    }
+    return __builtin_amdgcn_readlane(tbl, b - base);
+  };
+  auto tile_rsrc = [&](const char* base, int blk) __attribute__((always_inline)) {
     const bool ok = unsigned(blk) < unsigned(p.num_blocks);
     return make_rsrc(base + (ok ? int64_t(blk) * blk_stride : 0), ok ? TILE : 0);
   };
+  // a block of the stage being loaded lies outside the pool (its keys are
+  // masked when the stage is computed)
+  bool bad_ld[2] = {false, false};
+  bool bad_c[2] = {false, false};  // the same flags of the stage being computed
   auto load_stage = [&](int st) __attribute__((always_inline)) {
+    const int ids[2] = {table_entry(st * 2), table_entry(st * 2 + 1)};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) bad_ld[b] = !(unsigned(ids[b]) < unsigned(p.num_blocks));
 #pragma unroll
     for (int i = 0; i < KL; ++i) {
       const int idx = tid + i * kPfThreads;
       const int tok = idx / CH, ch = idx - (idx / CH) * CH;
       const int wtok = (wave * kWave + i * kPfThreads) / CH;  // first token of this wave's rows
-      const auto rs = tile_rsrc(kbase, st * 2 + wtok / kBlockTokens);
+      const auto rs = tile_rsrc(kbase, ids[wtok / kBlockTokens]);
       kr[i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (tok % kBlockTokens) * ROWB + ch * 16, 0, 0));
     }
     if (wave * kWave < VPAIRS) {
       const int ch = tid % CH, tok = 2 * (tid / CH);
       const int wtok = 2 * (wave * kWave / CH);
-      const auto rs = tile_rsrc(vbase, st * 2 + wtok / kBlockTokens);
+      const auto rs = tile_rsrc(vbase, ids[wtok / kBlockTokens]);
       const int off = (tok % kBlockTokens) * ROWB + ch * 16;
       vr0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
       vr1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + ROWB, 0, 0));
@@ -315,14 +332,9 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
         for (int j = 0; j < RG; ++j) sa[j][blk] = mfma32<DT>(a, qb[j][kt], sa[j][blk]);
       }
     }
-    // blocks outside the pool contribute nothing (wave-uniform)
-    bool bad[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int b = st * 2 + blk;
-      const int id = b < nblk ? trow[b] : -1;
-      bad[blk] = !(unsigned(id) < unsigned(p.num_blocks));
-    }
+    // blocks outside the pool contribute nothing (wave-uniform; flags taken
+    // when the stage was loaded)
+    const bool bad[2] = {bad_c[0], bad_c[1]};
     const bool masked = st >= mask_from || bad[0] || bad[1];
     u32x4 pb[RG], pl[RG];
     float alpha[RG];
@@ -404,6 +416,8 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
     for (int st = 0; st < wg_stages; ++st) {
       const int buf = st & 1;
       const bool more = st + 1 < wg_stages;
+      bad_c[0] = bad_ld[0];
+      bad_c[1] = bad_ld[1];
       if (more) load_stage(st + 1);
       if (st < wave_stages) compute(buf, st);
       if (more) store_stage(buf ^ 1, st + 1);
@@ -418,6 +432,8 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
     for (int st = s_begin; st < s_end; ++st) {
       const int buf = st & 1;
       const bool more = st + 1 < s_end;
+      bad_c[0] = bad_ld[0];
+      bad_c[1] = bad_ld[1];
       if (more) load_stage(st + 1);
       if (st < wave_stages) compute(buf, st);
       if (more) store_stage(buf ^ 1, st + 1);
