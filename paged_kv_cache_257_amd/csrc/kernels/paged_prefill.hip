@@ -393,12 +393,18 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[j][dt] *= alpha[j];
     }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+    // V^T operands, each read one d-tile ahead of its products
+    auto vt_operand = [&](int dt) __attribute__((always_inline)) -> u32x4 {
       const uint16_t* vrow = &lv[buf][(dt * 16 + n) * VROW];
       const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + vt_col(dt * 16, 4 * g));
       const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + vt_col(dt * 16, 16 + 4 * g));
-      const u32x4 a = {a0.x, a0.y, a1.x, a1.y};
+      return u32x4{a0.x, a0.y, a1.x, a1.y};
+    };
+    u32x4 a_next = vt_operand(0);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const u32x4 a = a_next;
+      if (dt + 1 < NDT) a_next = vt_operand(dt + 1);
 #pragma unroll
       for (int j = 0; j < RG; ++j) {
         o[j][dt] = mfma32<DT>(a, pb[j], o[j][dt]);
