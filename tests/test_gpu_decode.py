@@ -98,20 +98,24 @@ def test_nan_filled_pool_does_not_leak(dtype):
         case.close()
 
 
-@pytest.mark.parametrize("cfg", CONFIGS[:3], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
 def test_fused_append_decode(cfg):
     """k_new/v_new path: the pool holds every token but each sequence's newest;
-    one launch stores the newest rows and attends over all of them."""
+    one launch stores the newest rows and attends over all of them (at the
+    bench's first partition size and at the one fill mode picks)."""
     print(f"\n[gpu] append-decode {cfg.name}", flush=True)
     case = DecodeCase(cfg, fill=float("nan"))
     try:
         case.write_context(skip_last=True)
         seqs = sample_seqs(case.lens, 12, cfg.seed)
         ref = {i: case.oracle_out(i) for i in seqs}
-        out, info = case.decode(PARTITIONS[cfg.name][0], append=True)
-        err = max(float(np.max(np.abs(out[i] - ref[i]))) for i in seqs)
-        print(f"[gpu] append-decode {cfg.name} max_err={err:.3e}", flush=True)
-        assert err <= TOL[cfg.dtype] and np.isfinite(out).all()
+        wpi, resident = case.pool.decode_occupancy(cfg.num_q_heads)
+        p_fill = fill_partition(case.lens, wpi, resident, 512) or default_partition_tokens()
+        for P in (PARTITIONS[cfg.name][0], p_fill):
+            out, info = case.decode(P, append=True)
+            err = max(float(np.max(np.abs(out[i] - ref[i]))) for i in seqs)
+            print(f"[gpu] append-decode {cfg.name} P={info.partition_tokens} max_err={err:.3e}", flush=True)
+            assert err <= TOL[cfg.dtype] and np.isfinite(out).all()
         # the newest rows landed in the pool: bit-exact everywhere a token lives
         kd, vd = device_bits(case.k_cache), device_bits(case.v_cache)
         km, vm = host_bits(case.oracle.mirror.k), host_bits(case.oracle.mirror.v)
