@@ -91,9 +91,9 @@ const char* pkv_last_error(void);
  * Host: pool and allocator
  * ------------------------------------------------------------------------ */
 
-/* Create a pool.  k_cache / v_cache are device arrays of the layout above
- * (may both be NULL for allocator-only use; device calls then fail with
- * PKV_E_BAD_ARG).  free_order (host, num_blocks ids, a permutation; NULL =
+/* Create a pool.  k_cache / v_cache are device arrays of the layout above,
+ * 16-byte aligned (may both be NULL for allocator-only use; device calls then
+ * fail with PKV_E_BAD_ARG).  free_order (host, num_blocks ids, a permutation; NULL =
  * 0..num_blocks-1) is the free list's initial content: the first block handed
  * out is free_order[0].  The free list is a stack: freed blocks are handed
  * out again most-recent first ([preview] step 4). */
@@ -635,7 +635,7 @@ pkv_status pkv_read_kv(const pkv_pool* pool, const int64_t* slot_mapping, int32_
  * from the pool through block_tables[i][j / block_size] and
  * g = h / (num_q_heads / num_kv_heads).  Paging does not change the result of
  * dense attention ([preview] "Lo que deberías llevarte", item 2).
- *   q:            device [num_seqs][num_q_heads][head_dim], pool dtype
+ *   q:            device [num_seqs][num_q_heads][head_dim], pool dtype, 16-byte aligned
  *   k_new, v_new: device [num_seqs][num_kv_heads][head_dim], pool dtype, or
  *                 both NULL.  When given, they are the K/V rows of each
  *                 sequence's newest token (position context_lens[i] - 1, the
@@ -643,12 +643,12 @@ pkv_status pkv_read_kv(const pkv_pool* pool, const int64_t* slot_mapping, int32_
  *                 them into the pool at that position and attends over them,
  *                 i.e. pkv_write_kv and decode in one launch.  Copy-on-write
  *                 copies of the same iteration must be enqueued before.
- *   out:          device float32 [num_seqs][num_q_heads][head_dim]
+ *   out:          device float32 [num_seqs][num_q_heads][head_dim], 4-byte aligned
  *   block_tables: device int32 [num_seqs][table_stride]
  *   context_lens: device int32 [num_seqs]; every entry >= 1 and equal to the
  *                 lengths given to pkv_decode_plan
  *   plan, info:   device copy of the plan and its host-side info
- *   workspace:    device, >= pkv_decode_workspace_bytes(info, ...) bytes.  Its
+ *   workspace:    device, 16-byte aligned, >= pkv_decode_workspace_bytes(info, ...) bytes.  Its
  *                 first bytes hold completion tickets: they must be zero
  *                 before the first call (allocate it zeroed) and every call
  *                 leaves them zero.  Calls that share a workspace must not
@@ -696,7 +696,8 @@ pkv_status pkv_paged_decode_reduce(const pkv_pool* pool, const void* q, const vo
  * the kernel reads through the block table, paragraph 5; long prefills are
  * sliced, the scheduler paragraph).  The chunk's K/V must already be in the
  * pool (pkv_seq_append / pkv_write_kv).  q: device [total_q][H_q][head_dim]
- * in the pool dtype; out: device fp32 [total_q][H_q][head_dim]; block_tables
+ * in the pool dtype; out: device fp32 [total_q][H_q][head_dim] (q, out and
+ * workspace 16-byte aligned, else PKV_E_BAD_ARG); block_tables
  * / context_lens as for decode; plan / info from pkv_prefill_plan (plan
  * uploaded); workspace (device, zeroed once, every launch leaves its
  * tickets zero) of at least pkv_prefill_workspace_bytes(info, head_dim)

@@ -17,6 +17,7 @@
 //   * every call is all-or-nothing: a dry run checks ids, table capacity and
 //     the number of free blocks first, then the state is changed.
 #include <algorithm>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -159,6 +160,8 @@ pkv_status pkv_pool_create(const pkv_pool_desc* desc, void* k_cache, void* v_cac
     return fail(PKV_E_BAD_ARG, "bad dtype");
   if ((k_cache == nullptr) != (v_cache == nullptr))
     return fail(PKV_E_BAD_ARG, "k_cache and v_cache must both be set or both be NULL");
+  if ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15)
+    return fail(PKV_E_BAD_ARG, "k_cache and v_cache must be 16-byte aligned (the kernels move 16-byte chunks)");
   std::vector<int32_t> order(d.num_blocks);
   if (free_order) {
     std::vector<char> seen(d.num_blocks, 0);

@@ -880,6 +880,9 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
   const size_t need = pkv_decode_workspace_bytes(info, num_q_heads, d.head_dim);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_E_BAD_ARG, "workspace too small: need " + std::to_string(need) + " bytes");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(workspace)) & 15 ||
+      reinterpret_cast<uintptr_t>(out) & 3)
+    return fail(PKV_E_BAD_ARG, "q and workspace must be 16-byte aligned and out 4-byte aligned");
   const int group = num_q_heads / d.num_kv_heads;
   mfma = mfma_eligible(group, d.dtype, d.head_dim);
   gw = heads_per_workgroup(group, mfma ? 16 : 8);

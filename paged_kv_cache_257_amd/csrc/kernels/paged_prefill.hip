@@ -619,6 +619,9 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, flo
   const size_t need = pkv_prefill_workspace_bytes(info, d.head_dim);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_E_BAD_ARG, "workspace too small: need " + std::to_string(need) + " bytes");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) |
+       reinterpret_cast<uintptr_t>(workspace)) & 15)
+    return fail(PKV_E_BAD_ARG, "q, out and workspace must be 16-byte aligned");
   prm.work = plan;
   prm.q_start = plan + 6 * int64_t(info->n_work);
   prm.split_tab = prm.q_start + num_seqs + 1;

@@ -53,3 +53,38 @@ def test_device_calls_refuse_a_pool_without_device_memory():
     st = lib.pkv_write_kv(h, None, None, None, 1, None)
     assert st == _capi.E_BAD_ARG and b"device" in lib.pkv_last_error()
     lib.pkv_pool_destroy(h)
+
+
+def test_misaligned_device_arrays_are_refused_before_any_launch():
+    """The kernels move 16-byte chunks: misaligned pools, q, out or workspaces are
+    refused with PKV_E_BAD_ARG before a launch.  Fake device addresses are
+    passed, so this runs only where no GPU is visible (nothing is launched or
+    dereferenced on the refusal paths it checks)."""
+    import numpy as np
+    import pytest
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("passes fake device addresses: CPU-only check")
+    lib = _capi.load(host_only=False)
+    desc = _capi.PoolDesc(4, 16, 1, 64, 4, 0)
+    h = ctypes.c_void_p()
+    assert lib.pkv_pool_create(ctypes.byref(desc), ctypes.c_void_p(0x10008), ctypes.c_void_p(0x20000),
+                               None, ctypes.byref(h)) == _capi.E_BAD_ARG
+    assert b"16-byte" in lib.pkv_last_error()
+    assert lib.pkv_pool_create(ctypes.byref(desc), ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000),
+                               None, ctypes.byref(h)) == 0
+    try:
+        lens = np.array([5], np.int32)
+        info = _capi.PlanInfo()
+        plan = np.zeros(16, np.int32)
+        assert lib.pkv_decode_plan(_capi.i32p(lens), 1, 16, 0, _capi.i32p(plan), 16, ctypes.byref(info)) == 0
+        V = ctypes.c_void_p
+        args = [h, V(0x30004), None, None, V(0x40000), 1, 1, V(0x50000), 1, V(0x60000), ctypes.c_float(0.125),
+                V(0x70000), ctypes.byref(info), V(0x80000), 1 << 20, None]
+        assert lib.pkv_paged_decode(*args) == _capi.E_BAD_ARG  # q misaligned
+        assert b"aligned" in lib.pkv_last_error()
+        args[1], args[13] = V(0x30000), V(0x80008)
+        assert lib.pkv_paged_decode(*args) == _capi.E_BAD_ARG  # workspace misaligned
+        assert b"aligned" in lib.pkv_last_error()
+    finally:
+        lib.pkv_pool_destroy(h)
