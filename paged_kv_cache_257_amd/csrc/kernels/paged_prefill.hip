@@ -400,11 +400,15 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
       const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + vt_col(dt * 16, 16 + 4 * g));
       return u32x4{a0.x, a0.y, a1.x, a1.y};
     };
-    u32x4 a_next = vt_operand(0);
+    // (two ahead where the registers allow: fp16 without split records)
+    constexpr int AHEAD = (DT == PKV_F16 && !SPLIT) ? 2 : 1;
+    u32x4 a_q[AHEAD];
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) a_q[i] = vt_operand(i);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const u32x4 a = a_next;
-      if (dt + 1 < NDT) a_next = vt_operand(dt + 1);
+      const u32x4 a = a_q[dt % AHEAD];
+      if (dt + AHEAD < NDT) a_q[dt % AHEAD] = vt_operand(dt + AHEAD);
 #pragma unroll
       for (int j = 0; j < RG; ++j) {
         o[j][dt] = mfma32<DT>(a, pb[j], o[j][dt]);
