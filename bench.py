@@ -43,7 +43,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 METRIC = "paged-decode achieved HBM GB/s (% of peak) + decode tokens/s, 64-seq fp16 batch"
 KERNEL_SOURCES = ("paged_kv_cache_257_amd/csrc/kernels/paged_decode.hip",
-                  "paged_kv_cache_257_amd/csrc/kernels/device_common.h")
+                  "paged_kv_cache_257_amd/csrc/kernels/device_common.h",
+                  "paged_kv_cache_257_amd/csrc/kernels/mfma_common.h")
 COUNTER_SUMMARY = "profiles/paged_decode_gpt_f16_counters.txt"
 
 
@@ -66,7 +67,8 @@ def kernel_source_sha() -> str:
 
 
 PREFILL_SOURCES = ("paged_kv_cache_257_amd/csrc/kernels/paged_prefill.hip",
-                   "paged_kv_cache_257_amd/csrc/kernels/device_common.h")
+                   "paged_kv_cache_257_amd/csrc/kernels/device_common.h",
+                   "paged_kv_cache_257_amd/csrc/kernels/mfma_common.h")
 
 
 def _sources_sha(paths) -> str:

@@ -55,6 +55,7 @@
 
 #include "decode_launch.h"
 #include "device_common.h"
+#include "mfma_common.h"
 
 namespace pkv {
 namespace {
@@ -436,53 +437,11 @@ __global__ __launch_bounds__(kWave* NW, (decode_waves_hint<DT, D, GW>())) void p
 //    into the registers of the tile (the pool slot may still be being
 //    written by this launch), and the first head group stores it.
 // The partition's states then merge and combine as in the VALU kernel.
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef float f2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-typedef short s4 __attribute__((ext_vector_type(4)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef __bf16 b8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kNegBig = -3.0e38f;  // finite "no token yet" running maximum
-
-template <int DT>
-__device__ __forceinline__ f4 mfma_k32(const u32x4& a, const u32x4& b, const f4& c) {
-  if constexpr (DT == PKV_F16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0,
-                                                  0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c,
-                                                   0, 0, 0);
-}
-
-template <int DT>
-__device__ __forceinline__ f4 mfma_k16(const u32x2& a, const u32x2& b, const f4& c) {
-  if constexpr (DT == PKV_F16)
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, b), c, 0, 0,
-                                                 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c,
-                                                     0, 0, 0);
-}
-
 // A streamed 16-byte tile load (nontemporal, as load_stream) whose
 // wave-uniform part of the offset sits in a scalar register, so that one
 // vector offset serves all loads of a tile.
 __device__ __forceinline__ u32x4 load_stream_s(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, kCachePolicyNT));
-}
-
-// Maximum over the four lanes n, n + 16, n + 32, n + 48 of a column: a
-// swap of a register with itself leaves each lane its own value and its
-// partner's (16 lanes away for permlane16, 32 for permlane32).
-__device__ __forceinline__ float max_over_lane_groups(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(f_bits(x), f_bits(x), false, false);
-  x = fmaxf(bits_f(a[0]), bits_f(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
-  return fmaxf(bits_f(b[0]), bits_f(b[1]));
 }
 
 template <int DT, int GW, int NW>

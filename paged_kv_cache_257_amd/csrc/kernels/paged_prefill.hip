@@ -43,25 +43,16 @@
 // than 2^8 in weight, and the accumulators are rescaled only in stages where
 // some row's maximum moved (a wave-wide vote); otherwise the factor is
 // exactly 1.
-#include "device_common.h"
+#include "mfma_common.h"
 
 namespace pkv {
 namespace {
-
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef __bf16 b8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPfWaves = 4;
 constexpr int kPfRowGroups = kPrefillTileRows / (16 * kPfWaves);  // 16-row groups per wave
 constexpr int kPfThreads = kWave * kPfWaves;
 constexpr int kStage = 32;  // key tokens per stage (two blocks)
 constexpr float kLog2eF = 1.4426950408889634f;
-constexpr float kNegBig = -3.0e38f;  // finite "no key yet" running max
 // Slack of the running maximum, in base-2 units: a row's maximum is raised
 // (and its accumulators rescaled) only when a score exceeds it by more than
 // this, so after the first keys of a long context the rescale almost never
@@ -94,21 +85,6 @@ struct PrefillParams {
   float scale_log2;
 };
 
-template <int DT>
-__device__ __forceinline__ f4 mfma32(const u32x4& a, const u32x4& b, const f4& c);
-
-template <>
-__device__ __forceinline__ f4 mfma32<PKV_F16>(const u32x4& a, const u32x4& b, const f4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b),
-                                                c, 0, 0, 0);
-}
-
-template <>
-__device__ __forceinline__ f4 mfma32<PKV_BF16>(const u32x4& a, const u32x4& b, const f4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b),
-                                                 c, 0, 0, 0);
-}
-
 // 16-byte store / load at device scope: cache policy sc1, the coherence
 // level the compiler gives relaxed agent-scope atomics (which it emits as
 // 4-byte sc1 accesses), so records written this way are read by a
@@ -120,20 +96,6 @@ __device__ __forceinline__ void store_device(__amdgpu_buffer_rsrc_t r, int offse
 }
 __device__ __forceinline__ f4 load_device(__amdgpu_buffer_rsrc_t r, int offset) {
   return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, kCachePolicyDevice));
-}
-
-// Maximum over the four lanes n, n + 16, n + 32, n + 48 (one query row's
-// accumulator lanes), with gfx950's lane swaps instead of LDS permutes: a
-// swap of a register with itself leaves, in the two results, each lane's
-// own value and its partner's (16 lanes away for permlane16, 32 for
-// permlane32).
-__device__ __forceinline__ float max_over_columns(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
-                                                  __builtin_bit_cast(uint32_t, x), false, false);
-  x = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                                  __builtin_bit_cast(uint32_t, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
 }
 
 // Three waves per SIMD: the compiler then keeps the accumulators in the
@@ -329,7 +291,7 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
       for (int kt = 0; kt < KT; ++kt) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(&lk[buf][(blk * 16 + n) * KROW + 32 * kt + 8 * g]);
 #pragma unroll
-        for (int j = 0; j < RG; ++j) sa[j][blk] = mfma32<DT>(a, qb[j][kt], sa[j][blk]);
+        for (int j = 0; j < RG; ++j) sa[j][blk] = mfma_k32<DT>(a, qb[j][kt], sa[j][blk]);
       }
     }
     // blocks outside the pool contribute nothing (wave-uniform; flags taken
@@ -358,7 +320,7 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
       float mx = s[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-      mx = max_over_columns(mx);
+      mx = max_over_lane_groups(mx);
       // the running maximum moves only when a score exceeds it by more than
       // kRescaleSlack (weights stay <= 2^kRescaleSlack in between)
       const float mxs = mx * c2;
@@ -411,8 +373,8 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
       if (dt + AHEAD < NDT) a_q[dt % AHEAD] = vt_operand(dt + AHEAD);
 #pragma unroll
       for (int j = 0; j < RG; ++j) {
-        o[j][dt] = mfma32<DT>(a, pb[j], o[j][dt]);
-        if constexpr (DT == PKV_BF16) o[j][dt] = mfma32<DT>(a, pl[j], o[j][dt]);
+        o[j][dt] = mfma_k32<DT>(a, pb[j], o[j][dt]);
+        if constexpr (DT == PKV_BF16) o[j][dt] = mfma_k32<DT>(a, pl[j], o[j][dt]);
       }
     }
   };
