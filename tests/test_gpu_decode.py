@@ -22,7 +22,7 @@ import torch
 
 from paged_kv_cache_257_amd import default_partition_tokens, fill_partition
 from tests.gpu_helpers import TOL, DecodeCase, device_bits, host_bits, sync, to_device
-from workloads import CONFIGS, draw_normal_storage
+from workloads import CONFIGS, config_by_name, draw_normal_storage
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -84,7 +84,7 @@ def test_workload_parity(cfg):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_nan_filled_pool_does_not_leak(dtype):
-    cfg = dataclasses.replace(CONFIGS[0], dtype=dtype, index=20, head_dim=128 if dtype != "f32" else 64)
+    cfg = dataclasses.replace(config_by_name("tiny_f32"), dtype=dtype, index=20, head_dim=128 if dtype != "f32" else 64)
     lens = [1, 5, 16, 17, 31, 33, 60]
     order = np.random.default_rng(7).permutation(40)
     case = DecodeCase(cfg, lens=lens, num_blocks=40, free_order=order, fill=float("nan"))
@@ -131,7 +131,7 @@ def test_fused_append_decode(cfg):
 def test_fused_append_decode_gqa_groups(group, q_heads):
     """Several workgroups (query-head groups) read the same new row; one stores it."""
     kv = q_heads // group
-    cfg = dataclasses.replace(CONFIGS[2], name="append_gqa", index=40 + group, num_kv_heads=kv,
+    cfg = dataclasses.replace(config_by_name("ragged_bf16"), name="append_gqa", index=40 + group, num_kv_heads=kv,
                               num_q_heads=kv * group, dtype="bf16")
     lens = [1, 2, 16, 17, 31, 100, 513, 700]
     nb = sum(-(-L // 16) for L in lens) + 2
@@ -159,7 +159,7 @@ SWEEP = [(dt, d, hkv, g) for dt in ("f32", "f16", "bf16") for d in (64, 128, 256
 @pytest.mark.parametrize("dtype,head_dim,kv_heads,group", SWEEP)
 def test_shape_sweep(dtype, head_dim, kv_heads, group):
     idx = 100 + SWEEP.index((dtype, head_dim, kv_heads, group))
-    cfg = dataclasses.replace(CONFIGS[0], name="sweep", index=idx, dtype=dtype, head_dim=head_dim,
+    cfg = dataclasses.replace(config_by_name("tiny_f32"), name="sweep", index=idx, dtype=dtype, head_dim=head_dim,
                               num_kv_heads=kv_heads, num_q_heads=kv_heads * group, num_seqs=9)
     lens = [1, 15, 16, 17, 47, 64, 100, 129, 300]
     nb = sum(-(-L // 16) for L in lens) + 5
@@ -178,7 +178,7 @@ def test_shape_sweep(dtype, head_dim, kv_heads, group):
 
 
 def test_copy_blocks_bit_exact():
-    cfg = dataclasses.replace(CONFIGS[1], index=30, num_seqs=1)
+    cfg = dataclasses.replace(config_by_name("gpt_f16"), index=30, num_seqs=1)
     nb, H, d = 64, cfg.num_kv_heads, cfg.head_dim
     case = DecodeCase(cfg, lens=[nb * 16], num_blocks=nb, free_order=np.arange(nb))
     try:
@@ -196,7 +196,7 @@ def test_copy_blocks_bit_exact():
 
 
 def test_write_kv_skips_negative_and_out_of_pool_slots():
-    cfg = dataclasses.replace(CONFIGS[0], index=31)
+    cfg = dataclasses.replace(config_by_name("tiny_f32"), index=31)
     case = DecodeCase(cfg, lens=[32], num_blocks=4, free_order=np.arange(4))
     try:
         case.write_context()
@@ -219,7 +219,7 @@ def test_workspace_shared_by_launches_of_different_shapes():
     workspace's start and tickets sit at its end, so neither launch sees the
     other's leftovers."""
     from paged_kv_cache_257_amd import decode_workspace_bound
-    base = dataclasses.replace(CONFIGS[1], name="shared_ws", index=60, dtype="bf16", num_kv_heads=8,
+    base = dataclasses.replace(config_by_name("gpt_f16"), name="shared_ws", index=60, dtype="bf16", num_kv_heads=8,
                                num_q_heads=32)
     long_lens = [3000, 2500]
     short_lens = [int(x) for x in np.random.default_rng(60).integers(100, 2500, size=40)]
@@ -253,7 +253,7 @@ def test_gqa_both_kernels(dtype, group, monkeypatch):
     default; PKV_DECODE_MFMA=0 selects the VALU kernel.  Both against the
     oracle, with and without the fused append, split and unsplit."""
     idx = 300 + 10 * group + (dtype == "bf16")
-    cfg = dataclasses.replace(CONFIGS[0], name="gqa_kernels", index=idx, dtype=dtype, head_dim=128,
+    cfg = dataclasses.replace(config_by_name("tiny_f32"), name="gqa_kernels", index=idx, dtype=dtype, head_dim=128,
                               num_kv_heads=2, num_q_heads=2 * group, num_seqs=10)
     lens = [1, 2, 15, 16, 17, 33, 100, 257, 600, 1111]
     nb = sum(-(-L // 16) for L in lens) + 3

@@ -16,7 +16,7 @@ import pytest
 
 from oracle.allocator import AllocError, OracleAllocator
 from oracle.kvcache import DenseShadow, MirrorPool
-from workloads import CONFIGS
+from workloads import config_by_name
 from workloads.configs import draw_decode_shapes
 from tests.alloc_harness import OracleAdapter, check_invariants, load_trace, run_trace
 
@@ -29,7 +29,7 @@ def test_hand_worked_trace(golden_dir):
 
 
 def test_tiny_workload_block_counts_and_waste():
-    cfg = CONFIGS[0]
+    cfg = config_by_name("tiny_f32")
     sh = draw_decode_shapes(cfg)
     a = OracleAllocator(sh.num_blocks, 16, 8, sh.free_order)
     ids = [a.alloc(int(L))[0] for L in sh.lens]

@@ -22,7 +22,7 @@ from oracle.attention import (combine_partials, decode_attention, decode_partial
                               storage_to_f64)
 from oracle.kvcache import DenseShadow
 from oracle.runs import DecodeRun
-from workloads import CONFIGS, draw_decode_values
+from workloads import config_by_name, draw_decode_values
 from workloads.configs import draw_decode_shapes
 
 
@@ -40,7 +40,7 @@ def sdpa64(q, K, V, scale):
 
 
 def tiny_run():
-    cfg = CONFIGS[0]
+    cfg = config_by_name("tiny_f32")
     sh = draw_decode_shapes(cfg)
     vals = draw_decode_values(cfg, sh.lens)
     q, k, v = vals["q"], vals["k"], vals["v"]

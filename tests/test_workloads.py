@@ -2,19 +2,19 @@
 
 import numpy as np
 
-from workloads import CONFIGS, draw_normal_storage, storage_from_f32
+from workloads import config_by_name, draw_normal_storage, storage_from_f32
 from workloads.churn import choose_churn, draw_prefix_shared_plan
 from workloads.configs import PREFIX_SHARED, draw_decode_shapes
 
 
 def test_tiny_config_shapes():
-    sh = draw_decode_shapes(CONFIGS[0])
+    sh = draw_decode_shapes(config_by_name("tiny_f32"))
     assert list(sh.lens) == [5, 17, 33, 60]
     assert sh.num_blocks == 32 and sorted(sh.free_order) == list(range(32))
 
 
 def test_gpt_lengths_range_and_pool():
-    cfg = CONFIGS[1]
+    cfg = config_by_name("gpt_f16")
     sh = draw_decode_shapes(cfg)
     assert len(sh.lens) == 64 and sh.lens.min() >= 1 and sh.lens.max() <= 2048
     need = sum(-(-int(L) // 16) for L in sh.lens)
@@ -23,7 +23,7 @@ def test_gpt_lengths_range_and_pool():
 
 
 def test_ragged_lengths_include_pinned_values():
-    sh = draw_decode_shapes(CONFIGS[2])
+    sh = draw_decode_shapes(config_by_name("ragged_bf16"))
     assert len(sh.lens) == 96
     for v in (60, 200, 1500):
         assert v in sh.lens
@@ -31,7 +31,7 @@ def test_ragged_lengths_include_pinned_values():
 
 
 def test_gqa_config():
-    cfg = CONFIGS[3]
+    cfg = config_by_name("gqa_long_bf16")
     sh = draw_decode_shapes(cfg)
     assert list(sh.lens) == [32768] * 10 and cfg.group == 4
     assert cfg.num_kv_heads * cfg.head_dim * 2 * 2 == 4096  # 4 KiB K+V per token
