@@ -532,7 +532,7 @@ def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode path is not sharded across GPUs in this build)", file=sys.stderr)
+              "(the decode path runs on one GPU; it is not sharded across GPUs)", file=sys.stderr)
         return 2
     import numpy as np
     import torch
