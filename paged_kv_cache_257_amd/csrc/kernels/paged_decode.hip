@@ -686,21 +686,25 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const ReducePara
 
 using DecodeFn = void (*)(const DecodeParams);
 
+// The pickers take the requested waves per workgroup in nw and leave there
+// the waves of the instance they return (an instance may not exist for every
+// request): the launch's block size must be that instance's.
 template <int DT, int D, int GW>
-DecodeFn pick_waves(int nw) {
+DecodeFn pick_waves(int& nw) {
   switch (nw) {
     case 1: return paged_decode_kernel<DT, D, GW, 1>;
     case 2: return paged_decode_kernel<DT, D, GW, 2>;
     case 4: return paged_decode_kernel<DT, D, GW, 4>;
     case 8:  // 512 threads; its LDS merge area fits 64 KiB for GW <= 2 only
       if constexpr (GW <= 2) return paged_decode_kernel<DT, D, GW, 8>;
+      nw = 4;
       return paged_decode_kernel<DT, D, GW, 4>;
     default: return nullptr;
   }
 }
 
 template <int DT, int D>
-DecodeFn pick_gw(int gw, int nw) {
+DecodeFn pick_gw(int gw, int& nw) {
   switch (gw) {
     case 1: return pick_waves<DT, D, 1>(nw);
     case 2: return pick_waves<DT, D, 2>(nw);
@@ -711,7 +715,7 @@ DecodeFn pick_gw(int gw, int nw) {
 }
 
 template <int DT>
-DecodeFn pick_d(int d, int gw, int nw) {
+DecodeFn pick_d(int d, int gw, int& nw) {
   switch (d) {
     case 64: return pick_gw<DT, 64>(gw, nw);
     case 128: return pick_gw<DT, 128>(gw, nw);
@@ -720,7 +724,7 @@ DecodeFn pick_d(int d, int gw, int nw) {
   }
 }
 
-DecodeFn pick_decode(int dt, int d, int gw, int nw) {
+DecodeFn pick_decode(int dt, int d, int gw, int& nw) {
   switch (dt) {
     case PKV_F32: return pick_d<PKV_F32>(d, gw, nw);
     case PKV_F16: return pick_d<PKV_F16>(d, gw, nw);
@@ -730,20 +734,21 @@ DecodeFn pick_decode(int dt, int d, int gw, int nw) {
 }
 
 template <int DT, int GW>
-DecodeFn pick_mfma_waves(int nw) {
+DecodeFn pick_mfma_waves(int& nw) {
   switch (nw) {
     case 1: return paged_decode_mfma_kernel<DT, GW, 1>;
     case 2: return paged_decode_mfma_kernel<DT, GW, 2>;
     case 4: return paged_decode_mfma_kernel<DT, GW, 4>;
     case 8:  // its LDS merge area fits 32 KiB for GW <= 8
       if constexpr (GW <= 8) return paged_decode_mfma_kernel<DT, GW, 8>;
+      nw = 4;
       return paged_decode_mfma_kernel<DT, GW, 4>;
     default: return nullptr;
   }
 }
 
 template <int DT>
-DecodeFn pick_mfma_gw(int gw, int nw) {
+DecodeFn pick_mfma_gw(int gw, int& nw) {
   switch (gw) {
     case 2: return pick_mfma_waves<DT, 2>(nw);
     case 4: return pick_mfma_waves<DT, 4>(nw);
@@ -753,7 +758,7 @@ DecodeFn pick_mfma_gw(int gw, int nw) {
   }
 }
 
-DecodeFn pick_mfma(int dt, int gw, int nw) {
+DecodeFn pick_mfma(int dt, int gw, int& nw) {
   switch (dt) {
     case PKV_F16: return pick_mfma_gw<PKV_F16>(gw, nw);
     case PKV_BF16: return pick_mfma_gw<PKV_BF16>(gw, nw);
@@ -762,15 +767,14 @@ DecodeFn pick_mfma(int dt, int gw, int nw) {
 }
 
 // Waves per workgroup (they split a partition's blocks): 4 by default, the
-// best of {1, 2, 4} x partition {128, 256, 512} on the GPT-style fp16 batch;
-// PKV_DECODE_WAVES overrides it for tuning sweeps.
+// best of {1, 2, 4, 8} on the GPT-style fp16 batch; PKV_DECODE_WAVES
+// overrides it for tuning sweeps.  The tuning variables are read at every
+// launch (a lookup in the environment, next to a launch of tens of
+// microseconds), so one process can run every variant.
 int waves_per_item() {
-  static const int nw = [] {
-    const char* s = std::getenv("PKV_DECODE_WAVES");
-    int v = s ? std::atoi(s) : 0;
-    return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 4;
-  }();
-  return nw;
+  const char* s = std::getenv("PKV_DECODE_WAVES");
+  const int v = s ? std::atoi(s) : 0;
+  return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 4;
 }
 
 // Query heads of one KV head that one workgroup takes (GW): all of them,
@@ -779,11 +783,9 @@ int waves_per_item() {
 // nontemporal loads keep no copy in L2 for the others; measured 1.45x
 // slower for GQA-4 split in two).  PKV_DECODE_GW caps it for tuning sweeps.
 int heads_per_workgroup(int group, int limit) {
-  static const int cap = [] {
-    const char* s = std::getenv("PKV_DECODE_GW");
-    const int v = s ? std::atoi(s) : 0;
-    return (v == 1 || v == 2 || v == 4 || v == 8 || v == 16) ? v : 16;
-  }();
+  const char* s = std::getenv("PKV_DECODE_GW");
+  const int v = s ? std::atoi(s) : 0;
+  const int cap = (v == 1 || v == 2 || v == 4 || v == 8 || v == 16) ? v : 16;
   limit = std::min(limit, cap);
   int gw = 1;
   while (gw < limit && group % (2 * gw) == 0) gw *= 2;
@@ -888,7 +890,7 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
 pkv_status launch_partitions(const pkv_pool* pool, const DecodeParams& prm, int gw, bool mfma,
                              const pkv_decode_plan_info* info, hipStream_t s,
                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
-  const int nw = waves_per_item();
+  int nw = waves_per_item();  // becomes the chosen instance's waves
   DecodeFn fn = mfma ? pick_mfma(pool->desc.dtype, gw, nw) : pick_decode(pool->desc.dtype, pool->desc.head_dim, gw, nw);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group");
   const int64_t grid = int64_t(info->n_work) * prm.num_kv_heads * prm.hgroups_per_kv;
@@ -950,7 +952,7 @@ extern "C" pkv_status pkv_decode_occupancy(const pkv_pool* pool, int32_t num_q_h
   bool mfma = mfma_eligible(group, d.dtype, d.head_dim);
   const int gw = heads_per_workgroup(group, mfma ? 16 : 8);
   if (gw < 2) mfma = false;
-  const int nw = waves_per_item();
+  int nw = waves_per_item();  // becomes the chosen instance's waves
   DecodeFn fn = mfma ? pick_mfma(d.dtype, gw, nw) : pick_decode(d.dtype, d.head_dim, gw, nw);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group");
   int per_cu = 0, dev = 0, cus = 0;

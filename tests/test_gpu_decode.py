@@ -274,3 +274,35 @@ def test_gqa_both_kernels(dtype, group, monkeypatch):
                     assert case.last_tickets_zero
     finally:
         case.close()
+
+
+@pytest.mark.parametrize("dtype,group", [("f16", 1), ("bf16", 1), ("f32", 2), ("bf16", 4), ("f16", 8)])
+def test_tuning_variants(dtype, group, monkeypatch):
+    """Every decode variant the tuning variables reach (waves per workgroup
+    1/2/4/8, query heads per workgroup capped at 1/2/4, either kernel for
+    grouped queries) against the oracle, with the fused append, split and
+    unsplit: they are read at every launch."""
+    idx = 400 + 10 * group + {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+    d = 64 if dtype == "f32" else 128
+    cfg = dataclasses.replace(config_by_name("tiny_f32"), name="tuning", index=idx, dtype=dtype, head_dim=d,
+                              num_kv_heads=2, num_q_heads=2 * group, num_seqs=7)
+    lens = [1, 16, 17, 40, 129, 300, 700]
+    nb = sum(-(-L // 16) for L in lens) + 3
+    case = DecodeCase(cfg, lens=lens, num_blocks=nb, free_order=np.random.default_rng(idx).permutation(nb),
+                      fill=float("nan"))
+    try:
+        case.write_context(skip_last=True)
+        for waves in ("1", "2", "4", "8"):
+            for cap in ("16", "2", "1"):
+                for mfma in ("1", "0"):
+                    monkeypatch.setenv("PKV_DECODE_WAVES", waves)
+                    monkeypatch.setenv("PKV_DECODE_GW", cap)
+                    monkeypatch.setenv("PKV_DECODE_MFMA", mfma)
+                    for P in (64, 0):
+                        out, _ = case.decode(P, split=(P == 64 and waves == "2"), append=True)
+                        err = max_err(case, out, range(len(lens)))
+                        assert np.isfinite(out).all(), (waves, cap, mfma, P)
+                        assert err <= TOL[dtype], (waves, cap, mfma, P, err)
+                        assert case.last_tickets_zero
+    finally:
+        case.close()
