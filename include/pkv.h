@@ -551,10 +551,12 @@ pkv_status pkv_prepare_decode(pkv_pool* pool, const int32_t* seqs, int32_t n_seq
  * pinned host memory (staging_host) and in device memory (staging_dev), the
  * decode workspace (zeroed before first use, pkv_decode_workspace_bytes for
  * the largest batch) and a copy stream (NULL: uploads go on the compute
- * stream).  The stepper creates PKV_STEPPER_SLOTS + 2 HIP events and nothing
- * else.  The compute stream never waits on another stream; the host waits
- * for each upload before launching, and for the iterations that last used a
- * slot before rewriting it (one completion event per group of four slots).
+ * stream).  The stepper creates two HIP events (one completion event per
+ * group of four slots) and nothing else.  The compute stream never waits on
+ * another stream; the host waits for each upload before launching (it
+ * synchronises the copy stream, so give each stepper a copy stream of its
+ * own or one that carries nothing slow), and for the iterations that last
+ * used a slot before rewriting it.
  * All calls on one stepper must use the same compute stream.
  * partition_tokens: a concrete size, 0 (the default) or PKV_PARTITION_FILL
  * (re-chosen at every iteration from the batch's lengths after the append;
