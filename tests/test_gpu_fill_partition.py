@@ -8,6 +8,8 @@ the append, and the outputs of the appending decode match the oracle over
 the same logical tokens (max |err| <= 2e-3, fp32 accumulation).  One batch
 where the rule picks a size (grouped queries, a few long sequences) and one
 where nothing fits and the default is kept (many short MHA sequences).
+Each batch runs with the upload on a copy stream of its own and, without
+one, on the compute stream.
 """
 
 import dataclasses
@@ -35,8 +37,9 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("pipelined", [True, False], ids=["copy_stream", "compute_stream"])
 @pytest.mark.parametrize("name", sorted(CASES))
-def test_stepper_fill_mode(name):
+def test_stepper_fill_mode(name, pipelined):
     over, lens = CASES[name]
     lens = np.asarray(lens, dtype=np.int64)
     cfg = dataclasses.replace(config_by_name("gpt_f16"), name="fill_" + name, index=500 + len(name), head_dim=128,
@@ -63,8 +66,9 @@ def test_stepper_fill_mode(name):
         wpi, resident = pool.decode_occupancy(Hq)
         assert wpi >= 1 and resident >= 1
         want = fill_partition(lens, wpi, resident, 512) or default_partition_tokens()
-        print(f"\n[gpu] fill {name}: workgroups/item={wpi} resident={resident} -> P={want}", flush=True)
-        step = DecodeIteration(pool, len(lens), stride, Hq, PARTITION_FILL)
+        print(f"\n[gpu] fill {name} pipelined={pipelined}: workgroups/item={wpi} resident={resident} "
+              f"-> P={want}", flush=True)
+        step = DecodeIteration(pool, len(lens), stride, Hq, PARTITION_FILL, pipelined=pipelined)
         out = torch.full((len(lens), Hq, d), float("nan"), dtype=torch.float32, device="cuda")
         meta = step.step(list(range(len(lens))), to_device(vals["q"], dt), out,
                          to_device(np.ascontiguousarray(vals["k"][last]), dt),
