@@ -317,7 +317,8 @@ def bench_prefix_shared(args, cfg):
     def iteration(it):
         seqs = np.asarray([x for x in pool.live() if x != root], dtype=np.int32)
         q, k, v = vals[it % 4]
-        step.step(seqs, q, out, k, v, cfg.scale, events=ev[it] if it % args.time_every == 0 else None)
+        lay = step.step(seqs, q, out, k, v, cfg.scale, events=ev[it] if it % args.time_every == 0 else None)
+        loads.append(lay.plan.shared_kv)
         retire, parents = choose_churn(cfg, it, seqs.tolist())
         for x in retire:
             pool.free(x)
@@ -325,6 +326,7 @@ def bench_prefix_shared(args, cfg):
             pool.fork(x)
         return len(seqs)
 
+    loads = []  # the plan's load-policy hint of every iteration
     for it in range(warm):
         iteration(it)
     torch.cuda.synchronize()
@@ -355,7 +357,9 @@ def bench_prefix_shared(args, cfg):
         "config": {"workload": cfg.name, "num_seqs": cfg.num_seqs, "num_q_heads": Hq, "num_kv_heads": H,
                    "head_dim": d, "block_size": 16, "prefix_len": cfg.prefix_len,
                    "tail_max": cfg.tail_max, "churn_per_iteration": cfg.churn,
-                   "step": "append + copy-on-write + decode (new K/V stored inside) + retire/admit"},
+                   "step": "append + copy-on-write + decode (new K/V stored inside) + retire/admit",
+                   "kv_loads": "cached" if all(loads[warm:]) else
+                   "streaming" if not any(loads[warm:]) else "mixed"},
         "physical_GBps": round(physical / wall / 1e9, 2),
         "pct_of_hbm_peak_physical": round(100 * physical / wall / 1e9 / HBM_PEAK_GBPS, 2),
         "iteration_tokens_per_s": round(decoded / wall, 1),
@@ -671,6 +675,7 @@ def main(argv=None):
                    "mean_context_timed": round(timed_ctx, 1),
                    "max_context": int(sh.lens.max()), "partition_tokens": info.partition_tokens,
                    "partition_mode": {-1: "fill", 0: "default"}.get(partition, "fixed"),
+                   "kv_loads": "cached" if info.shared_kv else "streaming",
                    "work_items": info.n_work, "replicas": args.replicas,
                    "decode_launches": 2 if args.two_launch else 1,
                    "new_kv_store": "write_kv" if args.separate_write else "in decode",

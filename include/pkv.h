@@ -400,6 +400,15 @@ typedef struct {
   int32_t n_partials;
   int32_t plan_ints;
   int32_t max_context_len;
+  /* K/V load policy hint, read by pkv_paged_decode: 0 (what pkv_decode_plan
+   * sets) streams the tiles past the caches (nontemporal loads, the faster
+   * choice when every tile is read once); 1 reads them through the caches
+   * (4 waves per workgroup), for batches whose sequences share blocks, so
+   * that the repeated reads of a shared prefix hit in L2.
+   * pkv_prepare_decode sets 1 when at least a quarter of the batch's
+   * context tokens lie in blocks held by more than one sequence.  Any value
+   * gives the same results. */
+  int32_t shared_kv;
 } pkv_decode_plan_info;
 
 /* Upper bound of the plan length for these lengths. */

@@ -35,7 +35,8 @@ class Stats(C.Structure):
 
 class PlanInfo(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("num_seqs", "block_size", "partition_tokens", "n_work",
-                                         "n_reduce", "n_partials", "plan_ints", "max_context_len")]
+                                         "n_reduce", "n_partials", "plan_ints", "max_context_len",
+                                         "shared_kv")]
 
 
 class PrefillPlanInfo(C.Structure):

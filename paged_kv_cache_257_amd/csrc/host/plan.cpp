@@ -126,6 +126,7 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
   info->n_partials = n_partials;
   info->plan_ints = int32_t(need);
   info->max_context_len = max_len;
+  info->shared_kv = 0;
   return PKV_OK;
 }
 

@@ -182,7 +182,21 @@ constexpr int decode_waves_hint() {
   return 1;
 }
 
-template <int DT, int D, int GW, int NW>
+// Cache policy of the K/V tile loads.  Tiles that one launch reads once go
+// nontemporal (kCacheStream, as load_stream): that raises the rate of the
+// scattered tile reads.  When sequences of the batch share blocks (forked
+// prefixes), many workgroups read the same tiles at about the same time and
+// ordinary loads (kCacheReuse) let L2 serve the repeats; the nontemporal
+// policy evicts those lines first, and every repeat goes back to the fabric.
+constexpr int kCacheStream = kCachePolicyNT;
+constexpr int kCacheReuse = 0;
+
+template <int CP>
+__device__ __forceinline__ u32x4 load_tile(__amdgpu_buffer_rsrc_t r, int offset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, CP));
+}
+
+template <int DT, int D, int GW, int NW, int CP = kCacheStream>
 __global__ __launch_bounds__(kWave* NW, (decode_waves_hint<DT, D, GW>())) void paged_decode_kernel(
     const DecodeParams p) {
   constexpr int E = ElemBytes<DT>::value;
@@ -249,9 +263,9 @@ __global__ __launch_bounds__(kWave* NW, (decode_waves_hint<DT, D, GW>())) void p
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_cache + tile, ok ? TILE : 0);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_cache + tile, ok ? TILE : 0);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kk[i] = load_stream(rk, lane * 16 + i * 1024);
+    for (int i = 0; i < NI; ++i) kk[i] = load_tile<CP>(rk, lane * 16 + i * 1024);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vv[i] = load_stream(rv, lane * 16 + i * 1024);
+    for (int i = 0; i < NI; ++i) vv[i] = load_tile<CP>(rv, lane * 16 + i * 1024);
     return j < ce ? blk : -1;
   };
 
@@ -437,14 +451,15 @@ __global__ __launch_bounds__(kWave* NW, (decode_waves_hint<DT, D, GW>())) void p
 //    into the registers of the tile (the pool slot may still be being
 //    written by this launch), and the first head group stores it.
 // The partition's states then merge and combine as in the VALU kernel.
-// A streamed 16-byte tile load (nontemporal, as load_stream) whose
-// wave-uniform part of the offset sits in a scalar register, so that one
-// vector offset serves all loads of a tile.
-__device__ __forceinline__ u32x4 load_stream_s(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, kCachePolicyNT));
+// A 16-byte tile load (cache policy CP, as load_tile) whose wave-uniform part
+// of the offset sits in a scalar register, so that one vector offset serves
+// all loads of a tile.
+template <int CP>
+__device__ __forceinline__ u32x4 load_tile_s(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, CP));
 }
 
-template <int DT, int GW, int NW>
+template <int DT, int GW, int NW, int CP = kCacheStream>
 __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const DecodeParams p) {
   constexpr int D = 128;
   constexpr int R = D * 2;                // bytes per token row of one head
@@ -509,9 +524,9 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_cache + tile, rows * R);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_cache + tile, rows * R);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kk[i] = load_stream_s(rk, koff, 1024 * i);
+    for (int i = 0; i < 4; ++i) kk[i] = load_tile_s<CP>(rk, koff, 1024 * i);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) vv[t] = load_stream_s(rv, voff, t * R);
+    for (int t = 0; t < 4; ++t) vv[t] = load_tile_s<CP>(rv, voff, t * R);
     return j < ce ? blk : -1;
   };
 
@@ -688,9 +703,15 @@ using DecodeFn = void (*)(const DecodeParams);
 
 // The pickers take the requested waves per workgroup in nw and leave there
 // the waves of the instance they return (an instance may not exist for every
-// request): the launch's block size must be that instance's.
+// request): the launch's block size must be that instance's.  With `reuse`
+// (a batch that shares blocks) they return the 4-wave instance with cached
+// tile loads whatever the request.
 template <int DT, int D, int GW>
-DecodeFn pick_waves(int& nw) {
+DecodeFn pick_waves(int& nw, bool reuse) {
+  if (reuse) {
+    nw = 4;
+    return paged_decode_kernel<DT, D, GW, 4, kCacheReuse>;
+  }
   switch (nw) {
     case 1: return paged_decode_kernel<DT, D, GW, 1>;
     case 2: return paged_decode_kernel<DT, D, GW, 2>;
@@ -704,37 +725,41 @@ DecodeFn pick_waves(int& nw) {
 }
 
 template <int DT, int D>
-DecodeFn pick_gw(int gw, int& nw) {
+DecodeFn pick_gw(int gw, int& nw, bool reuse) {
   switch (gw) {
-    case 1: return pick_waves<DT, D, 1>(nw);
-    case 2: return pick_waves<DT, D, 2>(nw);
-    case 4: return pick_waves<DT, D, 4>(nw);
-    case 8: return pick_waves<DT, D, 8>(nw);
+    case 1: return pick_waves<DT, D, 1>(nw, reuse);
+    case 2: return pick_waves<DT, D, 2>(nw, reuse);
+    case 4: return pick_waves<DT, D, 4>(nw, reuse);
+    case 8: return pick_waves<DT, D, 8>(nw, reuse);
     default: return nullptr;
   }
 }
 
 template <int DT>
-DecodeFn pick_d(int d, int gw, int& nw) {
+DecodeFn pick_d(int d, int gw, int& nw, bool reuse) {
   switch (d) {
-    case 64: return pick_gw<DT, 64>(gw, nw);
-    case 128: return pick_gw<DT, 128>(gw, nw);
-    case 256: return pick_gw<DT, 256>(gw, nw);
+    case 64: return pick_gw<DT, 64>(gw, nw, reuse);
+    case 128: return pick_gw<DT, 128>(gw, nw, reuse);
+    case 256: return pick_gw<DT, 256>(gw, nw, reuse);
     default: return nullptr;
   }
 }
 
-DecodeFn pick_decode(int dt, int d, int gw, int& nw) {
+DecodeFn pick_decode(int dt, int d, int gw, int& nw, bool reuse) {
   switch (dt) {
-    case PKV_F32: return pick_d<PKV_F32>(d, gw, nw);
-    case PKV_F16: return pick_d<PKV_F16>(d, gw, nw);
-    case PKV_BF16: return pick_d<PKV_BF16>(d, gw, nw);
+    case PKV_F32: return pick_d<PKV_F32>(d, gw, nw, reuse);
+    case PKV_F16: return pick_d<PKV_F16>(d, gw, nw, reuse);
+    case PKV_BF16: return pick_d<PKV_BF16>(d, gw, nw, reuse);
     default: return nullptr;
   }
 }
 
 template <int DT, int GW>
-DecodeFn pick_mfma_waves(int& nw) {
+DecodeFn pick_mfma_waves(int& nw, bool reuse) {
+  if (reuse) {
+    nw = 4;
+    return paged_decode_mfma_kernel<DT, GW, 4, kCacheReuse>;
+  }
   switch (nw) {
     case 1: return paged_decode_mfma_kernel<DT, GW, 1>;
     case 2: return paged_decode_mfma_kernel<DT, GW, 2>;
@@ -748,20 +773,20 @@ DecodeFn pick_mfma_waves(int& nw) {
 }
 
 template <int DT>
-DecodeFn pick_mfma_gw(int gw, int& nw) {
+DecodeFn pick_mfma_gw(int gw, int& nw, bool reuse) {
   switch (gw) {
-    case 2: return pick_mfma_waves<DT, 2>(nw);
-    case 4: return pick_mfma_waves<DT, 4>(nw);
-    case 8: return pick_mfma_waves<DT, 8>(nw);
-    case 16: return pick_mfma_waves<DT, 16>(nw);
+    case 2: return pick_mfma_waves<DT, 2>(nw, reuse);
+    case 4: return pick_mfma_waves<DT, 4>(nw, reuse);
+    case 8: return pick_mfma_waves<DT, 8>(nw, reuse);
+    case 16: return pick_mfma_waves<DT, 16>(nw, reuse);
     default: return nullptr;
   }
 }
 
-DecodeFn pick_mfma(int dt, int gw, int& nw) {
+DecodeFn pick_mfma(int dt, int gw, int& nw, bool reuse) {
   switch (dt) {
-    case PKV_F16: return pick_mfma_gw<PKV_F16>(gw, nw);
-    case PKV_BF16: return pick_mfma_gw<PKV_BF16>(gw, nw);
+    case PKV_F16: return pick_mfma_gw<PKV_F16>(gw, nw, reuse);
+    case PKV_BF16: return pick_mfma_gw<PKV_BF16>(gw, nw, reuse);
     default: return nullptr;
   }
 }
@@ -891,7 +916,9 @@ pkv_status launch_partitions(const pkv_pool* pool, const DecodeParams& prm, int 
                              const pkv_decode_plan_info* info, hipStream_t s,
                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
   int nw = waves_per_item();  // becomes the chosen instance's waves
-  DecodeFn fn = mfma ? pick_mfma(pool->desc.dtype, gw, nw) : pick_decode(pool->desc.dtype, pool->desc.head_dim, gw, nw);
+  const bool reuse = info->shared_kv != 0;
+  DecodeFn fn = mfma ? pick_mfma(pool->desc.dtype, gw, nw, reuse)
+                     : pick_decode(pool->desc.dtype, pool->desc.head_dim, gw, nw, reuse);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group");
   const int64_t grid = int64_t(info->n_work) * prm.num_kv_heads * prm.hgroups_per_kv;
   if (ev_start || ev_stop)
@@ -953,7 +980,7 @@ extern "C" pkv_status pkv_decode_occupancy(const pkv_pool* pool, int32_t num_q_h
   const int gw = heads_per_workgroup(group, mfma ? 16 : 8);
   if (gw < 2) mfma = false;
   int nw = waves_per_item();  // becomes the chosen instance's waves
-  DecodeFn fn = mfma ? pick_mfma(d.dtype, gw, nw) : pick_decode(d.dtype, d.head_dim, gw, nw);
+  DecodeFn fn = mfma ? pick_mfma(d.dtype, gw, nw, false) : pick_decode(d.dtype, d.head_dim, gw, nw, false);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group");
   int per_cu = 0, dev = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kWave * nw, 0) !=

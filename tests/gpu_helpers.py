@@ -90,13 +90,15 @@ class DecodeCase:
         sync()
         del k, v
 
-    def decode(self, partition_tokens=0, split=False, append=False, workspace=None):
+    def decode(self, partition_tokens=0, split=False, append=False, workspace=None, shared_kv=0):
         """Decode the batch; ``append`` passes each sequence's newest token as
         k_new/v_new (fused store + decode); ``workspace`` (optional, zeroed
-        once by the caller) is reused instead of a fresh one."""
+        once by the caller) is reused instead of a fresh one; ``shared_kv``
+        is the plan's load-policy hint (1: tile loads through the caches)."""
         cfg = self.cfg
         tables, lens = self.pool.build_batch(self.seqs, self.stride)
         plan, info = decode_plan(lens, partition_tokens)
+        info.shared_kv = shared_kv
         q = to_device(self.vals["q"], cfg.dtype)
         out = torch.full((len(self.lens), cfg.num_q_heads, cfg.head_dim), float("nan"),
                          dtype=torch.float32, device="cuda")

@@ -306,3 +306,36 @@ def test_tuning_variants(dtype, group, monkeypatch):
                         assert case.last_tickets_zero
     finally:
         case.close()
+
+
+@pytest.mark.parametrize("dtype,group", [("f32", 1), ("f16", 1), ("bf16", 1), ("bf16", 4), ("f16", 8)])
+def test_cached_tile_loads(dtype, group, monkeypatch):
+    """The plan's load-policy hint (shared_kv = 1: tile loads through the
+    caches, 4 waves per workgroup) gives bit for bit the output of the
+    streaming loads at 4 waves, within the oracle's tolerance, for both
+    kernels, split and unsplit, with the fused append."""
+    idx = 600 + 10 * group + {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+    d = 64 if dtype == "f32" else 128
+    cfg = dataclasses.replace(config_by_name("tiny_f32"), name="cached_loads", index=idx, dtype=dtype,
+                              head_dim=d, num_kv_heads=2, num_q_heads=2 * group, num_seqs=7)
+    lens = [1, 16, 17, 40, 129, 300, 700]
+    nb = sum(-(-L // 16) for L in lens) + 3
+    case = DecodeCase(cfg, lens=lens, num_blocks=nb, free_order=np.random.default_rng(idx).permutation(nb),
+                      fill=float("nan"))
+    try:
+        case.write_context(skip_last=True)
+        monkeypatch.setenv("PKV_DECODE_WAVES", "4")
+        for mfma in (("1", "0") if group > 1 else ("0",)):
+            monkeypatch.setenv("PKV_DECODE_MFMA", mfma)
+            for P, split in ((64, False), (64, True), (0, False)):
+                outs = []
+                for shared in (0, 1):
+                    out, info = case.decode(P, split=split, append=True, shared_kv=shared)
+                    assert info.shared_kv == shared
+                    assert np.isfinite(out).all(), (mfma, P, split, shared)
+                    assert max_err(case, out, range(len(lens))) <= TOL[dtype], (mfma, P, split, shared)
+                    assert case.last_tickets_zero
+                    outs.append(out)
+                assert np.array_equal(outs[0], outs[1]), (mfma, P, split)
+    finally:
+        case.close()
