@@ -550,6 +550,15 @@ pkv_status pkv_prepare_decode(pkv_pool* pool, const int32_t* seqs, int32_t n_seq
                               int32_t partition_tokens, void* staging, size_t staging_bytes,
                               pkv_batch_layout* layout);
 
+/* The decode plan's K/V load-policy hint for a batch of live sequences
+ * (pkv_decode_plan_info.shared_kv): 1 when at least a quarter of their
+ * context tokens lie in blocks that more than one sequence holds (forked
+ * prefixes), else 0.  pkv_prepare_decode applies the same rule after its
+ * append; callers that plan with pkv_decode_plan can set the field from this.
+ * Read only.  PKV_E_BAD_SEQ for an unknown sequence id. */
+pkv_status pkv_batch_shared_kv(const pkv_pool* pool, const int32_t* seqs, int32_t n_seqs,
+                               int32_t* shared_kv);
+
 /* ---------------------------------------------------------------------------
  * One decode iteration in one call (host + device)
  * ------------------------------------------------------------------------ */

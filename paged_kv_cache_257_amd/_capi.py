@@ -172,6 +172,7 @@ SIGNATURES = {
     "pkv_prefill_workspace_bytes": [C.POINTER(PrefillPlanInfo), I32],
     "pkv_prepare_decode_bytes": [I32, I32, I32, I32, I32],
     "pkv_prepare_decode": [P, PI32, I32, I32, I32, I32, P, C.c_size_t, C.POINTER(BatchLayout)],
+    "pkv_batch_shared_kv": [P, PI32, I32, PI32],
     "pkv_stepper_slot_bytes": [I32, I32, I32, I32],
     "pkv_stepper_create": [P, I32, I32, I32, I32, P, P, C.c_size_t, P, C.c_size_t, P, C.POINTER(P)],
     "pkv_stepper_destroy": [P],

@@ -41,21 +41,20 @@ Offsets layout_for(int64_t n, int64_t append, int64_t pair_cap, int64_t stride, 
 // break-even point measured on MI355X: streaming (nontemporal) loads read
 // unshared tiles ~12% faster, cached loads read a prefix shared by 256
 // sequences ~2x faster.
-bool shares_context(const pkv_pool* p, const int32_t* tables, const int32_t* lens, int32_t n,
-                    int32_t stride) {
+bool shares_context(const pkv_pool* p, const int32_t* seqs, int32_t n) {
   const int32_t bs = p->desc.block_size;
   int64_t total = 0, shared = 0;
   for (int32_t i = 0; i < n; ++i) {
-    const int32_t* t = tables + int64_t(i) * stride;
-    const int32_t nblk = (lens[i] + bs - 1) / bs;
+    const pkv_seq_state* s = pkv::find_seq(p, seqs[i]);
+    const int32_t nblk = (s->length + bs - 1) / bs;
     int32_t lo = 0, hi = nblk;  // first block with a single holder lies in [lo, hi]
     while (lo < hi) {
       const int32_t mid = lo + (hi - lo) / 2;
-      if (p->rc[size_t(t[mid])] > 1) lo = mid + 1;
+      if (p->rc[size_t(s->table[size_t(mid)])] > 1) lo = mid + 1;
       else hi = mid;
     }
-    total += lens[i];
-    shared += std::min<int64_t>(lens[i], int64_t(lo) * bs);
+    total += s->length;
+    shared += std::min<int64_t>(s->length, int64_t(lo) * bs);
   }
   return total > 0 && 4 * shared >= total;
 }
@@ -77,6 +76,16 @@ size_t pkv_prepare_decode_bytes(int32_t max_seqs, int32_t append_tokens, int32_t
   const Offsets o = layout_for(max_seqs, append_tokens, max_seqs, table_stride,
                                plan_cap_for(max_seqs, table_stride, block_size, P));
   return size_t(o.end);
+}
+
+pkv_status pkv_batch_shared_kv(const pkv_pool* p, const int32_t* seqs, int32_t n_seqs,
+                               int32_t* shared_kv) {
+  if (!p || !shared_kv || n_seqs < 0 || (n_seqs > 0 && !seqs))
+    return fail(PKV_E_BAD_ARG, "null pool, sequences or output");
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (!pkv::find_seq(p, seqs[i])) return fail(PKV_E_BAD_SEQ, "unknown sequence " + std::to_string(seqs[i]));
+  *shared_kv = shares_context(p, seqs, n_seqs) ? 1 : 0;
+  return PKV_OK;
 }
 
 pkv_status pkv_prepare_decode(pkv_pool* p, const int32_t* seqs, int32_t n_seqs,
@@ -123,7 +132,7 @@ pkv_status pkv_prepare_decode(pkv_pool* p, const int32_t* seqs, int32_t n_seqs,
   if (pkv_status st = pkv_decode_plan(lens, n_seqs, bs, P, plan,
                                       int32_t(plan_cap_for(n_seqs, table_stride, bs, P)), &info))
     return st;  // unreachable: lengths were checked above
-  info.shared_kv = shares_context(p, tables, lens, n_seqs, table_stride) ? 1 : 0;
+  info.shared_kv = shares_context(p, seqs, n_seqs) ? 1 : 0;
   layout->n_seqs = n_seqs;
   layout->append_tokens = append_tokens;
   layout->n_pairs = n_pairs;

@@ -176,6 +176,15 @@ class Pool:
         n = int(pairs.shape[0])
         check(self.lib, self.lib.pkv_copy_blocks(self.handle, _dptr(pairs), n, _stream_ptr(stream)))
 
+    def batch_shared_kv(self, seqs) -> int:
+        """The decode plan's load-policy hint for these sequences: 1 when a
+        quarter or more of their context sits in blocks several sequences
+        hold (set PlanInfo.shared_kv from it), else 0."""
+        arr = np.ascontiguousarray(seqs, dtype=np.int32)
+        out = C.c_int32()
+        check(self.lib, self.lib.pkv_batch_shared_kv(self.handle, i32p(arr), len(arr), C.byref(out)))
+        return out.value
+
     def decode_occupancy(self, num_q_heads: int) -> Tuple[int, int]:
         """(workgroups per decode work item, resident workgroups on the device)."""
         wpi, res = C.c_int32(), C.c_int64()

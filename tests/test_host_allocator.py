@@ -286,12 +286,15 @@ def test_prepare_decode_shared_kv_hint():
         for _ in range(3):
             got, want = prepared(a, seqs)
             assert got == int(want), scenario
+            assert a.batch_shared_kv(seqs) == got, scenario  # same rule, no append
             cases += got
         if scenario == "forked_prefix":
             assert got == 1
         if scenario in ("unshared", "freed_parent", "small_fork"):
             assert got == 0
     assert cases == 3
+    with pytest.raises(PkvError):
+        a.batch_shared_kv([12345])
 
 
 def test_seq_slots_read_back_each_sequences_dense_history():
