@@ -382,7 +382,9 @@ pkv_status pkv_utilisation(const int32_t* lengths, int32_t n, int32_t max_len, i
  * partitions of partition_tokens (a multiple of block_size; 0 selects
  * pkv_default_partition_tokens()).  One work item per (sequence, partition); items are ordered
  * longest first so that the GPU's in-order dispatch fills the tail with short
- * ones.  Sequences with more than one partition write partial results that a
+ * ones; equal lengths go partition-major (partition 0 of every sequence
+ * first), so that sequences sharing a prefix read its blocks together.
+ * Sequences with more than one partition write partial results that a
  * second kernel combines.
  *
  * plan (host int32, cap >= pkv_decode_plan_ints(...)) receives
