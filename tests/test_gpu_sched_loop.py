@@ -9,7 +9,8 @@ with the same rows, and every output of every iteration is compared with
 the float64 oracle (prefill: causal attention of the slice; decode: the
 sequence's full context).  The small pool forces preemptions, so freed
 blocks are reused and recomputed sequences rewrite their K/V; shared
-prefixes are forked.  The whole pool is free at the end.
+prefixes are forked.  Decode launches alternate the two K/V load policies
+(the plan's shared_kv hint).  The whole pool is free at the end.
 """
 
 import numpy as np
@@ -114,6 +115,8 @@ def test_scheduler_drives_prefill_and_decode():
                     table = ora.a.table(seq)
                     mirror.write_kv(k1[None], v1[None], np.array([table[pos // 16] * 16 + pos % 16]))
                 plan, info = decode_plan(lens, 0)
+                assert pool.batch_shared_kv(seqs) in (0, 1)
+                info.shared_kv = steps % 2  # both load policies, alternately
                 assert decode_workspace_bytes(info, HQ, D) <= ws.numel()
                 out = torch.empty((len(dec), HQ, D), dtype=torch.float32, device="cuda")
                 pool.paged_decode(to_device(q, DT), out, torch.from_numpy(tables).cuda(),
