@@ -17,11 +17,16 @@ steps have pushed out of L2 and the 256 MiB Infinity Cache.
 
 Reported (one JSON line):
   value        K/V bytes the steps attended / wall time of the K steps (GB/s);
-  roofline     the decode launch alone, timed with HIP events on its
-               stream: algorithmic K/V bytes per launch / mean duration,
-               against the 8 TB/s HBM peak; ``traffic`` from rocprofv3
-               FETCH_SIZE + WRITE_SIZE counters when a counter summary for the
-               current kernel source is committed under profiles/;
+  roofline     the decode launches of the K timed steps: algorithmic K/V
+               bytes per launch / average launch duration, the span of the
+               decode stream between two HIP events around the timed steps
+               divided by K (so each dispatch's idle gap counts as
+               duration), against the 8 TB/s HBM peak; after the timed
+               steps, as many more launches (at least 20) each carry their
+               own events for the spread of single-kernel durations;
+               ``traffic`` scales the committed rocprofv3 counter summary's
+               ratio (FETCH_SIZE + WRITE_SIZE over algorithmic bytes) by this
+               line's bytes, while the kernel source is the profiled one;
   cpu_baseline the fp64 CPU oracle on a bounded sample of the same batch.
 """
 
@@ -42,6 +47,17 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "paged-decode achieved HBM GB/s (% of peak) + decode tokens/s, 64-seq fp16 batch"
+# the headline metric names the GPT-style 64-sequence fp16 batch; every other
+# decode workload reports the same quantities under its own description
+DECODE_METRICS = {
+    "gpt_f16": METRIC,
+    "tiny_f32": "paged-decode achieved HBM GB/s (% of peak) + decode tokens/s, tiny 4-seq fp32 batch",
+    "ragged_bf16": "paged-decode achieved HBM GB/s (% of peak) + decode tokens/s, 96-seq ragged bf16 batch",
+    "gqa_long_bf16": "paged-decode achieved HBM GB/s (% of peak) + decode tokens/s, "
+                     "10 x 32768-token GQA-4 bf16 batch",
+}
+PREFIX_METRIC = ("prefix-shared decode loop: logical K/V GB/s + iteration tokens/s, "
+                 "256 seqs over one 4096-token prefix, fp16")
 KERNEL_SOURCES = ("paged_kv_cache_257_amd/csrc/kernels/paged_decode.hip",
                   "paged_kv_cache_257_amd/csrc/kernels/device_common.h",
                   "paged_kv_cache_257_amd/csrc/kernels/mfma_common.h")
@@ -83,10 +99,7 @@ def prefill_source_sha() -> str:
     return _sources_sha(PREFILL_SOURCES)
 
 
-def committed_traffic(summary: str = COUNTER_SUMMARY, sha: Optional[str] = None,
-                      key: str = "hbm_bytes_per_launch"):
-    """HBM bytes from a committed counter summary, if it was taken on the
-    current kernel source (else None)."""
+def _summary_fields(summary: str, sha: Optional[str]):
     path = os.path.join(ROOT, summary)
     if not os.path.exists(path):
         return None
@@ -98,9 +111,32 @@ def committed_traffic(summary: str = COUNTER_SUMMARY, sha: Optional[str] = None,
                 kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha") != (sha or kernel_source_sha()):
         return None
+    return kv
+
+
+def committed_traffic(summary: str = COUNTER_SUMMARY, sha: Optional[str] = None,
+                      key: str = "hbm_bytes_per_launch"):
+    """HBM bytes from a committed counter summary, if it was taken on the
+    current kernel source (else None)."""
+    kv = _summary_fields(summary, sha)
     try:
-        return float(kv[key])
+        return float(kv[key]) if kv else None
     except (KeyError, ValueError):
+        return None
+
+
+def committed_traffic_ratio(summary: str, sha: Optional[str] = None):
+    """Counter bytes per algorithmic byte of the profiled run (HBM traffic
+    FETCH + WRITE, calibrated, over the K/V bytes the same launches attended),
+    if the summary was taken on the current kernel source.  A line scales it
+    by its own algorithmic bytes: the profiled run's contexts may have grown
+    further than this line's."""
+    kv = _summary_fields(summary, sha)
+    if not kv:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"]) / float(kv["algorithmic_bytes_per_launch"])
+    except (KeyError, ValueError, ZeroDivisionError):
         return None
 
 
@@ -125,8 +161,8 @@ def parse_args(argv=None):
                     help="store the new tokens with write_kv instead of inside the decode (comparison)")
     ap.add_argument("--no-overlap", action="store_true",
                     help="upload each step's metadata on the compute stream (comparison)")
-    ap.add_argument("--time-every", type=int, default=8,
-                    help="record the HIP timing events around every N-th decode launch (events cost GPU time)")
+    ap.add_argument("--time-every", type=int, default=1,
+                    help="prefix-shared loop: attach HIP timing events to every N-th iteration's decode")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args(argv)
@@ -206,6 +242,12 @@ def copy_probe():
     torch.cuda.empty_cache()
     best = min(ms)
     return {"bytes_moved": 2 * n, "ms_best": round(best, 4), "GBps": round(2 * n / best / 1e6, 1)}
+
+
+def event_launches(args) -> int:
+    """Decode launches timed one by one after the K timed steps: K, at
+    least 20 and at most 400."""
+    return max(20, min(args.steps, 400))
 
 
 def timing_events(n: int):
@@ -317,7 +359,7 @@ def bench_prefix_shared(args, cfg):
     def iteration(it):
         seqs = np.asarray([x for x in pool.live() if x != root], dtype=np.int32)
         q, k, v = vals[it % 4]
-        lay = step.step(seqs, q, out, k, v, cfg.scale, events=ev[it] if it % args.time_every == 0 else None)
+        lay = step.step(seqs, q, out, k, v, cfg.scale, events=ev[it] if it % every == 0 else None)
         loads.append(lay.plan.shared_kv)
         retire, parents = choose_churn(cfg, it, seqs.tolist())
         for x in retire:
@@ -327,6 +369,8 @@ def bench_prefix_shared(args, cfg):
         return len(seqs)
 
     loads = []  # the plan's load-policy hint of every iteration
+    # an iteration is ~1 ms, so timing events on every decode cost little
+    every = max(1, args.time_every)
     for it in range(warm):
         iteration(it)
     torch.cuda.synchronize()
@@ -341,13 +385,14 @@ def bench_prefix_shared(args, cfg):
     assert decoded == sum(sched[i][0] for i in timed)
     logical = sum(sched[i][1] for i in timed) * per_tok
     physical = sum(sched[i][2] for i in timed) * per_tok
-    sampled = [i for i in timed if i % args.time_every == 0]
+    sampled = [i for i in timed if i % every == 0]
     kern_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in sampled]
     s_log = float(np.mean([sched[i][1] for i in sampled])) * per_tok
     s_phy = float(np.mean([sched[i][2] for i in sampled])) * per_tok
     km = float(np.mean(kern_ms)) / 1e3 if kern_ms else float("nan")
+    ratio = committed_traffic_ratio(counter_summary(cfg.name)) if args.partition == -1 else None
     res = {
-        "metric": "prefix-shared decode loop: logical K/V GB/s + iteration tokens/s",
+        "metric": PREFIX_METRIC,
         "value": round(logical / wall / 1e9, 2),
         "unit": "GB/s (logical)",
         "n_gpus": 1, "steps": steps, "warmup": warm,
@@ -364,12 +409,65 @@ def bench_prefix_shared(args, cfg):
         "pct_of_hbm_peak_physical": round(100 * physical / wall / 1e9 / HBM_PEAK_GBPS, 2),
         "iteration_tokens_per_s": round(decoded / wall, 1),
         "cow_copies": stats["cow_copies"],
-        "kernel": {"ms_mean": round(km * 1e3, 4), "launches_timed": len(kern_ms),
-                   "logical_GBps": round(s_log / km / 1e9, 1),
-                   "physical_GBps": round(s_phy / km / 1e9, 1)},
+        # the decode of an iteration (every launch it makes), timed with HIP
+        # events on its stream; bytes are the distinct K/V the decoded
+        # contexts map to (a block shared by many sequences counted once):
+        # what one pass must read from HBM at the least
+        "roofline": {"bound": "hbm", "achieved": round(s_phy / km / 1e9, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(s_phy / km / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": round(ratio * s_phy) if ratio else None,
+                     "traffic_ratio": round(ratio, 4) if ratio else None,
+                     "bytes": "distinct K/V per iteration",
+                     "kernel_ms_mean": round(km * 1e3, 4),
+                     "kernel_ms_median": round(float(np.median(kern_ms)), 4),
+                     "kernel_ms_p10": round(float(np.percentile(kern_ms, 10)), 4),
+                     "kernel_ms_p90": round(float(np.percentile(kern_ms, 90)), 4),
+                     "timed_launches": len(kern_ms), "time_every": every,
+                     "algorithmic_bytes_per_launch": int(s_phy),
+                     "logical_bytes_per_launch": int(s_log),
+                     "logical_GBps": round(s_log / km / 1e9, 1),
+                     "kernel_source_sha": kernel_source_sha()},
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = prefix_cpu_baseline(cfg, plan, width, args.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def prefix_cpu_baseline(cfg, plan, width, budget_s):
+    """The fp64 oracle on a bounded sample of the prefix-shared loop: the
+    oracle allocator and mirrored pool are set up as the loop starts and
+    the first iteration's append is replayed (not timed); then seeded
+    decoding sequences attend with that iteration's queries until the
+    budget is spent.  Rate in the line's unit: logical K/V bytes attended
+    per second."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle.runs import PrefixSharedRun, iteration_values, prefix_values
+
+    cores = os.cpu_count() or 1
+    with threadpool_limits(limits=cores):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        ora = PrefixSharedRun(cfg, plan, width, with_mirror=True)
+        ora.setup(prefix_values(cfg, plan.tails))
+        seqs, slots, cow = ora.append_step()
+        q, k, v = iteration_values(cfg, 0, len(seqs))
+        ora.write_step(cow, k, v, slots)
+        order = np.random.default_rng(cfg.seed + 7).permutation(len(seqs))
+        done, tokens, t0 = 0, 0, time.perf_counter()
+        while time.perf_counter() - t0 <= budget_s:
+            i = int(order[done % len(order)])
+            ora.attend(seqs[i], q[i])
+            done += 1
+            tokens += ora.alloc.length(seqs[i])
+        dt = time.perf_counter() - t0
+    per_tok = 2 * cfg.num_kv_heads * cfg.head_dim * (4 if cfg.dtype == "f32" else 2)
+    return {"value": round(tokens * per_tok / dt / 1e9, 4), "unit": "GB/s (logical)", "cores": int(threads),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{done} sequence decodes of the loop's first iteration ({tokens} context tokens), "
+                      f"fp64 numpy attention through the oracle allocator, {dt:.1f} s",
+            "decode_tokens_per_s": round(done / dt, 3)}
 
 
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix-core peak
@@ -576,7 +674,9 @@ def main(argv=None):
     B, Hq, H, d, dt = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.dtype
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
     total = args.warmup + args.steps
-    grow = -(-total // args.replicas)  # tokens each replica appends
+    n_post = event_launches(args)  # per-launch event pass after the timed steps
+    total_all = total + n_post
+    grow = -(-total_all // args.replicas)  # tokens each replica appends
     stride = -(-(int(sh.lens.max()) + grow) // 16)
     # each replica's pool holds the batch plus its growth
     grow_blocks = B * (-(-grow // 16) + 1)
@@ -589,8 +689,8 @@ def main(argv=None):
         return (t.view(torch.bfloat16) if dt == "bf16" else t).to("cuda")
 
     k_ctx, v_ctx, q_dev = dev_tensor(vals["k"]), dev_tensor(vals["v"]), dev_tensor(vals["q"])
-    new_k = dev_tensor(draw_normal_storage((cfg.seed, 50), (total, B, H, d), dt))
-    new_v = dev_tensor(draw_normal_storage((cfg.seed, 51), (total, B, H, d), dt))
+    new_k = dev_tensor(draw_normal_storage((cfg.seed, 50), (total_all, B, H, d), dt))
+    new_v = dev_tensor(draw_normal_storage((cfg.seed, 51), (total_all, B, H, d), dt))
     native = not (args.two_launch or args.separate_write or args.no_overlap)
     # fill mode is chosen inside the native stepper; the Python-driven paths
     # take the library default instead
@@ -610,17 +710,16 @@ def main(argv=None):
     seqs = list(range(B))
     per_tok = 2 * H * d * cfg.elem_bytes
 
-    ev = timing_events(total)
+    ev = timing_events(n_post)
+    span = timing_events(1)[0]
     step_bytes, infos = [], []
 
     seqs_np = np.arange(B, dtype=np.int32)
     ctx_tokens = [int(sh.lens.sum())] * args.replicas  # tokens in each replica before a step
 
-    def step(s):
+    def step(s, evs=None):
         r = s % args.replicas
         pool, it, out, _, _ = reps[r]
-        timed_launch = (s % args.time_every) == 0
-        evs = ev[s] if timed_launch else None
         if native:
             lay = it.step(seqs_np, q_dev, out, new_k[s], new_v[s], cfg.scale, events=evs)
             info = lay.plan
@@ -637,28 +736,42 @@ def main(argv=None):
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
+    # the K timed steps carry no per-launch events (each costs the GPU ~5 us
+    # around its dispatch); two events on the decode stream bracket them
     t0 = time.perf_counter()
+    span[0].record()
     for s in range(args.warmup, total):
         step(s)
+    span[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    span_ms = span[0].elapsed_time(span[1])
+    # then n_post more steps with events attached to every decode dispatch:
+    # each launch's own duration, for the spread and for comparison with a
+    # profiler's kernel trace (not part of `value`)
+    for k in range(n_post):
+        step(total + k, ev[k])
+    torch.cuda.synchronize()
 
     timed = range(args.warmup, total)
     kbytes = sum(step_bytes[s] for s in timed)
-    sampled = [s for s in timed if s % args.time_every == 0]
-    if not sampled:
-        print("bench.py: --time-every leaves no timed launch in the measured steps", file=sys.stderr)
-        return 2
-    kern_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in sampled]
-    mean_kern_s = float(np.mean(kern_ms)) / 1e3
-    mean_bytes = float(np.mean([step_bytes[s] for s in sampled]))
+    mean_bytes = float(np.mean([step_bytes[s] for s in timed]))
+    # average decode launch on the GPU over the timed steps: the span of the
+    # decode stream / K, i.e. each launch's duration plus the idle gap before
+    # the next dispatch (a conservative duration: the gap is counted)
+    mean_kern_s = span_ms / 1e3 / args.steps
     achieved = mean_bytes / mean_kern_s / 1e9
+    kern_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(n_post)]
+    post_bytes = float(np.mean([step_bytes[total + k] for k in range(n_post)]))
     timed_ctx = float(np.mean([step_bytes[s] for s in timed])) / per_tok / B
     value = kbytes / wall / 1e9
     info = infos[-1]
-    traffic = committed_traffic(counter_summary(cfg.name))
+    # counter traffic per algorithmic byte of the committed profile, applied
+    # to this line's bytes (taken while the kernel source is unchanged)
+    ratio = committed_traffic_ratio(counter_summary(cfg.name)) if partition == -1 else None
+    traffic = round(ratio * mean_bytes) if ratio else None
     res = {
-        "metric": METRIC,
+        "metric": DECODE_METRICS.get(cfg.name, METRIC),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -689,14 +802,24 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
+                     "traffic_ratio": round(ratio, 4) if ratio else None,
                      "kernel": decode_kernel_name(dt, d, Hq // H) + (" (partition kernel of two launches)"
                                                                      if args.two_launch else ""),
-                     "kernel_ms_mean": round(float(np.mean(kern_ms)), 5),
-                     "kernel_ms_median": round(float(np.median(kern_ms)), 5),
-                     "kernel_ms_p10": round(float(np.percentile(kern_ms, 10)), 5),
-                     "kernel_ms_p90": round(float(np.percentile(kern_ms, 90)), 5),
-                     "timed_launches": len(sampled),
+                     "kernel_ms_mean": round(mean_kern_s * 1e3, 5),
+                     "timing": "HIP events on the decode stream around the K timed steps: span / K "
+                               "(each launch plus the idle gap before the next dispatch)",
+                     "timed_launches": args.steps,
                      "algorithmic_bytes_per_launch": int(mean_bytes),
+                     "per_launch_events": {
+                         "launches": n_post,
+                         "kernel_ms_mean": round(float(np.mean(kern_ms)), 5),
+                         "kernel_ms_median": round(float(np.median(kern_ms)), 5),
+                         "kernel_ms_p10": round(float(np.percentile(kern_ms, 10)), 5),
+                         "kernel_ms_p90": round(float(np.percentile(kern_ms, 90)), 5),
+                         "algorithmic_bytes_per_launch": int(post_bytes),
+                         "achieved": round(post_bytes / (float(np.mean(kern_ms)) / 1e3) / 1e9, 2),
+                         "note": "the steps right after the timed ones, each decode dispatch carrying "
+                                 "its own start/stop events (the kernel alone)"},
                      "kernel_source_sha": kernel_source_sha()},
     }
     for pool, it, *_ in reps:

@@ -4,7 +4,11 @@
  *
  * Sources the operations follow (cited by page title and section):
  *   [lesson]   "PagedAttention e continuous batching" (llmdeepdive lesson 7.8),
- *              section "01 · Conceito", paragraphs 1-9;
+ *              section "01 · Conceito", paragraphs 1-9 (paragraph 1 opens
+ *              "Você tem um acelerador de 80 GB", 3 "PagedAttention,
+ *              introduzida com o vLLM", 6 "A indireção também habilita
+ *              compartilhamento", 7 "A alocação resolve onde o estado
+ *              mora", 8 "Acompanhe as métricas operacionais");
  *   [preview]  "04 — Hacia PagedAttention (vista previa)" (lynx-cortex,
  *              phase 22 theory), section "La idea de PagedAttention", steps 1-5
  *              and "Propiedades"; "Lo que deberías llevarte"; "Lo que la
@@ -23,7 +27,7 @@
  * Conventions
  *   - Every function returns a pkv_status.  On any error nothing changes
  *     (a request that does not fit is turned away when admitted, with a
- *     status, instead of failing later: [lesson] paragraph 8);
+ *     status, instead of failing later: [lesson] paragraph 7);
  *     pkv_last_error() gives a message for the calling thread.
  *   - The caller owns all device memory: the K/V pools, q, out, tables,
  *     context lengths, plans and workspaces.  The library never allocates
@@ -70,7 +74,7 @@ typedef struct {
   int32_t dtype;              /* pkv_dtype of the K/V pools and of q      */
 } pkv_pool_desc;
 
-/* Operational counters ([lesson] paragraph 9). */
+/* Operational counters ([lesson] paragraph 8). */
 typedef struct {
   int64_t free_blocks;
   int64_t used_blocks;
@@ -106,16 +110,22 @@ pkv_status pkv_pool_destroy(pkv_pool* pool);
 pkv_status pkv_pool_reset(pkv_pool* pool);
 pkv_status pkv_pool_get_desc(const pkv_pool* pool, pkv_pool_desc* out);
 
-/* New sequence holding n_tokens tokens (n_tokens >= 0).  Writes its id to
- * *seq and, if slots != NULL, the slot of each token to slots[0..n_tokens).
- * Needs ceil(n_tokens / block_size) free blocks; ids count up from 0 and are
+/* New sequence holding n_tokens tokens (n_tokens >= 0): its block table
+ * gets ceil(n_tokens / block_size) blocks taken from the free list, and
+ * token t goes to row t % block_size of table entry t / block_size
+ * ([preview] "La idea de PagedAttention", steps 2-3: one table per
+ * sequence mapping logical blocks to physical ones, tokens filling blocks
+ * in order).  Writes its id to *seq and, if slots != NULL, the slot of each
+ * token to slots[0..n_tokens).  Fails with PKV_E_NO_BLOCKS, changing
+ * nothing, when fewer blocks are free ([lesson] paragraph 7: admission is
+ * decided in blocks and refused up front).  Ids count up from 0 and are
  * never reused. */
 pkv_status pkv_seq_alloc(pkv_pool* pool, int32_t n_tokens, int32_t* seq, int64_t* slots);
 
 /* Append n_tokens tokens to a sequence ([preview] step 3): a token goes into
  * the last block if it has room, otherwise into a newly taken block; nothing
  * already stored moves.  If the last block is partly filled and shared
- * (refcount > 1), the first token copies it first ([lesson] paragraph 7):
+ * (refcount > 1), the first token copies it first ([lesson] paragraph 6):
  * the appending sequence takes a fresh block, a (src, dst) copy is queued for
  * pkv_take_cow, and the source loses one reference. */
 pkv_status pkv_seq_append(pkv_pool* pool, int32_t seq, int32_t n_tokens, int64_t* slots);
@@ -126,7 +136,7 @@ pkv_status pkv_seq_append_batch(pkv_pool* pool, const int32_t* seqs, int32_t n_s
                                 int32_t n_tokens, int64_t* slots);
 
 /* New sequence sharing every block of parent (prefix sharing, parallel
- * samples; [lesson] paragraph 7, [preview] "Propiedades").  Takes no block:
+ * samples; [lesson] paragraph 6, [preview] "Propiedades").  Takes no block:
  * every block's refcount goes up by one. */
 pkv_status pkv_seq_fork(pkv_pool* pool, int32_t parent, int32_t* child);
 
@@ -134,12 +144,16 @@ pkv_status pkv_seq_fork(pkv_pool* pool, int32_t parent, int32_t* child);
  * <= its length): the child's table is the parent's first
  * ceil(n_tokens / block_size) blocks, each gaining a reference; requests
  * with an identical prompt prefix point at the same read-only blocks
- * ([lesson] paragraph 7).  If n_tokens ends inside a block, the child's
+ * ([lesson] paragraph 6).  If n_tokens ends inside a block, the child's
  * first append copies that block (copy-on-write). */
 pkv_status pkv_seq_fork_prefix(pkv_pool* pool, int32_t parent, int32_t n_tokens, int32_t* child);
 
-/* Release a sequence: each block of its table, front to back, loses one
- * reference; blocks reaching zero go back on the free list. */
+/* Release a sequence ([preview] "La idea de PagedAttention", step 4: a
+ * finished sequence returns its blocks to the free list; [lesson] paragraph
+ * 6: reference counts decide when a shared block goes back to the pool):
+ * each block of its table, front to back, loses one reference; blocks
+ * reaching zero are pushed on the free list.  PKV_E_BAD_SEQ for an unknown
+ * or already freed id (nothing changes). */
 pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq);
 
 pkv_status pkv_seq_length(const pkv_pool* pool, int32_t seq, int32_t* length);
@@ -161,16 +175,22 @@ pkv_status pkv_free_list(const pkv_pool* pool, int32_t* blocks, int32_t cap, int
 pkv_status pkv_refcounts(const pkv_pool* pool, int32_t* refcounts);
 pkv_status pkv_stats(const pkv_pool* pool, pkv_stats_t* out);
 
-/* Take the copy-on-write pairs queued since the last call, pairs[i][0] = src,
- * pairs[i][1] = dst.  If more than cap are queued, fails with PKV_E_BAD_ARG,
+/* Take the copy-on-write pairs queued since the last call ([lesson]
+ * paragraph 6: when a branch diverges, copy-on-write gives it a new block
+ * for the altered positions; the device half is pkv_copy_blocks), host
+ * int32 pairs[i][0] = src, pairs[i][1] = dst.  If more than cap are queued, fails with PKV_E_BAD_ARG,
  * sets *n to the count and takes nothing.  Contract: enqueue pkv_copy_blocks
  * for these pairs, then pkv_write_kv for the appended tokens, before the next
  * append or fork; the pairs of one append batch never depend on each other. */
 pkv_status pkv_take_cow(pkv_pool* pool, int32_t* pairs, int32_t cap, int32_t* n);
 
-/* Block tables (row i = table of seqs[i], padded with -1 to table_stride) and
- * context lengths of a batch, written to host arrays
- * block_tables[n_seqs][table_stride] and context_lens[n_seqs]. */
+/* Block tables and context lengths of a batch, the arguments the attention
+ * kernel takes to do its gathers itself ([preview] "La idea de
+ * PagedAttention", step 5), written to host arrays
+ * block_tables[n_seqs][table_stride] (row i = table of seqs[i], padded with
+ * -1) and context_lens[n_seqs].  PKV_E_BAD_SEQ for an unknown id,
+ * PKV_E_BAD_ARG if a table is wider than table_stride; nothing is written
+ * then. */
 pkv_status pkv_build_batch(const pkv_pool* pool, const int32_t* seqs, int32_t n_seqs,
                            int32_t* block_tables, int32_t table_stride, int32_t* context_lens);
 
@@ -183,7 +203,7 @@ pkv_status pkv_build_batch(const pkv_pool* pool, const int32_t* seqs, int32_t n_
  * boundary, finished sequences leave, waiting ones enter, running ones
  * advance one token; the scheduler weighs free blocks, tokens per batch and
  * the prefill/decode mix, slicing long prefills; admission is decided in
- * blocks; paragraph 9 names the metrics kept here).
+ * blocks; paragraph 8 names the metrics kept here).
  * The pages give the goals, not the rules; the rules below are readings.
  *
  * Requests are known up front with an arrival iteration; the policy does
@@ -301,14 +321,14 @@ pkv_status pkv_sched_stats(const pkv_sched* s, pkv_sched_stats_t* out);
 /* A hybrid model keeps paged K/V only for its attention layers; its other
  * layers carry a recurrent state of fixed size per sequence, so a server
  * aware of the hybrid runs two pools with different lifecycles
- * ("PagedAttention e continuous batching", 01 · Conceito, paragraph 7).
+ * ("PagedAttention e continuous batching", 01 · Conceito, paragraph 5).
  * pkv_hybrid pairs a K/V pool with a pool of num_slots state slots of
  * slot_bytes each (device memory at state_base, caller-owned; NULL for
  * host-only use).  A sequence admitted through it holds blocks and one
  * slot; a fork shares the parent's blocks (refcounts) but takes its own
  * slot and queues a (parent slot, child slot) copy, since the state changes
  * every step; free returns both.  Admission and fork are all-or-nothing
- * across the two pools and fail up front ([lesson] paragraph 8) with
+ * across the two pools and fail up front ([lesson] paragraph 7) with
  * PKV_E_NO_SLOTS or PKV_E_NO_BLOCKS.  The slot free list is a stack seeded
  * by slot_order (NULL = 0..num_slots-1; slot_order[0] is handed out first).
  * Sequences admitted here must be forked and freed here; appends go to the
@@ -539,7 +559,7 @@ size_t pkv_prepare_decode_bytes(int32_t max_seqs, int32_t append_tokens, int32_t
                                 int32_t block_size, int32_t partition_tokens);
 
 /* The host half of a continuous-batching decode iteration ([lesson]
- * paragraph 8: running sequences advance one token per iteration), in one
+ * paragraph 7: running sequences advance one token per iteration), in one
  * call: append append_tokens (0 or more) to each of seqs[0..n_seqs) in that
  * order (pkv_seq_append_batch), take the copy-on-write pairs, build block
  * tables and context lengths (pkv_build_batch) and the split-K plan
@@ -565,7 +585,7 @@ pkv_status pkv_batch_shared_kv(const pkv_pool* pool, const int32_t* seqs, int32_
  * One decode iteration in one call (host + device)
  * ------------------------------------------------------------------------ */
 
-/* A stepper runs continuous-batching decode iterations ([lesson] paragraph 8:
+/* A stepper runs continuous-batching decode iterations ([lesson] paragraph 7:
  * at every iteration the running sequences advance one token) over a pool.
  * The caller provides PKV_STEPPER_SLOTS staging slots of slot_bytes each, in
  * pinned host memory (staging_host) and in device memory (staging_dev), the
@@ -624,7 +644,7 @@ pkv_status pkv_stepper_step(pkv_stepper* stepper, const int32_t* seqs, int32_t n
 pkv_status pkv_decode_occupancy(const pkv_pool* pool, int32_t num_q_heads, int32_t* workgroups_per_item,
                                 int64_t* resident);
 
-/* Copy-on-write copies ([lesson] paragraph 7): for each pair, K[dst] = K[src]
+/* Copy-on-write copies ([lesson] paragraph 6): for each pair, K[dst] = K[src]
  * and V[dst] = V[src] over all heads and rows.  pairs: device int32
  * [n_pairs][2].  Pairs with an id outside the pool are skipped. */
 pkv_status pkv_copy_blocks(const pkv_pool* pool, const int32_t* pairs, int32_t n_pairs,
@@ -650,7 +670,7 @@ pkv_status pkv_write_kv(const pkv_pool* pool, const void* k_new, const void* v_n
 pkv_status pkv_read_kv(const pkv_pool* pool, const int64_t* slot_mapping, int32_t n_tokens,
                        void* k_out, void* v_out, void* stream);
 
-/* PagedAttention decode ([lesson] paragraph 5, [preview] step 5): for every
+/* PagedAttention decode ([lesson] paragraph 3, [preview] step 5): for every
  * sequence i and query head h,
  *     out[i][h] = softmax_j(scale * q[i][h] . K_i[j][g]) . V_i[j][g]
  * over the context_lens[i] tokens of sequence i, where K_i / V_i row j is read
@@ -670,11 +690,14 @@ pkv_status pkv_read_kv(const pkv_pool* pool, const int64_t* slot_mapping, int32_
  *   context_lens: device int32 [num_seqs]; every entry >= 1 and equal to the
  *                 lengths given to pkv_decode_plan
  *   plan, info:   device copy of the plan and its host-side info
- *   workspace:    device, 16-byte aligned, >= pkv_decode_workspace_bytes(info, ...) bytes.  Its
- *                 first bytes hold completion tickets: they must be zero
- *                 before the first call (allocate it zeroed) and every call
- *                 leaves them zero.  Calls that share a workspace must not
+ *   workspace:    device, 16-byte aligned, >= pkv_decode_workspace_bytes(info, ...) bytes.  Split-K
+ *                 partial records fill it from its start; its last bytes
+ *                 hold completion tickets, which must be zero before the
+ *                 first call (allocate it zeroed) and which every call
+ *                 leaves zero.  Calls that share a workspace must not
  *                 overlap in time.
+ *   scale:        finite and > 0 (1/sqrt(head_dim) for the pages' attention),
+ *                 else PKV_E_BAD_ARG.
  * One kernel launch: multi-partition sequences are combined by the last
  * workgroup of each sequence and head group to finish.
  * Arithmetic: fp32 accumulation and an online (running max) softmax; the
@@ -715,7 +738,7 @@ pkv_status pkv_paged_decode_reduce(const pkv_pool* pool, const void* q, const vo
  * query t of sequence i (row q_start[i] + t of q and out) sits at position
  * context_lens[i] - q_lens[i] + t and attends to that sequence's positions
  * 0 .. that position ("PagedAttention e continuous batching", 01 · Conceito:
- * the kernel reads through the block table, paragraph 5; long prefills are
+ * the kernel reads through the block table, paragraph 3; long prefills are
  * sliced, the scheduler paragraph).  The chunk's K/V must already be in the
  * pool (pkv_seq_append / pkv_write_kv).  q: device [total_q][H_q][head_dim]
  * in the pool dtype; out: device fp32 [total_q][H_q][head_dim] (q, out and

@@ -7,10 +7,10 @@ Follows [preview] "La idea de PagedAttention":
   step 3  appending a token writes into the last block if it has room,
           otherwise a free block is taken and the table grows;
   step 4  freeing a sequence returns its blocks to a free list;
-and [lesson] paragraph 7: sequences may point at the same read-only blocks
+and [lesson] paragraph 6: sequences may point at the same read-only blocks
 (forks, shared prefixes); when one of them diverges, copy-on-write gives the
 writer a new block for the altered positions, and reference counts decide
-when a shared block goes back to the pool.  [lesson] paragraph 8: admission
+when a shared block goes back to the pool.  [lesson] paragraph 7: admission
 is decided in blocks, and a request that cannot fit is turned away at once
 with an explicit error.
 
@@ -98,7 +98,7 @@ class OracleAllocator:
             raise AllocError(BAD_SEQ, f"unknown sequence {seq}")
         return s
 
-    # ---- one token (preview step 3, lesson paragraph 7) ----------------------
+    # ---- one token (preview step 3, lesson paragraph 6) ----------------------
     def _append_token(self, s: _Seq) -> int:
         bs = self.block_size
         L = s.length

@@ -2,7 +2,7 @@
 
 The pages never print the attention formula; they fix two facts about it:
 the attention kernel reads keys and values by following each sequence's
-block table ([lesson] paragraph 5; [preview] "La idea de PagedAttention",
+block table ([lesson] paragraph 3; [preview] "La idea de PagedAttention",
 step 5), and paging leaves the FLOPs and the result of dense attention
 unchanged ([preview] "Lo que deberías llevarte", item 2).  So the result is
 dense scaled dot-product attention over the sequence's logical tokens,

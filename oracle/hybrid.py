@@ -1,6 +1,6 @@
 """Hybrid two-pool manager (oracle; test infrastructure only).
 
-"PagedAttention e continuous batching", 01 · Conceito, paragraph 7: a
+"PagedAttention e continuous batching", 01 · Conceito, paragraph 5: a
 hybrid model pages the growing K/V of its attention layers, while its other
 layers keep a recurrent state of fixed size per sequence, so the server
 manages two pools with different lifecycles.  The model here: a state pool
@@ -12,7 +12,7 @@ names the two pools, not their rules):
     changes every step; the copy (parent slot, child slot) is queued;
   * free returns the blocks and the slot;
   * admission and fork are all-or-nothing across both pools and refuse
-    early ([lesson] paragraph 8): the slot is checked first, then blocks;
+    early ([lesson] paragraph 7): the slot is checked first, then blocks;
   * the slot free list is a stack seeded like the block free list.
 
 Budget split ([lesson] paragraph 4's arithmetic): a session of T tokens

@@ -5,7 +5,7 @@ in the storage dtype and zero-initialised, exactly the bits the device pools
 should hold.  [preview] "La idea de PagedAttention" step 3 writes a new
 token into its slot; slot s lives at block ``s // block`` and row
 ``s % block``.  A negative slot means "no write" (padding).  Copy-on-write
-([lesson] paragraph 7) copies a whole block, K and V, every head.
+([lesson] paragraph 6) copies a whole block, K and V, every head.
 
 ``DenseShadow`` is the dense, never-paged cache of [preview] "Lo que funciona
 en la Fase 22": per sequence, rows appended in logical order.  A fork copies

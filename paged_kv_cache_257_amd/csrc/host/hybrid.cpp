@@ -1,6 +1,6 @@
 // Hybrid two-pool manager: paged K/V blocks plus fixed-size per-sequence
 // state slots ("PagedAttention e continuous batching", 01 · Conceito,
-// paragraph 7).  Host side; the state copy kernel lives with the device code.
+// paragraph 5).  Host side; the state copy kernel lives with the device code.
 #include <algorithm>
 #include <string>
 

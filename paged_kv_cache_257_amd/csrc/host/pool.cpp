@@ -4,9 +4,9 @@
 // PagedAttention", steps 1-4 (fixed-size blocks, one block table per
 // sequence, append into the last block or a newly taken one, free back to a
 // free list) and "PagedAttention e continuous batching", 01 · Conceito,
-// paragraph 7 (shared read-only blocks, copy-on-write for the writer of a
+// paragraph 6 (shared read-only blocks, copy-on-write for the writer of a
 // diverging branch, reference counts deciding when a block returns to the
-// pool) and paragraph 8 (admission decided in blocks, failing up front).
+// pool) and paragraph 7 (admission decided in blocks, failing up front).
 //
 // Policy choices the pages leave open, fixed so that tables are
 // reproducible bit for bit:

@@ -32,7 +32,7 @@ Offsets layout_for(int64_t n, int64_t append, int64_t pair_cap, int64_t stride, 
 // Whether at least a quarter of the batch's context tokens lie in blocks that
 // more than one sequence holds (the K/V load policy hint of the decode plan).
 // Blocks are shared only through forks ("PagedAttention e continuous
-// batching", 01 · Conceito, paragraph 7: sequences with a common prefix point
+// batching", 01 · Conceito, paragraph 6: sequences with a common prefix point
 // at the same read-only blocks, a diverging writer gets a copy): a child takes
 // its parent's whole table, and copy-on-write replaces only the partly filled
 // last block, so along a table the holders of block j include

@@ -5,7 +5,7 @@
 // handed out ("04 — Hacia PagedAttention", La idea de PagedAttention, step 3:
 // a token goes into the last block, or a newly taken one).  copy_blocks is
 // the copy of copy-on-write ("PagedAttention e continuous batching",
-// 01 · Conceito, paragraph 7): the diverging sequence gets its own copy of a
+// 01 · Conceito, paragraph 6): the diverging sequence gets its own copy of a
 // shared block before it writes.
 //
 // Both are plain byte moves: each thread moves one 16-byte chunk with a

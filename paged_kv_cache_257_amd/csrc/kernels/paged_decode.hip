@@ -3,7 +3,7 @@
 // For every sequence i and query head h: out = softmax(scale * q . K^T) . V
 // over the sequence's logical tokens, with K/V rows read through the
 // sequence's block table ("PagedAttention e continuous batching",
-// 01 · Conceito, paragraph 5; "04 — Hacia PagedAttention", La idea de
+// 01 · Conceito, paragraph 3; "04 — Hacia PagedAttention", La idea de
 // PagedAttention, step 5).  Paging changes where rows live, not the result
 // or the FLOPs of dense attention ("Lo que deberías llevarte", item 2), so
 // the kernel is bound by HBM bandwidth: one pass over the K/V bytes.
@@ -51,6 +51,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 
 #include "decode_launch.h"
@@ -133,16 +134,27 @@ __device__ __forceinline__ void finish_item(const DecodeParams& p, const float* 
   // Split-K combine in the same launch.  Each workgroup of a (sequence, head
   // group) waits until its partial stores have completed, takes a ticket, and
   // the one taking the last ticket combines every partition's record and
-  // resets the ticket for the next launch.  Records and tickets are only
-  // touched through agent-scope atomics and every record owns whole cache
-  // lines, so no cache writeback or invalidate is needed.
+  // resets the ticket for the next launch.
+  // Ordering.  Writer side: every thread's record stores are agent-scope
+  // atomic stores, waited for (s_waitcnt) before the workgroup barrier, and
+  // the barrier orders them before thread 0's ticket add; the records are
+  // therefore performed at agent scope before the ticket can count them.
+  // No release fence is added there: at agent scope it writes back the
+  // whole L2 of the compute unit's XCD, in every workgroup of every split
+  // sequence.  Reader side: the workgroup that draws the last ticket takes
+  // an agent-scope acquire fence before the barrier that releases its
+  // threads to read the records (agent-scope atomic loads), so no load of a
+  // record can be satisfied before the ticket was observed.
   __shared__ int sm_last;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int32_t* ticket = p.counters + int64_t(seq) * hgroups + hg;
-  if (threadIdx.x == 0)
-    sm_last = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               n_parts - 1);
+  if (threadIdx.x == 0) {
+    const bool last =
+        __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_parts - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    sm_last = last;
+  }
   __syncthreads();
   if (!sm_last) return;
   const int base = p.part_offset[seq];
@@ -844,6 +856,9 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
   if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256)
     return fail(PKV_E_UNSUPPORTED, "head_dim must be 64, 128 or 256");
   if (!info) return fail(PKV_E_BAD_ARG, "null plan info");
+  // the matrix-core kernel scales a block's maximum score after taking it,
+  // which equals the maximum of the scaled scores only for a positive scale
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PKV_E_BAD_ARG, "scale must be finite and > 0");
   if (num_seqs < 0 || num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0)
     return fail(PKV_E_BAD_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
   if (info->num_seqs != num_seqs || info->block_size != d.block_size ||

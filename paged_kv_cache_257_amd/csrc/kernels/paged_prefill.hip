@@ -4,7 +4,7 @@
 // (L = C + T), brings T queries; query t sits at position C + t and attends
 // causally to positions 0 .. C + t of its sequence, reading K/V through the
 // block table ("PagedAttention e continuous batching", 01 · Conceito:
-// the kernel follows the block table, paragraph 5; long prefills are cut
+// the kernel follows the block table, paragraph 3; long prefills are cut
 // into slices, the scheduler paragraph).  Unlike decode, many queries share
 // every K/V tile, so the products are dense contractions and run as MFMA.
 //
@@ -43,6 +43,8 @@
 // than 2^8 in weight, and the accumulators are rescaled only in stages where
 // some row's maximum moved (a wave-wide vote); otherwise the factor is
 // exactly 1.
+#include <cmath>
+
 #include "mfma_common.h"
 
 namespace pkv {
@@ -560,6 +562,9 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, flo
   if (d.head_dim != 64 && d.head_dim != 128)
     return fail(PKV_E_UNSUPPORTED, "paged prefill takes head_dim 64 or 128");
   if (!info) return fail(PKV_E_BAD_ARG, "null plan info");
+  // the running maxima are taken over scaled scores, which equals scaling
+  // the maximum only for a positive scale
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PKV_E_BAD_ARG, "scale must be finite and > 0");
   if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0)
     return fail(PKV_E_BAD_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
   const int group = num_q_heads / d.num_kv_heads;

@@ -1,7 +1,7 @@
 // Decode-iteration stepper: the host half (pkv_prepare_decode) and the device
 // half (upload, copy-on-write copies, one decode launch) of a continuous-
 // batching iteration ("PagedAttention e continuous batching", 01 · Conceito,
-// paragraph 8: running sequences advance one token per iteration) in one
+// paragraph 7: running sequences advance one token per iteration) in one
 // native call, so that a caller pays one foreign-function call per iteration.
 //
 // The metadata of iteration t is uploaded on a separate copy stream while the

@@ -41,6 +41,20 @@ def sync():
     torch.cuda.synchronize()
 
 
+def oracle_map(fn, items, workers=None):
+    """[fn(x) for x in items] on a thread pool: the fp64 oracle spends its
+    time in numpy copies and BLAS calls that release the GIL, so full-size
+    parity checks of every sequence finish several times sooner."""
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+    items = list(items)
+    workers = workers or max(1, min(16, os.cpu_count() or 1))
+    if len(items) <= 1:
+        return [fn(x) for x in items]
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
+
+
 class DecodeCase:
     """A decode workload on the HIP path and on the oracle."""
 
@@ -121,6 +135,10 @@ class DecodeCase:
 
     def oracle_out(self, i: int) -> np.ndarray:
         return self.oracle.attend(i, self.vals["q"][i])
+
+    def oracle_all(self) -> np.ndarray:
+        """The oracle's output for every sequence, [B][H_q][d] float64."""
+        return np.stack(oracle_map(self.oracle_out, range(len(self.lens))))
 
     def close(self):
         self.pool.close()

@@ -1,10 +1,10 @@
 """GPU parity: write_kv, copy_blocks and paged_decode against the oracle.
 
 * every decode workload at its full size: block tables and slots bit-exact,
-  the whole written pool bit-exact, and attention outputs on a seeded sample
-  of sequences (all of them for the tiny workload) within the tolerance the
-  workload states: max |err| <= 1e-5 for fp32 inputs, <= 2e-3 for fp16/bf16
-  (fp32 accumulation, fp32 output);
+  the whole written pool bit-exact, and the attention output of every
+  sequence and head within the tolerance the workload states: max |err|
+  <= 1e-5 for fp32 inputs, <= 2e-3 for fp16/bf16 (fp32 accumulation, fp32
+  output);
 * each at the partition size the benchmark uses, at a second one and at the
   one fill mode picks, so both the single-partition and the split-K + reduce
   paths are compared;
@@ -32,18 +32,6 @@ PARTITIONS = {"tiny_f32": (0, 16), "gpt_f16": (0, 2048), "ragged_bf16": (0, 512)
               "gqa_long_bf16": (512, 0)}
 
 
-def sample_seqs(lens, k, seed):
-    lens = np.asarray(lens)
-    if len(lens) <= k:
-        return list(range(len(lens)))
-    rng = np.random.default_rng(seed)
-    pick = set(rng.choice(len(lens), size=k, replace=False).tolist())
-    pick |= {int(np.argmax(lens)), int(np.argmin(lens))}
-    for v in (60, 200, 1500):
-        pick |= set(np.nonzero(lens == v)[0].tolist())
-    return sorted(pick)
-
-
 def max_err(case, out, seqs):
     worst = 0.0
     for i in seqs:
@@ -64,15 +52,14 @@ def test_workload_parity(cfg):
         case.write_context()
         assert np.array_equal(device_bits(case.k_cache), host_bits(case.oracle.mirror.k))
         assert np.array_equal(device_bits(case.v_cache), host_bits(case.oracle.mirror.v))
-        seqs = sample_seqs(case.lens, 12, cfg.seed)
-        ref = {i: case.oracle_out(i) for i in seqs}
+        ref = case.oracle_all()  # every sequence
         # and the partition fill mode picks for this batch (the bench's default)
         wpi, resident = case.pool.decode_occupancy(cfg.num_q_heads)
         p_fill = fill_partition(case.lens, wpi, resident, 512) or default_partition_tokens()
         for P in PARTITIONS[cfg.name] + (p_fill,):
             for split in (False, True):
                 out, info = case.decode(P, split=split)
-                err = max(float(np.max(np.abs(out[i] - ref[i]))) for i in seqs)
+                err = float(np.max(np.abs(out - ref)))
                 print(f"[gpu] {cfg.name} P={info.partition_tokens} split={split} work={info.n_work} "
                       f"reduce={info.n_reduce} max_err={err:.3e}", flush=True)
                 assert err <= TOL[cfg.dtype], (P, split, err)
@@ -107,13 +94,12 @@ def test_fused_append_decode(cfg):
     case = DecodeCase(cfg, fill=float("nan"))
     try:
         case.write_context(skip_last=True)
-        seqs = sample_seqs(case.lens, 12, cfg.seed)
-        ref = {i: case.oracle_out(i) for i in seqs}
+        ref = case.oracle_all()  # every sequence
         wpi, resident = case.pool.decode_occupancy(cfg.num_q_heads)
         p_fill = fill_partition(case.lens, wpi, resident, 512) or default_partition_tokens()
         for P in (PARTITIONS[cfg.name][0], p_fill):
             out, info = case.decode(P, append=True)
-            err = max(float(np.max(np.abs(out[i] - ref[i]))) for i in seqs)
+            err = float(np.max(np.abs(out - ref)))
             print(f"[gpu] append-decode {cfg.name} P={info.partition_tokens} max_err={err:.3e}", flush=True)
             assert err <= TOL[cfg.dtype] and np.isfinite(out).all()
         # the newest rows landed in the pool: bit-exact everywhere a token lives

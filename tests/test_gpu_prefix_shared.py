@@ -5,8 +5,9 @@ their own tails; every iteration appends one token to each (copy-on-write on
 shared partly filled blocks, new blocks at boundaries), writes its K/V,
 decodes every sequence, retires 13 and admits 13 forks.  Checked against the
 oracle: slots, copy pairs and block tables bit-exact every iteration; the
-whole pool bit-exact after setup and at the end; attention outputs of a
-seeded sample of sequences at iterations 0, 1, 31 and 63 within 2e-3.
+whole pool bit-exact after setup and at the end; the attention output of
+every decoding sequence at iterations 0, 1, 31 and 63, and of a seeded
+sample of 16 at every other iteration, within 2e-3.
 Each iteration runs through the native stepper (one call: host half, upload
 on a side stream, copy-on-write copies, decode that stores the new tokens).
 """
@@ -18,16 +19,18 @@ import torch
 from oracle.runs import PrefixSharedRun, iteration_values, prefix_values
 from paged_kv_cache_257_amd import Pool
 from paged_kv_cache_257_amd.step import DecodeIteration
-from tests.gpu_helpers import TOL, TORCH_DTYPE, device_bits, host_bits, sync, to_device
+from tests.gpu_helpers import TOL, TORCH_DTYPE, device_bits, host_bits, oracle_map, sync, to_device
 from workloads.churn import choose_churn, draw_prefix_shared_plan
 from workloads.configs import PREFIX_SHARED
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
-CHECK_ITERS = (0, 1, 31, 63)
+CHECK_ITERS = (0, 1, 31, 63)  # every decoding sequence compared
+SAMPLE = 16                   # sequences compared at every other iteration
 
 
+@pytest.mark.timeout(1200)
 def test_prefix_shared_loop():
     cfg = PREFIX_SHARED
     plan = draw_prefix_shared_plan(cfg)
@@ -77,14 +80,17 @@ def test_prefix_shared_loop():
             assert np.array_equal(meta["host_lens"], np.asarray(l_o, np.int32)), it
             total_cow += meta["npairs"]
             ora.write_step(cow_o, k, v, slots_o)
+            sync()
+            got = out[:len(seqs)].cpu().numpy().astype(np.float64)
             if it in CHECK_ITERS:
-                sync()
-                got = out.cpu().numpy().astype(np.float64)
-                pick = sorted(rng.choice(len(seqs), size=8, replace=False).tolist())
-                err = max(float(np.max(np.abs(got[i] - ora.attend(seqs[i], q[i])))) for i in pick)
-                print(f"[gpu] prefix-shared it={it} work={meta['info'].n_work} cow={meta['npairs']} "
-                      f"max_err={err:.3e}", flush=True)
-                assert err <= TOL[dt], (it, err)
+                pick = list(range(len(seqs)))
+            else:
+                pick = sorted(rng.choice(len(seqs), size=min(SAMPLE, len(seqs)), replace=False).tolist())
+            ref = oracle_map(lambda i: ora.attend(seqs[i], q[i]), pick)
+            err = max(float(np.max(np.abs(got[i] - r))) for i, r in zip(pick, ref))
+            print(f"[gpu] prefix-shared it={it} work={meta['info'].n_work} cow={meta['npairs']} "
+                  f"checked={len(pick)} max_err={err:.3e}", flush=True)
+            assert err <= TOL[dt], (it, err)
             retire, parents = choose_churn(cfg, it, seqs)
             for s in retire:
                 pool.free(s)
