@@ -734,6 +734,26 @@ pkv_status pkv_paged_decode_reduce(const pkv_pool* pool, const void* q, const vo
                                    const int32_t* plan, const pkv_decode_plan_info* info,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* pkv_paged_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same kernels
+ * and results.  The split-K records and completion tickets live in a fixed
+ * scratch array inside the library, PKV_NOALLOC_SCRATCH_BYTES on each GPU
+ * the library runs on, held until the process ends; its device address is
+ * looked up once per device, on that device's first call.  A batch whose
+ * pkv_decode_workspace_bytes exceeds it is refused with PKV_E_BAD_ARG and
+ * nothing is launched.  The call allocates nothing; it clears the tickets it
+ * will use with a small kernel before the decode.  Every call on a GPU
+ * shares that GPU's scratch: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller. */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pkv_status pkv_paged_decode_noalloc(const pkv_pool* pool, const void* q, const void* k_new,
+                                    const void* v_new, float* out, int32_t num_seqs,
+                                    int32_t num_q_heads, const int32_t* block_tables,
+                                    int32_t table_stride, const int32_t* context_lens, float scale,
+                                    const int32_t* plan, const pkv_decode_plan_info* info,
+                                    void* stream);
+
 /* Causal attention of chunked-prefill queries through the block tables:
  * query t of sequence i (row q_start[i] + t of q and out) sits at position
  * context_lens[i] - q_lens[i] + t and attends to that sequence's positions

@@ -53,6 +53,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 
 #include "decode_launch.h"
 #include "device_common.h"
@@ -1029,4 +1030,77 @@ extern "C" pkv_status pkv_paged_decode_reduce(PKV_DECODE_ARGS) {
   (void)gw;
   (void)mfma;
   return launch_reduce(pool, prm, num_seqs, info, s);
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace, for callers that cannot allocate device
+// memory.  Its split-K records and completion tickets live in `scratch`, a
+// fixed array of this library's code object: every GPU the library runs on
+// holds one copy of PKV_NOALLOC_SCRATCH_BYTES until the process ends.  In
+// host code the array's name only stands for the device symbol; its device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current and kept in scratch_ptr.  Calls on one device share the
+// array: calls that overlap in time on one GPU race.
+static __device__ __align__(256) char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace pkv {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (set up on the first call
+// on that device).
+pkv_status current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_E_HIP, "no current HIP device for the decode scratch");
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PKV_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return PKV_OK;
+}
+
+// Zero n completion tickets (a plain kernel, not a memset node, so that the
+// call stays valid inside a captured graph).
+__global__ __launch_bounds__(256) void clear_tickets_kernel(int32_t* tickets, int n) {
+  const int i = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (i < n) tickets[i] = 0;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" pkv_status pkv_paged_decode_noalloc(const pkv_pool* pool, const void* q, const void* k_new,
+                                               const void* v_new, float* out, int32_t num_seqs,
+                                               int32_t num_q_heads, const int32_t* block_tables,
+                                               int32_t table_stride, const int32_t* context_lens,
+                                               float scale, const int32_t* plan,
+                                               const pkv_decode_plan_info* info, void* stream) {
+  if (!pool || !info) return fail(PKV_E_BAD_ARG, "null pool or plan info");
+  const size_t need = pkv_decode_workspace_bytes(info, num_q_heads, pool->desc.head_dim);
+  if (need > size_t(PKV_NOALLOC_SCRATCH_BYTES))
+    return fail(PKV_E_BAD_ARG, "this batch needs " + std::to_string(need) +
+                                   " bytes of split-K scratch; the no-allocation decode holds " +
+                                   std::to_string(size_t(PKV_NOALLOC_SCRATCH_BYTES)) +
+                                   " (use pkv_paged_decode with a workspace, or longer partitions)");
+  void* ws = nullptr;
+  if (pkv_status st = current_scratch(&ws)) return st;
+  const size_t workspace_bytes = size_t(PKV_NOALLOC_SCRATCH_BYTES);
+  void* workspace = ws;
+  PKV_SETUP
+  if (info->n_reduce > 0) {
+    // this launch's tickets start at zero whatever an earlier call left there
+    const int n = num_seqs * num_q_heads;
+    hipLaunchKernelGGL(clear_tickets_kernel, dim3(uint32_t((n + 255) / 256)), dim3(256), 0, s, prm.counters, n);
+    if (pkv_status st = launch_status("decode scratch ticket clear")) return st;
+  }
+  return launch_partitions(pool, prm, gw, mfma, info, s);
 }

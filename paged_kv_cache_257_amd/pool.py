@@ -210,6 +210,16 @@ class Pool:
         else:
             check(self.lib, self.lib.pkv_paged_decode(*args))
 
+    def paged_decode_noalloc(self, q, out, block_tables, context_lens, scale: float, plan, info: PlanInfo,
+                             stream=None, k_new=None, v_new=None) -> None:
+        """``paged_decode`` without a workspace: the library's fixed per-GPU
+        scratch holds the split-K records (see pkv_paged_decode_noalloc)."""
+        B, Hq = int(q.shape[0]), int(q.shape[1])
+        check(self.lib, self.lib.pkv_paged_decode_noalloc(
+            self.handle, _dptr(q), _dptr(k_new), _dptr(v_new), _dptr(out), B, Hq,
+            _dptr(block_tables), int(block_tables.shape[1]), _dptr(context_lens), float(scale),
+            _dptr(plan), C.byref(info), _stream_ptr(stream)))
+
 
     def paged_prefill(self, q, out, block_tables, context_lens, scale: float, plan,
                       info: PrefillPlanInfo, workspace=None, stream=None) -> None:

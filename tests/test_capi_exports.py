@@ -88,3 +88,12 @@ def test_misaligned_device_arrays_are_refused_before_any_launch():
         assert b"aligned" in lib.pkv_last_error()
     finally:
         lib.pkv_pool_destroy(h)
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    """The binding's copy of PKV_NOALLOC_SCRATCH_BYTES (used to size checks
+    and messages) is the header's value."""
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    m = re.search(r"#define PKV_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m, "PKV_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == _capi.NOALLOC_SCRATCH_BYTES
