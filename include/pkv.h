@@ -431,6 +431,14 @@ typedef struct {
    * context tokens lie in blocks held by more than one sequence.  Any value
    * gives the same results. */
   int32_t shared_kv;
+  /* Shared-block section (pkv_decode_plan_shared; all 0 from
+   * pkv_decode_plan): nodes of blocks held in common by several sequences
+   * of the batch, read once for all of them by a separate launch. */
+  int32_t n_nodes;             /* shared nodes (0: no shared section)         */
+  int32_t n_shared_items;      /* workgroups of the shared launch per KV head  */
+  int32_t shared_chunk_blocks; /* blocks per shared work item                  */
+  int32_t shared_group;        /* query heads per KV head the plan was made for */
+  int32_t off_shared;          /* int offset of the shared section in the plan */
 } pkv_decode_plan_info;
 
 /* Upper bound of the plan length for these lengths. */
@@ -439,6 +447,49 @@ pkv_status pkv_decode_plan_ints(const int32_t* context_lens, int32_t num_seqs, i
 pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
                            int32_t partition_tokens, int32_t* plan, int32_t cap,
                            pkv_decode_plan_info* info);
+
+/* Split-K plan of a batch of live sequences of `pool` that reads every block
+ * held in common by several of them once for all its holders ("PagedAttention
+ * e continuous batching", 01 · Conceito, paragraph 6: requests with an
+ * identical prompt prefix point at the same read-only blocks; "04 — Hacia
+ * PagedAttention", Propiedades: prefix sharing comes free).
+ *
+ * The sequences' tables are taken from the pool as they stand.  Sequences
+ * whose tables agree on a run of blocks form a node: blocks [j0, j1) of the
+ * table of its first member, which every member holds at the same positions,
+ * full in every member (a sequence's last block is never in a node).  Nodes
+ * nest like a prefix tree: the members of a node share all blocks of its
+ * ancestors.  A node's blocks are cut into chunks of shared_chunk_blocks and
+ * its members into column sets of 64 / group sequences; each (chunk, column
+ * set, KV head) is one workgroup of the shared launch, which reads the chunk
+ * once and writes one split-K record per member and query head.  Every
+ * sequence then attends over the rest of its blocks (from private_start) as
+ * in pkv_decode_plan, and its records, shared ones first, are combined.
+ * Nodes are built only when at least a quarter of the batch's context tokens
+ * lie in them, for fp16 / bf16 pools of head_dim 128 and group = num_q_heads
+ * / num_kv_heads dividing 16; otherwise the result is pkv_decode_plan's
+ * (with shared_kv set as pkv_batch_shared_kv would).  chunk_tokens: a
+ * multiple of block_size, or 0 (chunks sized so that the shared launch has
+ * about 512 workgroups, 16 to 256 blocks each).  A sequence's shared
+ * records (one per node chunk on its path) are capped at
+ * PKV_MAX_SHARED_RECORDS: a node stops where the cap would be passed.
+ *
+ * Layout: pkv_decode_plan's, then, from info->off_shared when n_nodes > 0,
+ *   [num_seqs]       private_start: first block of each sequence's own part
+ *   [num_seqs]       n_shared: shared records of each sequence
+ *   [num_seqs]       order: batch indices, each node's members contiguous
+ *   [8 * n_nodes]    nodes (rep, j0, j1, first member in order, members,
+ *                    first record, first shared item, column sets)
+ * where a member s of node v writes, for chunk c, the record at
+ * part_offset[s] + first record + c.  Upload it unchanged. */
+/* A sequence owns at most this many shared records (pkv_decode_plan_shared
+ * stops a node early rather than pass it; workspace bounds count on it). */
+#define PKV_MAX_SHARED_RECORDS 8
+pkv_status pkv_decode_plan_shared_ints(const pkv_pool* pool, const int32_t* seqs, int32_t n_seqs,
+                                       int32_t partition_tokens, int32_t* plan_ints);
+pkv_status pkv_decode_plan_shared(const pkv_pool* pool, const int32_t* seqs, int32_t n_seqs,
+                                  int32_t partition_tokens, int32_t num_q_heads, int32_t chunk_tokens,
+                                  int32_t* plan, int32_t cap, pkv_decode_plan_info* info);
 
 /* Device workspace bytes pkv_paged_decode needs for this plan: the split-K
  * partial records (from the workspace's start) and completion tickets for
@@ -451,8 +502,10 @@ size_t pkv_decode_workspace_bytes(const pkv_decode_plan_info* info, int32_t num_
                                   int32_t head_dim);
 
 /* Workspace bytes that suffice for every plan of at most max_seqs sequences
- * no longer than max_context_len tokens (0 on bad arguments); for callers
- * that size the workspace once. */
+ * no longer than max_context_len tokens, pkv_decode_plan's and
+ * pkv_decode_plan_shared's (each sequence may add PKV_MAX_SHARED_RECORDS
+ * shared records), 0 on bad arguments; for callers that size the workspace
+ * once. */
 size_t pkv_decode_workspace_bound(int32_t max_seqs, int32_t max_context_len, int32_t block_size,
                                   int32_t partition_tokens, int32_t num_q_heads, int32_t head_dim);
 
@@ -562,15 +615,18 @@ size_t pkv_prepare_decode_bytes(int32_t max_seqs, int32_t append_tokens, int32_t
  * paragraph 7: running sequences advance one token per iteration), in one
  * call: append append_tokens (0 or more) to each of seqs[0..n_seqs) in that
  * order (pkv_seq_append_batch), take the copy-on-write pairs, build block
- * tables and context lengths (pkv_build_batch) and the split-K plan
- * (pkv_decode_plan), all written into the host buffer `staging` (ideally
- * pinned) at the offsets returned in *layout.  Upload the first
- * layout->bytes bytes unchanged to a device buffer; the device arrays then
- * sit at the same offsets.  All or nothing: on error the pool is unchanged. */
+ * tables and context lengths (pkv_build_batch) and the split-K plan, all
+ * written into the host buffer `staging` (ideally pinned) at the offsets
+ * returned in *layout.  The plan is pkv_decode_plan_shared's for
+ * num_q_heads > 0 (blocks held in common read once for their holders) and
+ * pkv_decode_plan's with the load-policy hint for num_q_heads = 0.  Upload
+ * the first layout->bytes bytes unchanged to a device buffer; the device
+ * arrays then sit at the same offsets.  All or nothing: on error the pool is
+ * unchanged. */
 pkv_status pkv_prepare_decode(pkv_pool* pool, const int32_t* seqs, int32_t n_seqs,
                               int32_t append_tokens, int32_t table_stride,
-                              int32_t partition_tokens, void* staging, size_t staging_bytes,
-                              pkv_batch_layout* layout);
+                              int32_t partition_tokens, int32_t num_q_heads, void* staging,
+                              size_t staging_bytes, pkv_batch_layout* layout);
 
 /* The decode plan's K/V load-policy hint for a batch of live sequences
  * (pkv_decode_plan_info.shared_kv): 1 when at least a quarter of their

@@ -9,10 +9,10 @@ first call does, and raises if it is not built (there is no fallback).
 """
 
 from ._capi import PkvError, load  # noqa: F401
-from .pool import (Pool, decode_plan, decode_workspace_bound, decode_workspace_bytes,  # noqa: F401
+from .pool import (Pool, decode_plan, decode_plan_shared, decode_workspace_bound, decode_workspace_bytes,  # noqa: F401
                    default_partition_tokens, fill_partition, prefill_plan, prefill_workspace_bytes)
 
-__all__ = ["Pool", "PkvError", "decode_plan", "decode_workspace_bound", "decode_workspace_bytes",
+__all__ = ["Pool", "PkvError", "decode_plan", "decode_plan_shared", "decode_workspace_bound", "decode_workspace_bytes",
            "default_partition_tokens", "fill_partition", "prefill_plan", "prefill_workspace_bytes", "load",
            "DecodeIteration", "PagedKVCache", "attention"]
 

@@ -17,6 +17,7 @@ STATUS_KIND = {E_NO_BLOCKS: "no_blocks", E_BAD_SEQ: "bad_seq", E_BAD_ARG: "bad_a
                E_NO_SLOTS: "no_slots"}
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES of include/pkv.h
+MAX_SHARED_RECORDS = 8            # PKV_MAX_SHARED_RECORDS of include/pkv.h
 
 
 class PoolDesc(C.Structure):
@@ -37,7 +38,8 @@ class Stats(C.Structure):
 class PlanInfo(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("num_seqs", "block_size", "partition_tokens", "n_work",
                                          "n_reduce", "n_partials", "plan_ints", "max_context_len",
-                                         "shared_kv")]
+                                         "shared_kv", "n_nodes", "n_shared_items", "shared_chunk_blocks",
+                                         "shared_group", "off_shared")]
 
 
 class PrefillPlanInfo(C.Structure):
@@ -163,6 +165,8 @@ SIGNATURES = {
     "pkv_hybrid_plan": [C.c_int64, C.c_int64, I32, C.c_int64, C.c_int64, PI32, PI32, PI32],
     "pkv_decode_plan_ints": [PI32, I32, I32, I32, PI32],
     "pkv_decode_plan": [PI32, I32, I32, I32, PI32, I32, C.POINTER(PlanInfo)],
+    "pkv_decode_plan_shared_ints": [P, PI32, I32, I32, PI32],
+    "pkv_decode_plan_shared": [P, PI32, I32, I32, I32, I32, PI32, I32, C.POINTER(PlanInfo)],
     "pkv_decode_workspace_bytes": [C.POINTER(PlanInfo), I32, I32],
     "pkv_decode_workspace_bound": [I32, I32, I32, I32, I32, I32],
     "pkv_default_partition_tokens": [],
@@ -172,7 +176,7 @@ SIGNATURES = {
     "pkv_prefill_plan": [PI32, PI32, I32, I32, I32, I32, PI32, I32, C.POINTER(PrefillPlanInfo)],
     "pkv_prefill_workspace_bytes": [C.POINTER(PrefillPlanInfo), I32],
     "pkv_prepare_decode_bytes": [I32, I32, I32, I32, I32],
-    "pkv_prepare_decode": [P, PI32, I32, I32, I32, I32, P, C.c_size_t, C.POINTER(BatchLayout)],
+    "pkv_prepare_decode": [P, PI32, I32, I32, I32, I32, I32, P, C.c_size_t, C.POINTER(BatchLayout)],
     "pkv_batch_shared_kv": [P, PI32, I32, PI32],
     "pkv_stepper_slot_bytes": [I32, I32, I32, I32],
     "pkv_stepper_create": [P, I32, I32, I32, I32, P, P, C.c_size_t, P, C.c_size_t, P, C.POINTER(P)],

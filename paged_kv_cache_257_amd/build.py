@@ -27,7 +27,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")
 ARCH = "gfx950"
 
-HOST_SOURCES = ["host/pool.cpp", "host/plan.cpp", "host/prepare.cpp", "host/prefill_plan.cpp",
+HOST_SOURCES = ["host/pool.cpp", "host/plan.cpp", "host/plan_shared.cpp", "host/prepare.cpp", "host/prefill_plan.cpp",
                 "host/utilisation.cpp", "host/hybrid.cpp", "host/sched.cpp"]
 HIP_SOURCES = ["kernels/kv_write.hip", "kernels/paged_decode.hip", "kernels/paged_prefill.hip",
                "kernels/stepper.cpp"]

@@ -31,55 +31,34 @@ pkv_status check_lens(const int32_t* lens, int32_t n, int32_t bs, int32_t& P, in
 
 }  // namespace
 
-namespace {
+namespace pkv {
 
-struct PlanCounts {
-  int64_t work = 0, reduce = 0, partials = 0;
-};
-
-PlanCounts count_plan(const int32_t* lens, int32_t n, int32_t P) {
-  PlanCounts c;
+// Work items, record offsets and reduce list of a split-K plan over the
+// private blocks of each sequence: blocks [first_block[i], nblk_i) (all
+// blocks when first_block is null), cut into partitions of P tokens.  A
+// sequence also owns n_shared[i] records written before (null: none); its
+// records are then its shared ones followed by one per private partition.
+// Writes plan[0 .. 2 n_work + n + n_reduce) and the matching info fields.
+pkv_status fill_private_plan(const int32_t* lens, int32_t n, int32_t bs, int32_t P,
+                             const int32_t* first_block, const int32_t* n_shared, int32_t* plan,
+                             int64_t cap, pkv_decode_plan_info* info) {
+  const int32_t pblocks = P / bs;
+  auto priv_blocks = [&](int32_t i) {
+    const int32_t nblk = (lens[i] + bs - 1) / bs;
+    return nblk - (first_block ? first_block[i] : 0);
+  };
+  int64_t work = 0, reduce = 0;
   for (int32_t i = 0; i < n; ++i) {
-    const int64_t parts = (int64_t(lens[i]) + P - 1) / P;
-    c.work += parts;
-    if (parts > 1) {
-      c.reduce++;
-      c.partials += parts;
-    }
+    const int64_t parts = (int64_t(priv_blocks(i)) + pblocks - 1) / pblocks;
+    work += parts;
+    if (parts + (n_shared ? n_shared[i] : 0) > 1) reduce++;
   }
-  return c;
-}
-
-}  // namespace
-
-extern "C" {
-
-pkv_status pkv_decode_plan_ints(const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
-                                int32_t partition_tokens, int32_t* plan_ints) {
-  if (!plan_ints) return fail(PKV_E_BAD_ARG, "null plan_ints");
-  int32_t P = partition_tokens, max_len = 0;
-  if (pkv_status st = check_lens(context_lens, num_seqs, block_size, P, max_len)) return st;
-  const PlanCounts c = count_plan(context_lens, num_seqs, P);
-  const int64_t total = 2 * c.work + num_seqs + c.reduce;
-  if (total > INT32_MAX) return fail(PKV_E_BAD_ARG, "plan too large");
-  *plan_ints = int32_t(total);
-  return PKV_OK;
-}
-
-pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
-                           int32_t partition_tokens, int32_t* plan, int32_t cap,
-                           pkv_decode_plan_info* info) {
-  if (!info) return fail(PKV_E_BAD_ARG, "null info");
-  int32_t P = partition_tokens, max_len = 0;
-  if (pkv_status st = check_lens(context_lens, num_seqs, block_size, P, max_len)) return st;
-  const PlanCounts c = count_plan(context_lens, num_seqs, P);
-  const int64_t need = 2 * c.work + num_seqs + c.reduce;
+  const int64_t need = 2 * work + n + reduce;
   if (need > INT32_MAX) return fail(PKV_E_BAD_ARG, "plan too large");
   if (cap < need || (need > 0 && !plan)) return fail(PKV_E_BAD_ARG, "plan buffer too small");
-  const int32_t pblocks = P / block_size;
-  const int32_t n_work = int32_t(c.work);
+  const int32_t n_work = int32_t(work);
   int32_t* part_offset = plan + 2 * int64_t(n_work);
-  int32_t* reduce = part_offset + num_seqs;
+  int32_t* reduce_list = part_offset + n;
 
   // Counting sort of the work items by their block count, longest first;
   // ties in partition-major order (partition 0 of every sequence, then
@@ -90,17 +69,19 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
   // Scratch is reused across calls.
   thread_local std::vector<int32_t> start;
   start.assign(size_t(pblocks) + 2, 0);
-  int32_t n_reduce = 0, n_partials = 0;
-  for (int32_t i = 0; i < num_seqs; ++i) {
-    const int32_t nblk = (context_lens[i] + block_size - 1) / block_size;
-    const int32_t parts = (nblk + pblocks - 1) / pblocks;
-    const int32_t last = nblk - (parts - 1) * pblocks;  // blocks of the last partition
+  int32_t n_reduce = 0, n_partials = 0, max_parts = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t nb = priv_blocks(i);
+    const int32_t parts = (nb + pblocks - 1) / pblocks;
+    const int32_t last = nb - (parts - 1) * pblocks;  // blocks of the last partition
+    const int32_t records = parts + (n_shared ? n_shared[i] : 0);
+    max_parts = std::max(max_parts, parts);
     start[pblocks] += parts - 1;
     start[last] += 1;
-    if (parts > 1) {
+    if (records > 1) {
       part_offset[i] = n_partials;
-      n_partials += parts;
-      reduce[n_reduce++] = i;
+      n_partials += records;
+      reduce_list[n_reduce++] = i;
     } else {
       part_offset[i] = -1;
     }
@@ -112,25 +93,21 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
     start[b] = pos;
     pos += cnt;
   }
-  int32_t max_parts = 0;
-  for (int32_t i = 0; i < num_seqs; ++i) {
-    const int32_t nblk = (context_lens[i] + block_size - 1) / block_size;
-    max_parts = std::max(max_parts, (nblk + pblocks - 1) / pblocks);
-  }
   for (int32_t q = 0; q < max_parts; ++q) {
-    for (int32_t i = 0; i < num_seqs; ++i) {
-      const int32_t nblk = (context_lens[i] + block_size - 1) / block_size;
-      const int32_t parts = (nblk + pblocks - 1) / pblocks;
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t nb = priv_blocks(i);
+      const int32_t parts = (nb + pblocks - 1) / pblocks;
       if (q >= parts) continue;
-      const int32_t b = q + 1 < parts ? pblocks : nblk - q * pblocks;
+      const int32_t b = q + 1 < parts ? pblocks : nb - q * pblocks;
       const int32_t w = start[b]++;
       plan[2 * w] = i;
       plan[2 * w + 1] = q;
     }
   }
-
-  info->num_seqs = num_seqs;
-  info->block_size = block_size;
+  int32_t max_len = 0;
+  for (int32_t i = 0; i < n; ++i) max_len = std::max(max_len, lens[i]);
+  info->num_seqs = n;
+  info->block_size = bs;
   info->partition_tokens = P;
   info->n_work = n_work;
   info->n_reduce = n_reduce;
@@ -138,7 +115,40 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
   info->plan_ints = int32_t(need);
   info->max_context_len = max_len;
   info->shared_kv = 0;
+  info->n_nodes = 0;
+  info->n_shared_items = 0;
+  info->shared_chunk_blocks = 0;
+  info->shared_group = 0;
+  info->off_shared = 0;
   return PKV_OK;
+}
+
+}  // namespace pkv
+
+extern "C" {
+
+pkv_status pkv_decode_plan_ints(const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                                int32_t partition_tokens, int32_t* plan_ints) {
+  if (!plan_ints) return fail(PKV_E_BAD_ARG, "null plan_ints");
+  int32_t P = partition_tokens, max_len = 0;
+  if (pkv_status st = check_lens(context_lens, num_seqs, block_size, P, max_len)) return st;
+  int64_t total = num_seqs;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int64_t parts = (int64_t(context_lens[i]) + P - 1) / P;
+    total += 2 * parts + (parts > 1 ? 1 : 0);
+  }
+  if (total > INT32_MAX) return fail(PKV_E_BAD_ARG, "plan too large");
+  *plan_ints = int32_t(total);
+  return PKV_OK;
+}
+
+pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                           int32_t partition_tokens, int32_t* plan, int32_t cap,
+                           pkv_decode_plan_info* info) {
+  if (!info) return fail(PKV_E_BAD_ARG, "null info");
+  int32_t P = partition_tokens, max_len = 0;
+  if (pkv_status st = check_lens(context_lens, num_seqs, block_size, P, max_len)) return st;
+  return pkv::fill_private_plan(context_lens, num_seqs, block_size, P, nullptr, nullptr, plan, cap, info);
 }
 
 int32_t pkv_default_partition_tokens(void) { return pkv::kDefaultPartitionTokens; }
@@ -183,7 +193,9 @@ size_t pkv_decode_workspace_bound(int32_t max_seqs, int32_t max_context_len, int
   worst.num_seqs = max_seqs;
   worst.block_size = block_size;
   worst.partition_tokens = P;
-  const int64_t partials = parts > 1 ? int64_t(max_seqs) * parts : 0;
+  // a shared-block plan: every sequence's private partitions plus its capped
+  // shared records (at least as many as an unshared plan's partials)
+  const int64_t partials = int64_t(max_seqs) * (parts + PKV_MAX_SHARED_RECORDS);
   if (partials > INT32_MAX) return 0;
   worst.n_partials = int32_t(partials);
   return pkv_decode_workspace_bytes(&worst, num_q_heads, head_dim);

@@ -120,6 +120,21 @@ inline int32_t sizing_partition(int32_t P) {
 // waves of two 16-row groups each.
 constexpr int32_t kPrefillTileRows = 128;
 
+// Split-K plan over each sequence's private blocks (plan.cpp).
+pkv_status fill_private_plan(const int32_t* lens, int32_t n, int32_t bs, int32_t P,
+                             const int32_t* first_block, const int32_t* n_shared, int32_t* plan,
+                             int64_t cap, pkv_decode_plan_info* info);
+
+// Shared-block plan of a batch of live sequences (plan_shared.cpp): lens and
+// shared_kv out; see pkv_decode_plan_shared.
+pkv_status build_shared_plan(const pkv_pool* p, const int32_t* seqs, int32_t n, int32_t P,
+                             int32_t num_q_heads, int32_t chunk_tokens, int32_t* plan, int64_t cap,
+                             pkv_decode_plan_info* info);
+
+// Upper bound of the ints build_shared_plan writes for n sequences whose
+// tables hold at most the given total of blocks.
+int64_t shared_plan_bound(int64_t n, int64_t total_blocks, int32_t pblocks);
+
 // Live sequence with this id, or null.
 inline pkv_seq_state* find_seq(pkv_pool* p, int32_t id) {
   const int32_t s = p->index.find(id);

@@ -61,7 +61,7 @@ bool shares_context(const pkv_pool* p, const int32_t* seqs, int32_t n) {
 
 int64_t plan_cap_for(int64_t n, int64_t stride, int32_t bs, int32_t P) {
   const int64_t max_parts = (stride * bs + P - 1) / P;
-  return 2 * n * max_parts + 2 * n;
+  return std::max(2 * n * max_parts + 2 * n, pkv::shared_plan_bound(n, n * stride, P / bs));
 }
 
 }  // namespace
@@ -90,11 +90,13 @@ pkv_status pkv_batch_shared_kv(const pkv_pool* p, const int32_t* seqs, int32_t n
 
 pkv_status pkv_prepare_decode(pkv_pool* p, const int32_t* seqs, int32_t n_seqs,
                               int32_t append_tokens, int32_t table_stride,
-                              int32_t partition_tokens, void* staging, size_t staging_bytes,
-                              pkv_batch_layout* layout) {
+                              int32_t partition_tokens, int32_t num_q_heads, void* staging,
+                              size_t staging_bytes, pkv_batch_layout* layout) {
   if (!p || !layout || !staging) return fail(PKV_E_BAD_ARG, "null pool, staging or layout");
   if (n_seqs < 0 || append_tokens < 0 || table_stride < 1 || (n_seqs > 0 && !seqs))
     return fail(PKV_E_BAD_ARG, "bad batch arguments");
+  if (num_q_heads < 0 || (num_q_heads > 0 && num_q_heads % p->desc.num_kv_heads != 0))
+    return fail(PKV_E_BAD_ARG, "num_q_heads must be 0 or a positive multiple of num_kv_heads");
   const int32_t bs = p->desc.block_size;
   const int32_t P = partition_tokens ? partition_tokens : pkv::kDefaultPartitionTokens;
   if (P < bs || P % bs != 0)
@@ -129,10 +131,16 @@ pkv_status pkv_prepare_decode(pkv_pool* p, const int32_t* seqs, int32_t n_seqs,
   pkv_take_cow(p, pairs, int32_t(pair_cap), &n_pairs);
   pkv_build_batch(p, seqs, n_seqs, tables, table_stride, lens);
   pkv_decode_plan_info info{};
-  if (pkv_status st = pkv_decode_plan(lens, n_seqs, bs, P, plan,
-                                      int32_t(plan_cap_for(n_seqs, table_stride, bs, P)), &info))
-    return st;  // unreachable: lengths were checked above
-  info.shared_kv = shares_context(p, seqs, n_seqs) ? 1 : 0;
+  const int64_t cap = plan_cap_for(n_seqs, table_stride, bs, P);
+  if (num_q_heads > 0) {
+    // blocks held in common are read once for all their holders
+    if (pkv_status st = pkv::build_shared_plan(p, seqs, n_seqs, P, num_q_heads, 0, plan, cap, &info))
+      return st;  // unreachable: ids and lengths were checked above
+  } else {
+    if (pkv_status st = pkv_decode_plan(lens, n_seqs, bs, P, plan, int32_t(cap), &info))
+      return st;  // unreachable: lengths were checked above
+    info.shared_kv = shares_context(p, seqs, n_seqs) ? 1 : 0;
+  }
   layout->n_seqs = n_seqs;
   layout->append_tokens = append_tokens;
   layout->n_pairs = n_pairs;

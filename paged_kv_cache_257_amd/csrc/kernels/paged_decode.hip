@@ -75,6 +75,8 @@ struct DecodeParams {
   const int32_t* context_lens;
   const int32_t* work;         // [n_work][2] (sequence, partition)
   const int32_t* part_offset;  // [num_seqs] first partial index or -1
+  const int32_t* priv_start;   // [num_seqs] first block of the sequence's own part, or null (0)
+  const int32_t* n_shared;     // [num_seqs] records the shared launch wrote, or null (0)
   float* part;                 // [n_partials][H_q] records of rec_floats
   int32_t* counters;           // [num_seqs][H_q] completion tickets, or null
   int32_t rec_floats;          // record: o[D], m, l, padded to whole 128-byte lines
@@ -92,22 +94,38 @@ struct DecodeParams {
 // The end of a work item, shared by both decode kernels.  sm_m, sm_l
 // ([NSUB][GW]) and sm_o ([NSUB][GW][D]) hold the workgroup's NSUB partial
 // softmax states per query head (base-2 maxima in scaled units), written
-// before a barrier.  They are merged; a single-partition sequence writes
-// o / l, otherwise the partition's (o, m, l) becomes a record and the last
-// partition to finish combines all records of the (sequence, head group).
+// before a barrier.  They are merged.  A sequence owns n_sh records written
+// by the shared launch (blocks it holds in common with others), then one
+// per partition of its own blocks.
+//  * one partition and no shared record: the item writes o / l;
+//  * one partition and shared records (combine fused in): the item merges
+//    its state with the shared records and writes the output;
+//  * otherwise the partition's (o, m, l) becomes a record and the last
+//    partition to finish combines all records of the (sequence, head group)
+//    (without tickets, the two-launch variant, a separate kernel does).
 template <int D, int GW, int NSUB, int NT>
 __device__ __forceinline__ void finish_item(const DecodeParams& p, const float* sm_m, const float* sm_l,
-                                            const float* sm_o, int seq, int part, int n_parts, int hg,
-                                            int hgroups, int qh0) {
-  const bool single = (n_parts <= 1);
-  const int pidx = single ? -1 : p.part_offset[seq] + part;
-  if (!single && (pidx < 0 || pidx >= p.n_partials)) return;
+                                            const float* sm_o, int seq, int part, int n_parts, int n_sh,
+                                            int hg, int hgroups, int qh0) {
+  const int n_rec = n_sh + n_parts;
+  const bool single = (n_rec <= 1);
+  const bool fold = (n_parts == 1 && n_sh > 0 && p.counters != nullptr);
+  const int base = single ? -1 : p.part_offset[seq];
+  if (!single && (base < 0 || base + n_rec > p.n_partials)) return;
+  const int pidx = base + n_sh + part;
+  const int64_t step = int64_t(p.num_q_heads) * p.rec_floats;
   for (int idx = threadIdx.x; idx < GW * D; idx += NT) {
     const int g = idx / D;
     const int dd = idx - g * D;
     float M = -INFINITY;
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) M = fmaxf(M, sm_m[s * GW + g]);
+    const int qh = qh0 + g;
+    const float* rec0 = p.part + (int64_t(base) * p.num_q_heads + qh) * p.rec_floats;
+    if (fold) {
+      for (int q = 0; q < n_sh; ++q)
+        M = fmaxf(M, __hip_atomic_load(rec0 + q * step + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    }
     const float M_use = (M == -INFINITY) ? 0.f : M;
     float num = 0.f, den = 0.f;
 #pragma unroll
@@ -116,8 +134,17 @@ __device__ __forceinline__ void finish_item(const DecodeParams& p, const float* 
       num = __builtin_fmaf(w, sm_o[(s * GW + g) * D + dd], num);
       den = __builtin_fmaf(w, sm_l[s * GW + g], den);
     }
-    const int qh = qh0 + g;
-    if (single) {
+    if (fold) {
+      // the shared records were written by the launch before this one
+      for (int q = 0; q < n_sh; ++q) {
+        const float* rec = rec0 + q * step;
+        const float w = __builtin_amdgcn_exp2f(
+            __hip_atomic_load(rec + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M_use);
+        num = __builtin_fmaf(w, __hip_atomic_load(rec + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), num);
+        den = __builtin_fmaf(w, __hip_atomic_load(rec + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), den);
+      }
+    }
+    if (single || fold) {
       p.out[(int64_t(seq) * p.num_q_heads + qh) * D + dd] = num / den;
     } else {
       // partial record of (partition, query head): agent-scope stores, so
@@ -130,12 +157,12 @@ __device__ __forceinline__ void finish_item(const DecodeParams& p, const float* 
       }
     }
   }
-  if (single || p.counters == nullptr) return;
+  if (single || fold || p.counters == nullptr) return;
 
   // Split-K combine in the same launch.  Each workgroup of a (sequence, head
   // group) waits until its partial stores have completed, takes a ticket, and
-  // the one taking the last ticket combines every partition's record and
-  // resets the ticket for the next launch.
+  // the one taking the last ticket combines every record of the sequence
+  // (shared ones included) and resets the ticket for the next launch.
   // Ordering.  Writer side: every thread's record stores are agent-scope
   // atomic stores, waited for (s_waitcnt) before the workgroup barrier, and
   // the barrier orders them before thread 0's ticket add; the records are
@@ -158,20 +185,17 @@ __device__ __forceinline__ void finish_item(const DecodeParams& p, const float* 
   }
   __syncthreads();
   if (!sm_last) return;
-  const int base = p.part_offset[seq];
-  if (base < 0 || base + n_parts > p.n_partials) return;
   for (int idx = threadIdx.x; idx < GW * D; idx += NT) {
     const int g = idx / D;
     const int dd = idx - g * D;
     const int qh = qh0 + g;
     const float* rec0 = p.part + (int64_t(base) * p.num_q_heads + qh) * p.rec_floats;
-    const int64_t step = int64_t(p.num_q_heads) * p.rec_floats;
     float M = -INFINITY;
-    for (int q = 0; q < n_parts; ++q)
+    for (int q = 0; q < n_rec; ++q)
       M = fmaxf(M, __hip_atomic_load(rec0 + q * step + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     const float M_use = (M == -INFINITY) ? 0.f : M;
     float num = 0.f, den = 0.f;
-    for (int q = 0; q < n_parts; ++q) {
+    for (int q = 0; q < n_rec; ++q) {
       const float* rec = rec0 + q * step;
       const float w = __builtin_amdgcn_exp2f(
           __hip_atomic_load(rec + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M_use);
@@ -236,8 +260,10 @@ __global__ __launch_bounds__(kWave* NW, (decode_waves_hint<DT, D, GW>())) void p
   const int qh0 = kvh * p.group + (hg - kvh * p.hgroups_per_kv) * GW;
   const int L = p.context_lens[seq];
   const int nblk = min((L + kBlockTokens - 1) / kBlockTokens, p.table_stride);
-  const int n_parts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
-  const int b0 = part * p.partition_blocks;
+  const int ps = p.priv_start ? p.priv_start[seq] : 0;  // blocks before it: shared launch
+  const int n_sh = p.n_shared ? p.n_shared[seq] : 0;
+  const int n_parts = (nblk - ps + p.partition_blocks - 1) / p.partition_blocks;
+  const int b0 = ps + part * p.partition_blocks;
   const int b1 = min(b0 + p.partition_blocks, nblk);
 
   const int rg = lane / LPR;  // row group
@@ -418,7 +444,7 @@ __global__ __launch_bounds__(kWave* NW, (decode_waves_hint<DT, D, GW>())) void p
   }
   __syncthreads();
 
-  finish_item<D, GW, NW * RPI, kWave * NW>(p, sm_m, sm_l, sm_o, seq, part, n_parts, hg, hgroups, qh0);
+  finish_item<D, GW, NW * RPI, kWave * NW>(p, sm_m, sm_l, sm_o, seq, part, n_parts, n_sh, hg, hgroups, qh0);
 }
 
 // ---------------------------------------------------------------------------
@@ -499,8 +525,10 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
   const int qh0 = kvh * p.group + (hg - kvh * p.hgroups_per_kv) * GW;
   const int L = p.context_lens[seq];
   const int nblk = min((L + kBlockTokens - 1) / kBlockTokens, p.table_stride);
-  const int n_parts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
-  const int b0 = part * p.partition_blocks;
+  const int ps = p.priv_start ? p.priv_start[seq] : 0;  // blocks before it: shared launch
+  const int n_sh = p.n_shared ? p.n_shared[seq] : 0;
+  const int n_parts = (nblk - ps + p.partition_blocks - 1) / p.partition_blocks;
+  const int b0 = ps + part * p.partition_blocks;
   const int b1 = min(b0 + p.partition_blocks, nblk);
   const bool writes_new = (hg - kvh * p.hgroups_per_kv) == 0;
   const float c2 = p.scale_log2;
@@ -668,7 +696,258 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
   }
   __syncthreads();
 
-  finish_item<D, GW, NW, kWave * NW>(p, sm_m, sm_l, sm_o, seq, part, n_parts, hg, hgroups, qh0);
+  finish_item<D, GW, NW, kWave * NW>(p, sm_m, sm_l, sm_o, seq, part, n_parts, n_sh, hg, hgroups, qh0);
+}
+
+// ---------------------------------------------------------------------------
+// Shared-block decode (fp16 / bf16, head_dim 128): blocks held in common by
+// several sequences of the batch, read once for all of them.
+//
+// Forked sequences point at the same read-only blocks ("PagedAttention e
+// continuous batching", 01 · Conceito, paragraph 6).  The host plan groups
+// such sequences into nodes (a run of blocks every member holds at the same
+// table positions) and cuts each node into chunks of blocks and column sets
+// of members.  One workgroup takes one (chunk, column set, KV head): its
+// columns are the (member, query head) pairs of the set, up to 64, that read
+// this KV head, so S^T = K Q^T (16 tokens x 64 columns per block) and
+// O^T += V^T P^T are real dense products for the matrix cores even where
+// every sequence has a single query head (MHA).
+//
+// The workgroup stages four blocks at a time through LDS: all 256 threads
+// load the K and V tiles (one 16-byte load each per block and pool, every
+// load instruction 1 KiB contiguous), the next stage's loads are in flight
+// while the current stage is computed from LDS, and every wave reads the
+// staged tiles it needs.  With C column tiles of 16 (C = 1, 2 or 4 after
+// rounding up), wave w serves column tile w / (4 / C) and takes every
+// (4 / C)-th block of the stage; waves of one tile merge through LDS at the
+// end.  Operand layouts are those of the grouped-query kernel above (K rows
+// as the A operand of the 16x16x32 product, V rows paired into the A operand
+// of the 16x16x16 product, the score accumulator reused as its B operand),
+// and so is the online softmax.  Each column's (o, m, l) becomes the split-K
+// record of its (member, query head) for this chunk; the decode launch that
+// follows merges them with the member's own blocks.
+// Every block in a node is full in every member (a sequence's last block is
+// never shared), so only table entries outside the pool are masked.
+struct SharedParams {
+  const char* q;
+  const char* k_cache;
+  const char* v_cache;
+  const int32_t* block_tables;
+  const int32_t* part_offset;  // [num_seqs] first record of each sequence
+  const int32_t* order;        // [num_seqs] batch indices, node members contiguous
+  const int32_t* nodes;        // [n_nodes][8]
+  float* part;
+  int32_t rec_floats;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t table_stride;
+  int32_t num_blocks;
+  int32_t n_nodes;
+  int32_t chunk_blocks;
+  int32_t per_set;  // members per column set: 64 / group
+  int32_t n_partials;
+  float scale_log2;
+};
+
+constexpr int kSharedStage = 4;  // blocks per LDS stage
+constexpr int kSharedRowB = 256 + 16;  // LDS bytes per staged token row (padded against bank conflicts)
+
+template <int DT, int CP>
+__global__ __launch_bounds__(256, 2) void paged_decode_shared_kernel(const SharedParams p) {
+  constexpr int D = 128;
+  constexpr int R = D * 2;
+  constexpr int TILE = kBlockTokens * R;
+  constexpr int TILE_LDS = kBlockTokens * kSharedRowB;
+  // stage: K tiles then V tiles of kSharedStage blocks; reused for the merge
+  __shared__ __attribute__((aligned(16))) char sm[2 * kSharedStage * TILE_LDS];
+  static_assert(sizeof(sm) >= 4 * 16 * (D + 2) * sizeof(float), "merge area");
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int item = blockIdx.x / p.num_kv_heads;
+  const int kvh = blockIdx.x - item * p.num_kv_heads;
+
+  // the node holding this item: the last one whose first item is <= item
+  int lo = 0, hi = p.n_nodes - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.nodes[8 * mid + 6] <= item) lo = mid;
+    else hi = mid - 1;
+  }
+  const int32_t* nd = p.nodes + 8 * lo;
+  const int rep = nd[0], j0 = nd[1], j1 = nd[2], first = nd[3], members = nd[4], k_base = nd[5];
+  const int colsets = nd[7];
+  const int local = item - nd[6];
+  const int chunk = local / colsets;
+  const int cset = local - chunk * colsets;
+  const int b0 = j0 + chunk * p.chunk_blocks;
+  const int b1 = min(j1, b0 + p.chunk_blocks);
+  const int m0 = cset * p.per_set;
+  const int cols = min(p.per_set, members - m0) * p.group;
+  const int ct = (cols + 15) >> 4;
+  const int ctp = ct <= 1 ? 1 : ct <= 2 ? 2 : 4;  // column tiles, rounded up to a power of two
+  const int wpt = 4 / ctp;                        // waves per column tile
+  const int tile = wave / wpt;
+  const int sub = wave - tile * wpt;
+  const float c2 = p.scale_log2;
+
+  // this lane's column: (member, query head) of the set; columns past the
+  // set repeat its first one and write nothing
+  const int col = tile * 16 + n;
+  const bool col_ok = col < cols;
+  const int cc = col_ok ? col : 0;
+  const int mem = p.order[first + m0 + cc / p.group];
+  const int qh = kvh * p.group + (cc - (cc / p.group) * p.group);
+  u32x4 qb[4];
+  {
+    const char* qrow = p.q + (int64_t(mem) * p.num_q_heads + qh) * R;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) qb[kc] = *reinterpret_cast<const u32x4*>(qrow + 64 * kc + 16 * g);
+  }
+  float m = kNegBig, lsum = 0.f;
+  f4 o[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) o[t] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* trow = p.block_tables + int64_t(rep) * p.table_stride;
+  const int64_t blk_stride = int64_t(p.num_kv_heads) * TILE;
+  const int tid = threadIdx.x;
+  // staging: thread tid moves bytes [16 tid, 16 tid + 16) of each tile, i.e.
+  // token tid / 16, dims 8 (tid % 16) .. + 7
+  const int st_off = (tid >> 4) * kSharedRowB + 16 * (tid & 15);
+  u32x4 rk[kSharedStage], rv[kSharedStage];
+  auto issue = [&](int sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kSharedStage; ++i) {
+      const int j = sb + i;
+      const int blk = j < b1 ? trow[j] : -1;
+      const bool ok = unsigned(blk) < unsigned(p.num_blocks);
+      const int64_t tile_off = int64_t(ok ? blk : 0) * blk_stride + int64_t(kvh) * TILE;
+      rk[i] = load_tile<CP>(make_rsrc(p.k_cache + tile_off, ok ? TILE : 0), 16 * tid);
+      rv[i] = load_tile<CP>(make_rsrc(p.v_cache + tile_off, ok ? TILE : 0), 16 * tid);
+    }
+  };
+
+  issue(b0);
+  for (int sb = b0; sb < b1; sb += kSharedStage) {
+    __syncthreads();  // every wave is done with the previous stage
+#pragma unroll
+    for (int i = 0; i < kSharedStage; ++i) {
+      *reinterpret_cast<u32x4*>(sm + i * TILE_LDS + st_off) = rk[i];
+      *reinterpret_cast<u32x4*>(sm + (kSharedStage + i) * TILE_LDS + st_off) = rv[i];
+    }
+    __syncthreads();
+    issue(sb + kSharedStage);  // past b1: no records, nothing read
+    const int nb = min(kSharedStage, b1 - sb);
+    for (int i = sub; i < nb; i += wpt) {
+      const char* kl = sm + i * TILE_LDS;
+      const char* vl = sm + (kSharedStage + i) * TILE_LDS;
+      const bool blk_ok = unsigned(trow[sb + i]) < unsigned(p.num_blocks);
+      f4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        sacc = mfma_k32<DT>(*reinterpret_cast<const u32x4*>(kl + n * kSharedRowB + 64 * kc + 16 * g), qb[kc], sacc);
+      float sc[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
+      if (!blk_ok) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = -INFINITY;
+      }
+      const float mx = max_over_lane_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+      const float mn = fmaxf(m, mx * c2);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c2, -mn));
+      lsum = lsum * alpha + ((x[0] + x[1]) + (x[2] + x[3]));
+      const f2 x01 = {x[0], x[1]}, x23 = {x[2], x[3]};
+      u32x2 pb, pl;
+      if constexpr (DT == PKV_F16) {
+        pb = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01, h2)),
+                   __builtin_bit_cast(uint32_t, __builtin_convertvector(x23, h2))};
+      } else {
+        const b2 h01 = __builtin_convertvector(x01, b2), h23 = __builtin_convertvector(x23, b2);
+        pb = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+        pl = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01 - __builtin_convertvector(h01, f2), b2)),
+                   __builtin_bit_cast(uint32_t, __builtin_convertvector(x23 - __builtin_convertvector(h23, f2), b2))};
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t] *= alpha;
+      // rows 4 g + j of the V tile, dims 8 n .. 8 n + 7 (the grouped-query
+      // kernel's V layout), paired into the A operand of O^T += V^T P^T
+      uint32_t vw[4][4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const u32x4 vv = *reinterpret_cast<const u32x4*>(vl + (4 * g + jj) * kSharedRowB + 16 * n);
+        vw[jj][0] = vv.x;
+        vw[jj][1] = vv.y;
+        vw[jj][2] = vv.z;
+        vw[jj][3] = vv.w;
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const u32x2 lo2 = {(vw[0][w] & 0xFFFFu) | (vw[1][w] << 16), (vw[2][w] & 0xFFFFu) | (vw[3][w] << 16)};
+        const u32x2 hi2 = {(vw[0][w] >> 16) | (vw[1][w] & 0xFFFF0000u), (vw[2][w] >> 16) | (vw[3][w] & 0xFFFF0000u)};
+        o[2 * w] = mfma_k16<DT>(lo2, pb, o[2 * w]);
+        o[2 * w + 1] = mfma_k16<DT>(hi2, pb, o[2 * w + 1]);
+        if constexpr (DT == PKV_BF16) {
+          o[2 * w] = mfma_k16<DT>(lo2, pl, o[2 * w]);
+          o[2 * w + 1] = mfma_k16<DT>(hi2, pl, o[2 * w + 1]);
+        }
+      }
+    }
+  }
+
+  // per wave and column: m, the sum over the four lane groups, and o with
+  // dims 32 g + 8 r + t in o[t][r]; waves of one column tile merge in LDS
+  float lt = lsum + __shfl_xor(lsum, 16);
+  lt += __shfl_xor(lt, 32);
+  __syncthreads();  // the stage area becomes the merge area
+  float* sm_m = reinterpret_cast<float*>(sm);
+  float* sm_l = sm_m + 4 * 16;
+  float* sm_o = sm_l + 4 * 16;
+  if (g == 0) {
+    sm_m[wave * 16 + n] = m;
+    sm_l[wave * 16 + n] = lt;
+  }
+  {
+    float* orow = sm_o + (wave * 16 + n) * D + 32 * g;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<f4*>(orow + 8 * r) = f4{o[0][r], o[1][r], o[2][r], o[3][r]};
+      *reinterpret_cast<f4*>(orow + 8 * r + 4) = f4{o[4][r], o[5][r], o[6][r], o[7][r]};
+    }
+  }
+  __syncthreads();
+  const int64_t rec_step = int64_t(p.num_q_heads) * p.rec_floats;
+  for (int idx = threadIdx.x; idx < ct * 16 * D; idx += 256) {
+    const int c = idx / D;  // column of the set
+    const int dd = idx - c * D;
+    if (c >= cols) continue;
+    const int t = c >> 4, cn = c & 15;
+    float M = -INFINITY;
+    for (int w = t * wpt; w < (t + 1) * wpt; ++w) M = fmaxf(M, sm_m[w * 16 + cn]);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    float num = 0.f, den = 0.f;
+    for (int w = t * wpt; w < (t + 1) * wpt; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(sm_m[w * 16 + cn] - M_use);
+      num = __builtin_fmaf(wt, sm_o[(w * 16 + cn) * D + dd], num);
+      den = __builtin_fmaf(wt, sm_l[w * 16 + cn], den);
+    }
+    const int mc = p.order[first + m0 + c / p.group];
+    const int qc = kvh * p.group + (c - (c / p.group) * p.group);
+    const int ridx = p.part_offset[mc] + k_base + chunk;
+    if (p.part_offset[mc] < 0 || ridx >= p.n_partials) continue;
+    float* rec = p.part + int64_t(ridx) * rec_step + int64_t(qc) * p.rec_floats;
+    rec[dd] = num;
+    if (dd == 0) {
+      rec[D] = M;
+      rec[D + 1] = den;
+    }
+  }
 }
 
 struct ReduceParams {
@@ -677,6 +956,8 @@ struct ReduceParams {
   const int32_t* context_lens;
   const int32_t* part_offset;
   const int32_t* reduce_seqs;
+  const int32_t* priv_start;  // or null
+  const int32_t* n_shared;    // or null
   int32_t num_q_heads;
   int32_t table_stride;
   int32_t partition_blocks;
@@ -693,7 +974,8 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const ReducePara
   const int seq = p.reduce_seqs[r];
   const int L = p.context_lens[seq];
   const int nblk = min((L + kBlockTokens - 1) / kBlockTokens, p.table_stride);
-  const int n_parts = (nblk + p.partition_blocks - 1) / p.partition_blocks;
+  const int ps = p.priv_start ? p.priv_start[seq] : 0;
+  const int n_parts = (p.n_shared ? p.n_shared[seq] : 0) + (nblk - ps + p.partition_blocks - 1) / p.partition_blocks;
   const int base = p.part_offset[seq];
   if (base < 0 || base + n_parts > p.n_partials) return;
   const int dd = threadIdx.x;
@@ -899,6 +1181,20 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
   prm.context_lens = context_lens;
   prm.work = plan;
   prm.part_offset = plan + 2 * int64_t(info->n_work);
+  prm.priv_start = nullptr;
+  prm.n_shared = nullptr;
+  if (info->n_nodes > 0) {
+    if ((d.dtype != PKV_F16 && d.dtype != PKV_BF16) || d.head_dim != 128)
+      return fail(PKV_E_UNSUPPORTED, "shared-block plans take fp16 / bf16 pools of head_dim 128");
+    if (info->shared_group != group || info->shared_chunk_blocks < 1 || info->n_shared_items < 1 ||
+        info->off_shared < 2 * info->n_work + num_seqs + info->n_reduce ||
+        int64_t(info->off_shared) + 3 * int64_t(num_seqs) + 8 * int64_t(info->n_nodes) > info->plan_ints)
+      return fail(PKV_E_BAD_ARG, "shared-block plan does not match this batch (made for another head count?)");
+    if (int64_t(info->n_shared_items) * d.num_kv_heads > INT32_MAX)
+      return fail(PKV_E_BAD_ARG, "shared launch too large");
+    prm.priv_start = plan + info->off_shared;
+    prm.n_shared = prm.priv_start + num_seqs;
+  }
   // workspace: records from its start, one per (partial, query head):
   // o[D], m, l padded to 128 bytes; completion tickets [num_seqs][H_q] at
   // its end (128-byte aligned).  A workspace shared by launches of
@@ -928,16 +1224,57 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
 // ev_start / ev_stop (optional) are attached to the dispatch itself
 // (hipExtLaunchKernel), so their interval is the kernel's execution, without
 // the queueing of separate marker packets.
+// The shared-block launch of a plan with nodes: one workgroup per (shared
+// item, KV head), writing the nodes' split-K records.
+pkv_status launch_shared(const pkv_pool* pool, const DecodeParams& prm, const int32_t* plan,
+                         const pkv_decode_plan_info* info, hipStream_t s, hipEvent_t ev_start) {
+  SharedParams sp;
+  sp.q = prm.q;
+  sp.k_cache = prm.k_cache;
+  sp.v_cache = prm.v_cache;
+  sp.block_tables = prm.block_tables;
+  sp.part_offset = prm.part_offset;
+  sp.order = plan + info->off_shared + 2 * int64_t(info->num_seqs);
+  sp.nodes = sp.order + info->num_seqs;
+  sp.part = prm.part;
+  sp.rec_floats = prm.rec_floats;
+  sp.num_q_heads = prm.num_q_heads;
+  sp.num_kv_heads = prm.num_kv_heads;
+  sp.group = prm.group;
+  sp.table_stride = prm.table_stride;
+  sp.num_blocks = prm.num_blocks;
+  sp.n_nodes = info->n_nodes;
+  sp.chunk_blocks = info->shared_chunk_blocks;
+  sp.per_set = 64 / prm.group;
+  sp.n_partials = info->n_partials;
+  sp.scale_log2 = prm.scale_log2;
+  void (*fn)(const SharedParams) = pool->desc.dtype == PKV_F16
+                                       ? paged_decode_shared_kernel<PKV_F16, kCacheReuse>
+                                       : paged_decode_shared_kernel<PKV_BF16, kCacheReuse>;
+  const uint32_t grid = uint32_t(int64_t(info->n_shared_items) * prm.num_kv_heads);
+  if (ev_start)
+    hipExtLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, s, ev_start, nullptr, 0, sp);
+  else
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, s, sp);
+  return launch_status("paged_decode shared-block launch");
+}
+
 pkv_status launch_partitions(const pkv_pool* pool, const DecodeParams& prm, int gw, bool mfma,
                              const pkv_decode_plan_info* info, hipStream_t s,
                              hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
+  if (info->n_nodes > 0) {
+    // blocks held in common first: their records must exist before the
+    // decode launch below combines them (stream order)
+    if (pkv_status st = launch_shared(pool, prm, prm.work, info, s, ev_start)) return st;
+    ev_start = nullptr;
+  }
   int nw = waves_per_item();  // becomes the chosen instance's waves
   const bool reuse = info->shared_kv != 0;
   DecodeFn fn = mfma ? pick_mfma(pool->desc.dtype, gw, nw, reuse)
                      : pick_decode(pool->desc.dtype, pool->desc.head_dim, gw, nw, reuse);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group");
   const int64_t grid = int64_t(info->n_work) * prm.num_kv_heads * prm.hgroups_per_kv;
-  if (ev_start || ev_stop)
+  if (ev_start || ev_stop)  // one start / stop pair spans both launches of a shared-block plan
     hipExtLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kWave * nw), 0, s, ev_start, ev_stop, 0, prm);
   else
     hipLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kWave * nw), 0, s, prm);
@@ -954,6 +1291,8 @@ pkv_status launch_reduce(const pkv_pool* pool, const DecodeParams& prm, int32_t 
   rp.context_lens = prm.context_lens;
   rp.part_offset = prm.part_offset;
   rp.reduce_seqs = prm.part_offset + num_seqs;
+  rp.priv_start = prm.priv_start;
+  rp.n_shared = prm.n_shared;
   rp.num_q_heads = prm.num_q_heads;
   rp.table_stride = prm.table_stride;
   rp.partition_blocks = prm.partition_blocks;

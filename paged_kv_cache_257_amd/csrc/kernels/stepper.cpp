@@ -162,7 +162,8 @@ pkv_status pkv_stepper_step(pkv_stepper* s, const int32_t* seqs, int32_t n_seqs,
     if (P == 0) P = pkv::kDefaultPartitionTokens;
   }
   pkv_batch_layout lay{};
-  if (pkv_status st = pkv_prepare_decode(s->pool, seqs, n_seqs, 1, s->stride, P, host, s->slot_bytes, &lay))
+  if (pkv_status st = pkv_prepare_decode(s->pool, seqs, n_seqs, 1, s->stride, P, s->num_q_heads, host,
+                                                 s->slot_bytes, &lay))
     return st;  // the pool is unchanged
   s->next = (k + 1) % kSlots;
   if (layout_out) *layout_out = lay;

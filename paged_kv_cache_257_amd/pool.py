@@ -274,6 +274,22 @@ def decode_plan(context_lens: np.ndarray, partition_tokens: int = 0, block_size:
     return plan[:info.plan_ints], info
 
 
+def decode_plan_shared(pool: "Pool", seqs, num_q_heads: int, partition_tokens: int = 0,
+                       chunk_tokens: int = 0) -> Tuple[np.ndarray, PlanInfo]:
+    """Split-K plan of live sequences of ``pool`` that reads blocks held in
+    common once for all their holders (see pkv_decode_plan_shared)."""
+    lib = pool.lib
+    seqs_np = np.ascontiguousarray(seqs, dtype=np.int32)
+    n = C.c_int32()
+    check(lib, lib.pkv_decode_plan_shared_ints(pool.handle, i32p(seqs_np), len(seqs_np), partition_tokens,
+                                               C.byref(n)))
+    plan = np.empty(max(n.value, 1), dtype=np.int32)
+    info = PlanInfo()
+    check(lib, lib.pkv_decode_plan_shared(pool.handle, i32p(seqs_np), len(seqs_np), partition_tokens,
+                                          num_q_heads, chunk_tokens, i32p(plan), len(plan), C.byref(info)))
+    return plan[:info.plan_ints], info
+
+
 def decode_workspace_bytes(info: PlanInfo, num_q_heads: int, head_dim: int,
                            host_only: bool = False) -> int:
     lib = _capi.load(host_only=host_only)

@@ -144,7 +144,8 @@ class DecodeIteration:
             raise ValueError("fill-mode partitioning is chosen by the native stepper (step()); "
                              "prepare() takes a concrete partition size or 0")
         check(self.lib, self.lib.pkv_prepare_decode(self.pool.handle, i32p(seqs_np), n, a, self.stride,
-                                                    self.P, host.data_ptr(), self.nbytes, C.byref(lay)))
+                                                    self.P, self.Hq, host.data_ptr(), self.nbytes,
+                                                    C.byref(lay)))
         compute = torch.cuda.current_stream() if stream is None else stream
         cs = self.copy_stream if self.copy_stream is not None else compute
         if self.copy_stream is not None and self.compute_done[k] is not None:

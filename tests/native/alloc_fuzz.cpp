@@ -210,6 +210,135 @@ static void fuzz_plans(std::mt19937& rng) {
   CHECK(u.paged_waste_tokens >= 0 && u.paged_waste_tokens < 16 * b);
 }
 
+// Shared-block plans over forked batches: every block of every sequence is
+// covered exactly once (by the chunks of the nodes it belongs to, or by its
+// own range), node members hold the node's blocks at the same positions and
+// never their last block, record indices are distinct and capped, and the
+// order array keeps each node's members contiguous.
+static void fuzz_shared_plan(std::mt19937& rng) {
+  pkv_pool_desc d{};
+  d.num_blocks = 400;
+  d.block_size = 16;
+  d.num_kv_heads = 1 << int(rng() % 3);
+  d.head_dim = 128;
+  d.max_blocks_per_seq = 40;
+  d.dtype = PKV_F16;
+  pkv_pool* p = nullptr;
+  CHECK(pkv_pool_create(&d, nullptr, nullptr, nullptr, &p) == PKV_OK);
+  std::vector<int32_t> live;
+  int32_t s0 = 0;
+  CHECK(pkv_seq_alloc(p, 16 * int32_t(1 + rng() % 12), &s0, nullptr) == PKV_OK);
+  live.push_back(s0);
+  for (int op = 0; op < 60; ++op) {
+    const int32_t any = live[rng() % live.size()];
+    int32_t out = 0, len = 0;
+    CHECK(pkv_seq_length(p, any, &len) == PKV_OK);
+    const int kind = int(rng() % 3);
+    if (kind == 0 && pkv_seq_fork(p, any, &out) == PKV_OK) live.push_back(out);
+    if (kind == 1 && pkv_seq_fork_prefix(p, any, int32_t(rng() % (len + 1)), &out) == PKV_OK) live.push_back(out);
+    if (kind == 2) (void)pkv_seq_append(p, any, 1 + int32_t(rng() % 40), nullptr);
+  }
+  std::vector<int32_t> seqs;
+  for (int32_t id : live) {
+    int32_t len = 0;
+    CHECK(pkv_seq_length(p, id, &len) == PKV_OK);
+    if (len > 0 && rng() % 8 != 0) seqs.push_back(id);
+  }
+  const int32_t n = int32_t(seqs.size());
+  const int32_t groups[] = {1, 2, 4, 8, 16};
+  const int32_t group = groups[rng() % 5];
+  const int32_t chunks[] = {0, 16, 64, 256};
+  const int32_t chunk_tokens = chunks[rng() % 4];
+  const int32_t P = 16 * int32_t(1 + rng() % 8);
+  int32_t need = 0;
+  CHECK(pkv_decode_plan_shared_ints(p, seqs.data(), n, P, &need) == PKV_OK);
+  std::vector<int32_t> plan(size_t(need) + 1);
+  pkv_decode_plan_info info{};
+  CHECK(pkv_decode_plan_shared(p, seqs.data(), n, P, group * d.num_kv_heads, chunk_tokens, plan.data(), need,
+                               &info) == PKV_OK);
+  CHECK(info.plan_ints <= need);
+  std::vector<std::vector<int32_t>> tab(n);
+  std::vector<int32_t> nblk(n), cover_count;
+  for (int32_t i = 0; i < n; ++i) {
+    tab[i].resize(d.max_blocks_per_seq);
+    int32_t m = 0, len = 0;
+    CHECK(pkv_seq_table(p, seqs[i], tab[i].data(), d.max_blocks_per_seq, &m) == PKV_OK);
+    CHECK(pkv_seq_length(p, seqs[i], &len) == PKV_OK);
+    nblk[i] = (len + 15) / 16;
+    CHECK(m == nblk[i]);
+  }
+  std::vector<std::vector<int32_t>> cover(n);
+  for (int32_t i = 0; i < n; ++i) cover[i].assign(nblk[i], 0);
+  const int32_t* part_offset = plan.data() + 2 * info.n_work;
+  const int32_t pb = P / 16;
+  std::vector<int32_t> priv(n, 0), nsh(n, 0);
+  if (info.n_nodes > 0) {
+    const int32_t* sec = plan.data() + info.off_shared;
+    const int32_t* order = sec + 2 * n;
+    const int32_t* nodes = sec + 3 * n;
+    std::vector<int32_t> seen(n, 0);
+    for (int32_t i = 0; i < n; ++i) {
+      priv[i] = sec[i];
+      nsh[i] = sec[n + i];
+      CHECK(order[i] >= 0 && order[i] < n && !seen[order[i]]);
+      seen[order[i]] = 1;
+      CHECK(nsh[i] <= PKV_MAX_SHARED_RECORDS);
+    }
+    std::vector<std::vector<int32_t>> recs(n);
+    int64_t items = 0;
+    const int32_t cb = info.shared_chunk_blocks;
+    for (int32_t v = 0; v < info.n_nodes; ++v) {
+      const int32_t* nd = nodes + 8 * v;
+      const int32_t rep = nd[0], j0 = nd[1], j1 = nd[2], first = nd[3], mem = nd[4], kb = nd[5];
+      CHECK(nd[6] == items && j0 < j1 && mem >= 2 && first + mem <= n);
+      CHECK(nd[7] == (mem * group + 63) / 64);
+      const int32_t nch = (j1 - j0 + cb - 1) / cb;
+      items += int64_t(nch) * nd[7];
+      bool rep_in = false;
+      for (int32_t t = first; t < first + mem; ++t) {
+        const int32_t s = order[t];
+        rep_in |= (s == rep);
+        CHECK(j1 <= nblk[s] - 1);
+        for (int32_t j = j0; j < j1; ++j) {
+          CHECK(tab[s][j] == tab[rep][j]);
+          cover[s][j]++;
+        }
+        for (int32_t c = 0; c < nch; ++c) recs[s].push_back(kb + c);
+      }
+      CHECK(rep_in);
+    }
+    CHECK(items == info.n_shared_items);
+    for (int32_t i = 0; i < n; ++i) {
+      std::sort(recs[i].begin(), recs[i].end());
+      CHECK(int32_t(recs[i].size()) == nsh[i]);
+      for (int32_t r = 0; r < nsh[i]; ++r) CHECK(recs[i][r] == r);
+    }
+  }
+  // private ranges through the work items
+  int32_t partials = 0;
+  std::vector<int32_t> parts_seen(n, 0);
+  for (int32_t w = 0; w < info.n_work; ++w) {
+    const int32_t s = plan[2 * w], q = plan[2 * w + 1];
+    CHECK(s >= 0 && s < n);
+    const int32_t b0 = priv[s] + q * pb, b1 = std::min(b0 + pb, nblk[s]);
+    CHECK(b0 < b1);
+    for (int32_t j = b0; j < b1; ++j) cover[s][j]++;
+    parts_seen[s]++;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    for (int32_t j = 0; j < nblk[i]; ++j) CHECK(cover[i][j] == 1);
+    const int32_t records = nsh[i] + parts_seen[i];
+    if (records > 1) {
+      CHECK(part_offset[i] == partials);
+      partials += records;
+    } else {
+      CHECK(part_offset[i] == -1);
+    }
+  }
+  CHECK(partials == info.n_partials);
+  CHECK(pkv_pool_destroy(p) == PKV_OK);
+}
+
 int main(int argc, char** argv) {
   const int seeds = argc > 1 ? std::atoi(argv[1]) : 20;
   for (int seed = 0; seed < seeds; ++seed) {
@@ -277,6 +406,7 @@ int main(int argc, char** argv) {
     fuzz_hybrid(rng);
     fuzz_scheduler(rng);
     fuzz_plans(rng);
+    for (int k = 0; k < 4; ++k) fuzz_shared_plan(rng);
   }
   std::printf("alloc_fuzz ok (%d seeds)\n", seeds);
   return 0;

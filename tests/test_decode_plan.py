@@ -73,11 +73,15 @@ def test_default_partition_and_workspace_bound():
         need = decode_workspace_bytes(info, 12, 64, host_only=True)
         for nb in (B, B + 3):
             assert decode_workspace_bound(nb, Lmax, 12, 64, P, host_only=True) >= need
-    # tight when every sequence has the maximum length
+    # when every sequence has the maximum length the bound is that plan's
+    # workspace plus the shared records a shared-block plan may add (at
+    # most PKV_MAX_SHARED_RECORDS per sequence, one per query head each)
+    from paged_kv_cache_257_amd import _capi
     lens = np.full(9, 5000)
     _, info = decode_plan(lens, 0, host_only=True)
+    record = 640  # o[128], m, l as fp32, padded to whole 128-byte lines
     assert decode_workspace_bound(9, 5000, 8, 128, 0, host_only=True) == \
-        decode_workspace_bytes(info, 8, 128, host_only=True)
+        decode_workspace_bytes(info, 8, 128, host_only=True) + 9 * _capi.MAX_SHARED_RECORDS * 8 * record
     with pytest.raises(ValueError):
         decode_workspace_bound(4, 100, 8, 128, 24, host_only=True)
 

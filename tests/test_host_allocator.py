@@ -211,7 +211,7 @@ def test_prepare_decode_matches_separate_calls():
         seqs = b.live()
         lay = _capi.BatchLayout()
         _capi.check(lib, lib.pkv_prepare_decode(a.handle, _capi.i32p(np.asarray(seqs, np.int32)),
-                                                len(seqs), 1, width, 64, buf.ctypes.data, nbytes,
+                                                len(seqs), 1, width, 64, 0, buf.ctypes.data, nbytes,
                                                 C.byref(lay)))
         n = len(seqs)
         slots = buf[lay.off_slots:lay.off_slots + 8 * n].view(np.int64)
@@ -230,10 +230,10 @@ def test_prepare_decode_matches_separate_calls():
     # errors leave the pool unchanged
     before = (a.live(), a.free_list(), a.refcounts())
     lay = _capi.BatchLayout()
-    st = lib.pkv_prepare_decode(a.handle, _capi.i32p(np.asarray([0, 999], np.int32)), 2, 1, width, 64,
+    st = lib.pkv_prepare_decode(a.handle, _capi.i32p(np.asarray([0, 999], np.int32)), 2, 1, width, 64, 0,
                                 buf.ctypes.data, nbytes, C.byref(lay))
     assert st == _capi.E_BAD_SEQ
-    st = lib.pkv_prepare_decode(a.handle, _capi.i32p(np.asarray([0], np.int32)), 1, 1, width, 64,
+    st = lib.pkv_prepare_decode(a.handle, _capi.i32p(np.asarray([0], np.int32)), 1, 1, width, 64, 0,
                                 buf.ctypes.data, 64, C.byref(lay))
     assert st == _capi.E_BAD_ARG
     assert (a.live(), a.free_list(), a.refcounts()) == before
@@ -256,7 +256,7 @@ def test_prepare_decode_shared_kv_hint():
         buf = np.zeros(nbytes, dtype=np.uint8)
         lay = _capi.BatchLayout()
         _capi.check(lib, lib.pkv_prepare_decode(a.handle, _capi.i32p(np.asarray(seqs, np.int32)),
-                                                len(seqs), 1, width, 0, buf.ctypes.data, nbytes,
+                                                len(seqs), 1, width, 0, 0, buf.ctypes.data, nbytes,
                                                 C.byref(lay)))
         n = len(seqs)
         tables = buf[lay.off_tables:lay.off_tables + 4 * n * width].view(np.int32).reshape(n, width)

@@ -22,7 +22,7 @@ def test_allocator_fuzz_under_sanitizers(tmp_path):
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-I" + os.path.join(ROOT, "include"),
            os.path.join(ROOT, "tests", "native", "alloc_fuzz.cpp"),
-           *[os.path.join(SRC, f) for f in ("pool.cpp", "plan.cpp", "prepare.cpp", "prefill_plan.cpp",
+           *[os.path.join(SRC, f) for f in ("pool.cpp", "plan.cpp", "plan_shared.cpp", "prepare.cpp", "prefill_plan.cpp",
                                             "utilisation.cpp", "hybrid.cpp", "sched.cpp")], "-o", exe]
     b = subprocess.run(cmd, capture_output=True, text=True)
     assert b.returncode == 0, b.stderr
