@@ -434,11 +434,18 @@ typedef struct {
   /* Shared-block section (pkv_decode_plan_shared; all 0 from
    * pkv_decode_plan): nodes of blocks held in common by several sequences
    * of the batch, read once for all of them by a separate launch. */
-  int32_t n_nodes;             /* shared nodes (0: no shared section)         */
-  int32_t n_shared_items;      /* workgroups of the shared launch per KV head  */
-  int32_t shared_chunk_blocks; /* blocks per shared work item                  */
+  int32_t n_nodes;             /* shared nodes (0: no shared section)          */
+  int32_t n_wide_nodes;        /* the first n_wide_nodes are wide, the rest narrow */
+  int32_t n_shared_items;      /* wide workgroups per KV head                   */
+  int32_t n_narrow_items;      /* narrow workgroups per KV head                 */
+  int32_t shared_chunk_blocks; /* smallest blocks per wide work item            */
+  int32_t narrow_chunk_blocks; /* smallest blocks per narrow work item          */
   int32_t shared_group;        /* query heads per KV head the plan was made for */
-  int32_t off_shared;          /* int offset of the shared section in the plan */
+  int32_t off_shared;          /* int offset of the shared section in the plan  */
+  /* Mean blocks per work item, rounded up.  The decode gives short items
+   * fewer waves per workgroup (4 from 16 blocks, 2 from 6, else 1) unless
+   * PKV_DECODE_WAVES says otherwise. */
+  int32_t item_blocks;
 } pkv_decode_plan_info;
 
 /* Upper bound of the plan length for these lengths. */
@@ -459,32 +466,41 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
  * table of its first member, which every member holds at the same positions,
  * full in every member (a sequence's last block is never in a node).  Nodes
  * nest like a prefix tree: the members of a node share all blocks of its
- * ancestors.  A node's blocks are cut into chunks of shared_chunk_blocks and
- * its members into column sets of 64 / group sequences; each (chunk, column
- * set, KV head) is one workgroup of the shared launch, which reads the chunk
- * once and writes one split-K record per member and query head.  Every
+ * ancestors.  A node of more than 16 (member, query head) columns is wide:
+ * its blocks are cut into chunks and its members into column sets of
+ * 128 / group sequences, each (chunk, column set, KV head) one workgroup
+ * of the wide launch, which stages the chunk through LDS once for all the
+ * set's columns.  A narrow node's blocks are cut into chunks, each (chunk,
+ * KV head) one workgroup of the narrow launch, whose waves stream the
+ * chunk's blocks for its columns.  Both write one split-K record per
+ * member, query head and chunk.  A chunk is chunk_tokens / block_size
+ * blocks (at least 64 for a narrow node), or, for chunk_tokens = 0, at
+ * least 32 blocks (wide) or 64 (narrow), long nodes being cut into at most
+ * 8 chunks (wide) or 4 (narrow); shared_chunk_blocks / narrow_chunk_blocks
+ * give the smallest size of each kind and every node stores its own.  Every
  * sequence then attends over the rest of its blocks (from private_start) as
  * in pkv_decode_plan, and its records, shared ones first, are combined.
  * Nodes are built only when at least a quarter of the batch's context tokens
  * lie in them, for fp16 / bf16 pools of head_dim 128 and group = num_q_heads
  * / num_kv_heads dividing 16; otherwise the result is pkv_decode_plan's
  * (with shared_kv set as pkv_batch_shared_kv would).  chunk_tokens: a
- * multiple of block_size, or 0 (chunks sized so that the shared launch has
- * about 512 workgroups, 16 to 256 blocks each).  A sequence's shared
- * records (one per node chunk on its path) are capped at
+ * multiple of block_size, or 0 (the sizes above; the environment variable
+ * PKV_SHARED_CHUNK_TOKENS, read at every call, replaces 0 for tuning).  A
+ * sequence's shared records (one per node chunk on its path) are capped at
  * PKV_MAX_SHARED_RECORDS: a node stops where the cap would be passed.
  *
  * Layout: pkv_decode_plan's, then, from info->off_shared when n_nodes > 0,
  *   [num_seqs]       private_start: first block of each sequence's own part
  *   [num_seqs]       n_shared: shared records of each sequence
  *   [num_seqs]       order: batch indices, each node's members contiguous
- *   [8 * n_nodes]    nodes (rep, j0, j1, first member in order, members,
- *                    first record, first shared item, column sets)
+ *   [9 * n_nodes]    nodes (rep, j0, j1, first member in order, members,
+ *                    first record, first item of its kind, column sets,
+ *                    blocks per chunk), the n_wide_nodes wide ones first
  * where a member s of node v writes, for chunk c, the record at
  * part_offset[s] + first record + c.  Upload it unchanged. */
 /* A sequence owns at most this many shared records (pkv_decode_plan_shared
  * stops a node early rather than pass it; workspace bounds count on it). */
-#define PKV_MAX_SHARED_RECORDS 8
+#define PKV_MAX_SHARED_RECORDS 16
 pkv_status pkv_decode_plan_shared_ints(const pkv_pool* pool, const int32_t* seqs, int32_t n_seqs,
                                        int32_t partition_tokens, int32_t* plan_ints);
 pkv_status pkv_decode_plan_shared(const pkv_pool* pool, const int32_t* seqs, int32_t n_seqs,

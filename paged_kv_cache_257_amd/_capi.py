@@ -17,7 +17,7 @@ STATUS_KIND = {E_NO_BLOCKS: "no_blocks", E_BAD_SEQ: "bad_seq", E_BAD_ARG: "bad_a
                E_NO_SLOTS: "no_slots"}
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES of include/pkv.h
-MAX_SHARED_RECORDS = 8            # PKV_MAX_SHARED_RECORDS of include/pkv.h
+MAX_SHARED_RECORDS = 16           # PKV_MAX_SHARED_RECORDS of include/pkv.h
 
 
 class PoolDesc(C.Structure):
@@ -38,8 +38,9 @@ class Stats(C.Structure):
 class PlanInfo(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("num_seqs", "block_size", "partition_tokens", "n_work",
                                          "n_reduce", "n_partials", "plan_ints", "max_context_len",
-                                         "shared_kv", "n_nodes", "n_shared_items", "shared_chunk_blocks",
-                                         "shared_group", "off_shared")]
+                                         "shared_kv", "n_nodes", "n_wide_nodes", "n_shared_items",
+                                         "n_narrow_items", "shared_chunk_blocks", "narrow_chunk_blocks",
+                                         "shared_group", "off_shared", "item_blocks")]
 
 
 class PrefillPlanInfo(C.Structure):

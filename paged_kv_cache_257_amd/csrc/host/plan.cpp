@@ -105,7 +105,12 @@ pkv_status fill_private_plan(const int32_t* lens, int32_t n, int32_t bs, int32_t
     }
   }
   int32_t max_len = 0;
-  for (int32_t i = 0; i < n; ++i) max_len = std::max(max_len, lens[i]);
+  int64_t priv_total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    max_len = std::max(max_len, lens[i]);
+    priv_total += priv_blocks(i);
+  }
+  info->item_blocks = n_work > 0 ? int32_t((priv_total + n_work - 1) / n_work) : 0;
   info->num_seqs = n;
   info->block_size = bs;
   info->partition_tokens = P;
@@ -116,8 +121,11 @@ pkv_status fill_private_plan(const int32_t* lens, int32_t n, int32_t bs, int32_t
   info->max_context_len = max_len;
   info->shared_kv = 0;
   info->n_nodes = 0;
+  info->n_wide_nodes = 0;
   info->n_shared_items = 0;
+  info->n_narrow_items = 0;
   info->shared_chunk_blocks = 0;
+  info->narrow_chunk_blocks = 0;
   info->shared_group = 0;
   info->off_shared = 0;
   return PKV_OK;

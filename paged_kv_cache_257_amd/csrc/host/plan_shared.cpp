@@ -6,12 +6,13 @@
 // read-only blocks).  A decode that walks every table separately reads such
 // a block once per holder.  This plan groups the holders: sequences whose
 // tables agree on a run of full blocks form a node, and one workgroup per
-// (chunk of the node's blocks, set of 64 / group members, KV head) reads the
+// (chunk of the node's blocks, set of 128 / group members, KV head) reads the
 // chunk once and serves all those members' query heads.  Nodes nest like a
 // prefix tree (forks share a prefix of the table), so the batch is walked
 // once, depth first: at each depth the sequences still together are split
 // by the block they hold there.
 #include <algorithm>
+#include <cstdlib>
 #include <vector>
 
 #include "pool_internal.h"
@@ -20,13 +21,22 @@ using pkv::fail;
 
 namespace {
 
-constexpr int32_t kNodeInts = 8;
-constexpr int32_t kColumnsPerItem = 64;     // query columns of one shared workgroup
-constexpr int64_t kTargetSharedWorkgroups = 512;
-constexpr int32_t kMinChunkBlocks = 16, kMaxChunkBlocks = 256;
+constexpr int32_t kNodeInts = 9;
+constexpr int32_t kColumnsPerItem = 128;  // query columns of one wide workgroup
+constexpr int32_t kNarrowColumns = 16;    // a node of at most this many columns is narrow
+// Chunk sizes without an explicit chunk_tokens: at least kWideChunkBlocks
+// (wide) or kNarrowChunkBlocks (narrow), and long nodes cut into at most
+// kWideChunks or kNarrowChunks chunks, which keeps the records a sequence
+// owns per node few.  A narrow workgroup streams its chunk with four waves;
+// a wide one computes up to 128 columns per staged block, so its chunks are
+// shorter (a 256-sequence batch over a 4096-token prefix: 32-block chunks
+// 0.2275 ms per decode, 64-block 0.2356, 128-block 0.2701).
+constexpr int32_t kWideChunkBlocks = 32, kNarrowChunkBlocks = 64;
+constexpr int32_t kWideChunks = 8, kNarrowChunks = 4;
 
 struct Node {
-  int32_t rep, j0, j1, first, members, k_base, first_item, colsets;
+  int32_t rep, j0, j1, first, members, k_base, first_item, colsets, chunk;
+  bool narrow;
 };
 
 struct Builder {
@@ -36,10 +46,12 @@ struct Builder {
   std::vector<int32_t>& n_shared;
   std::vector<int32_t>& order;
   std::vector<Node>& nodes;
-  int32_t chunk = 0;  // blocks per chunk; 0 while only the tree is built
+  std::vector<int32_t>& buf;  // batch indices being grouped; ranges of it are groups
+  int32_t fixed_chunk = 0;    // blocks per chunk when the caller fixed it, else 0
   int32_t per_set = 1;
+  int32_t gq = 1;             // query heads per KV head: columns per member
   size_t max_nodes = 0;
-  int32_t max_records = 0;  // shared records a sequence may own (with chunk > 0)
+  int32_t max_records = 0;    // shared records a sequence may own
 
   void leaf(int32_t s, int32_t j, int32_t k) {
     priv_start[s] = j;
@@ -47,64 +59,69 @@ struct Builder {
     order.push_back(s);
   }
 
-  // members agree on table entries [0, j0) and each has elig > j0; split them
-  // by the block at j0 and extend every group of two or more into a node
-  void split(std::vector<int32_t> members, int32_t j0, int32_t k) {
-    std::sort(members.begin(), members.end(), [&](int32_t a, int32_t b) {
+  // buf[lo, hi) agree on table entries [0, j0) and each has elig > j0: sort
+  // them by the block at j0 and extend every run of two or more into a node
+  void split(size_t lo, size_t hi, int32_t j0, int32_t k) {
+    std::sort(buf.begin() + lo, buf.begin() + hi, [&](int32_t a, int32_t b) {
       return rows[a][j0] != rows[b][j0] ? rows[a][j0] < rows[b][j0] : a < b;
     });
-    size_t i = 0;
-    while (i < members.size()) {
+    size_t i = lo;
+    while (i < hi) {
       size_t e = i + 1;
-      while (e < members.size() && rows[members[e]][j0] == rows[members[i]][j0]) ++e;
-      if (e - i == 1 || nodes.size() >= max_nodes || (chunk > 0 && k >= max_records)) {
-        for (size_t t = i; t < e; ++t) leaf(members[t], j0, k);
+      while (e < hi && rows[buf[e]][j0] == rows[buf[i]][j0]) ++e;
+      if (e - i == 1 || nodes.size() >= max_nodes || k >= max_records) {
+        for (size_t t = i; t < e; ++t) leaf(buf[t], j0, k);
       } else {
-        extend(std::vector<int32_t>(members.begin() + i, members.begin() + e), j0, k);
+        extend(i, e, j0, k);
       }
       i = e;
     }
   }
 
-  // the group agrees on [0, j0 + 1): take the longest run [j0, j1) all of
-  // its members hold, then continue with those that go on
-  void extend(std::vector<int32_t> group, int32_t j0, int32_t k) {
-    int32_t emin = elig[group[0]];
-    for (int32_t s : group) emin = std::min(emin, elig[s]);
-    const int32_t* rep = rows[group[0]];
-    int32_t j1 = j0 + 1;
-    while (j1 < emin) {
-      bool same = true;
-      for (int32_t s : group)
-        if (rows[s][j1] != rep[j1]) {
-          same = false;
-          break;
-        }
-      if (!same) break;
-      ++j1;
+  // buf[lo, hi) agree on [0, j0 + 1): take the longest run [j0, j1) all of
+  // them hold (one contiguous comparison per member against the first),
+  // then continue with those that go on
+  void extend(size_t lo, size_t hi, int32_t j0, int32_t k) {
+    int32_t j1 = elig[buf[lo]];
+    for (size_t t = lo; t < hi; ++t) j1 = std::min(j1, elig[buf[t]]);
+    const int32_t* rep = rows[buf[lo]];
+    for (size_t t = lo + 1; t < hi && j1 > j0 + 1; ++t)
+      j1 = int32_t(std::mismatch(rep + j0 + 1, rep + j1, rows[buf[t]] + j0 + 1).first - rep);
+    // narrow nodes (few columns) go to the streaming kernel
+    const int32_t members = int32_t(hi - lo);
+    const bool narrow = int64_t(members) * gq <= kNarrowColumns;
+    int32_t cv = fixed_chunk;
+    if (cv == 0) {
+      const int32_t parts = narrow ? kNarrowChunks : kWideChunks;
+      cv = std::max(narrow ? kNarrowChunkBlocks : kWideChunkBlocks, (j1 - j0 + parts - 1) / parts);
+    } else if (narrow) {
+      cv = std::max(cv, kNarrowChunkBlocks);
     }
     // a sequence's shared records are capped (the workspace bound counts
     // on it): a node that would pass the cap stops early and its members
     // read the rest of the run as their own blocks
-    if (chunk > 0) j1 = std::min<int64_t>(j1, j0 + int64_t(max_records - k) * chunk);
-    const int32_t chunks = chunk > 0 ? (j1 - j0 + chunk - 1) / chunk : 1;
+    j1 = int32_t(std::min<int64_t>(j1, j0 + int64_t(max_records - k) * cv));
+    const int32_t chunks = (j1 - j0 + cv - 1) / cv;
     Node v;
-    v.rep = group[0];
+    v.narrow = narrow;
+    v.rep = buf[lo];
     v.j0 = j0;
     v.j1 = j1;
     v.first = int32_t(order.size());
-    v.members = int32_t(group.size());
+    v.members = members;
     v.k_base = k;
     v.first_item = 0;
-    v.colsets = (v.members + per_set - 1) / per_set;
+    v.colsets = narrow ? 1 : (members + per_set - 1) / per_set;
+    v.chunk = cv;
     nodes.push_back(v);
-    std::vector<int32_t> rest;
-    for (int32_t s : group) {
-      if (elig[s] == j1) leaf(s, j1, k + chunks);  // its own blocks start here
-      else rest.push_back(s);
-    }
-    if (rest.size() == 1) leaf(rest[0], j1, k + chunks);
-    else if (rest.size() > 1) split(std::move(rest), j1, k + chunks);
+    // members whose sharing ends at j1 first (their own blocks start there),
+    // then the rest
+    const size_t mid = size_t(std::partition(buf.begin() + lo, buf.begin() + hi,
+                                             [&](int32_t s) { return elig[s] == j1; }) -
+                              buf.begin());
+    for (size_t t = lo; t < mid; ++t) leaf(buf[t], j1, k + chunks);
+    if (hi - mid == 1) leaf(buf[mid], j1, k + chunks);
+    else if (hi - mid > 1) split(mid, hi, j1, k + chunks);
   }
 };
 
@@ -132,7 +149,7 @@ pkv_status build_shared_plan(const pkv_pool* p, const int32_t* seqs, int32_t n, 
   if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0)
     return fail(PKV_E_BAD_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
   thread_local std::vector<const int32_t*> rows;
-  thread_local std::vector<int32_t> lens, elig, priv_start, n_shared, order;
+  thread_local std::vector<int32_t> lens, elig, priv_start, n_shared, order, buf;
   thread_local std::vector<Node> nodes;
   rows.resize(size_t(n));
   lens.resize(size_t(n));
@@ -151,27 +168,35 @@ pkv_status build_shared_plan(const pkv_pool* p, const int32_t* seqs, int32_t n, 
   const bool eligible = (d.dtype == PKV_F16 || d.dtype == PKV_BF16) && d.head_dim == 128 && bs == 16 &&
                         group <= 16 && 16 % group == 0;
 
-  // the prefix tree of the batch (chunk size not yet known)
+  // PKV_SHARED_CHUNK_TOKENS (read at every call, a multiple of the block
+  // size) fixes the chunk size for tuning sweeps when chunk_tokens is 0
+  if (chunk_tokens == 0) {
+    const char* e = std::getenv("PKV_SHARED_CHUNK_TOKENS");
+    const int v = e ? std::atoi(e) : 0;
+    if (v > 0 && v % bs == 0) chunk_tokens = v;
+  }
+  // the prefix tree of the batch, depth first
   priv_start.assign(size_t(n), 0);
   n_shared.assign(size_t(n), 0);
   order.clear();
   nodes.clear();
-  Builder b{rows, elig, priv_start, n_shared, order, nodes};
+  Builder b{rows, elig, priv_start, n_shared, order, nodes, buf};
   b.per_set = kColumnsPerItem / group;
+  b.gq = group;
   b.max_nodes = size_t(2) * size_t(n);
   b.max_records = PKV_MAX_SHARED_RECORDS;
-  {
-    std::vector<int32_t> all;
-    for (int32_t i = 0; i < n; ++i)
-      if (elig[i] > 0) all.push_back(i);
-    if (all.size() > 1) b.split(std::move(all), 0, 0);
-    else for (int32_t s : all) b.leaf(s, 0, 0);
-  }
-  int64_t shared_tokens = 0, units = 0;
-  for (const Node& v : nodes) {
-    shared_tokens += int64_t(v.j1 - v.j0) * bs * v.members;
-    units += int64_t(v.j1 - v.j0) * v.colsets;
-  }
+  b.fixed_chunk = chunk_tokens / bs;
+  order.reserve(size_t(n));
+  nodes.reserve(b.max_nodes);
+  buf.clear();
+  for (int32_t i = 0; i < n; ++i)
+    if (elig[i] > 0) buf.push_back(i);
+  if (buf.size() > 1) b.split(0, buf.size(), 0, 0);
+  else for (int32_t s : buf) b.leaf(s, 0, 0);
+  for (int32_t i = 0; i < n; ++i)
+    if (elig[i] <= 0) order.push_back(i);
+  int64_t shared_tokens = 0;
+  for (const Node& v : nodes) shared_tokens += int64_t(v.j1 - v.j0) * bs * v.members;
   // the quarter rule of the load-policy hint: below it, the separate launch
   // and the extra records are not worth their cost
   const bool share = total_tokens > 0 && 4 * shared_tokens >= total_tokens;
@@ -180,27 +205,6 @@ pkv_status build_shared_plan(const pkv_pool* p, const int32_t* seqs, int32_t n, 
     info->shared_kv = share ? 1 : 0;
     return PKV_OK;
   }
-
-  // chunk size, then the tree again with record counts per chunk
-  int32_t chunk = chunk_tokens / bs;
-  if (chunk == 0) {
-    const int64_t c = (units * d.num_kv_heads + kTargetSharedWorkgroups - 1) / kTargetSharedWorkgroups;
-    chunk = int32_t(std::min<int64_t>(kMaxChunkBlocks, std::max<int64_t>(kMinChunkBlocks, c)));
-  }
-  priv_start.assign(size_t(n), 0);
-  n_shared.assign(size_t(n), 0);
-  order.clear();
-  nodes.clear();
-  b.chunk = chunk;
-  {
-    std::vector<int32_t> all;
-    for (int32_t i = 0; i < n; ++i)
-      if (elig[i] > 0) all.push_back(i);
-    if (all.size() > 1) b.split(std::move(all), 0, 0);
-    else for (int32_t s : all) b.leaf(s, 0, 0);
-  }
-  for (int32_t i = 0; i < n; ++i)
-    if (elig[i] <= 0) order.push_back(i);
 
   if (pkv_status st = fill_private_plan(lens.data(), n, bs, P, priv_start.data(), n_shared.data(), plan, cap,
                                         info))
@@ -212,20 +216,30 @@ pkv_status build_shared_plan(const pkv_pool* p, const int32_t* seqs, int32_t n, 
   std::copy(priv_start.begin(), priv_start.end(), sec);
   std::copy(n_shared.begin(), n_shared.end(), sec + n);
   std::copy(order.begin(), order.end(), sec + 2 * int64_t(n));
+  // wide nodes first, then narrow ones; each kind numbers its items from 0
   int32_t* nv = sec + 3 * int64_t(n);
-  int64_t items = 0;
-  for (size_t t = 0; t < nodes.size(); ++t) {
-    const Node& v = nodes[t];
-    const int32_t chunks = (v.j1 - v.j0 + chunk - 1) / chunk;
-    const int32_t w[kNodeInts] = {v.rep, v.j0, v.j1, v.first, v.members, v.k_base, int32_t(items), v.colsets};
-    std::copy(w, w + kNodeInts, nv + kNodeInts * t);
-    items += int64_t(chunks) * v.colsets;
+  int64_t items[2] = {0, 0};
+  int32_t written = 0, n_wide = 0;
+  for (int kind = 0; kind < 2; ++kind) {
+    for (const Node& v : nodes) {
+      if (v.narrow != (kind == 1)) continue;
+      const int32_t chunks = (v.j1 - v.j0 + v.chunk - 1) / v.chunk;
+      const int32_t w[kNodeInts] = {v.rep,     v.j0,    v.j1, v.first, v.members, v.k_base, int32_t(items[kind]),
+                                    v.colsets, v.chunk};
+      std::copy(w, w + kNodeInts, nv + kNodeInts * int64_t(written++));
+      items[kind] += int64_t(chunks) * v.colsets;
+      if (kind == 0) n_wide++;
+    }
   }
-  if (items * d.num_kv_heads > INT32_MAX) return fail(PKV_E_BAD_ARG, "shared plan too large for one launch");
+  if (std::max(items[0], items[1]) * d.num_kv_heads > INT32_MAX)
+    return fail(PKV_E_BAD_ARG, "shared plan too large for one launch");
   info->plan_ints = int32_t(need);
   info->n_nodes = int32_t(nodes.size());
-  info->n_shared_items = int32_t(items);
-  info->shared_chunk_blocks = chunk;
+  info->n_wide_nodes = n_wide;
+  info->n_shared_items = int32_t(items[0]);
+  info->n_narrow_items = int32_t(items[1]);
+  info->shared_chunk_blocks = b.fixed_chunk > 0 ? b.fixed_chunk : kWideChunkBlocks;
+  info->narrow_chunk_blocks = std::max(b.fixed_chunk, kNarrowChunkBlocks);
   info->shared_group = group;
   info->off_shared = int32_t(off);
   info->shared_kv = 0;  // what is left per sequence is its own

@@ -91,6 +91,52 @@ struct DecodeParams {
   float scale_log2;
 };
 
+// Split-K records are merged in batches: every load of a batch is issued
+// before any is used, so their latencies overlap (a record-by-record loop
+// waits for each load in turn, and a short item merging ten records spent
+// most of its time there).
+constexpr int kRecBatch = 8;
+
+template <bool AGENT>
+__device__ __forceinline__ float rec_load(const float* a) {
+  if constexpr (AGENT) return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *a;
+}
+
+// Merge records rec0 + q * step, q < count, element dd, into the running
+// state (M: base-2 maximum in scaled units, -inf for none; num, den scaled
+// to it).  AGENT: records written in this launch (agent-scope loads);
+// otherwise they come from an earlier launch and plain loads see them.
+template <int D, bool AGENT>
+__device__ __forceinline__ void merge_records(const float* rec0, int64_t step, int count, int dd, float& M,
+                                              float& num, float& den) {
+  for (int q0 = 0; q0 < count; q0 += kRecBatch) {
+    float mq[kRecBatch], oq[kRecBatch], lq[kRecBatch];
+#pragma unroll
+    for (int i = 0; i < kRecBatch; ++i) {
+      const bool ok = q0 + i < count;
+      const float* rec = rec0 + int64_t(ok ? q0 + i : q0) * step;
+      mq[i] = ok ? rec_load<AGENT>(rec + D) : -INFINITY;
+      oq[i] = rec_load<AGENT>(rec + dd);
+      lq[i] = rec_load<AGENT>(rec + D + 1);
+    }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kRecBatch; ++i) Mb = fmaxf(Mb, mq[i]);
+    const float Mu = (Mb == -INFINITY) ? 0.f : Mb;
+    const float a = __builtin_amdgcn_exp2f(M - Mu);
+    num *= a;
+    den *= a;
+#pragma unroll
+    for (int i = 0; i < kRecBatch; ++i) {
+      const float w = (q0 + i < count) ? __builtin_amdgcn_exp2f(mq[i] - Mu) : 0.f;
+      num = __builtin_fmaf(w, oq[i], num);
+      den = __builtin_fmaf(w, lq[i], den);
+    }
+    M = Mb;
+  }
+}
+
 // The end of a work item, shared by both decode kernels.  sm_m, sm_l
 // ([NSUB][GW]) and sm_o ([NSUB][GW][D]) hold the workgroup's NSUB partial
 // softmax states per query head (base-2 maxima in scaled units), written
@@ -121,11 +167,6 @@ __device__ __forceinline__ void finish_item(const DecodeParams& p, const float* 
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) M = fmaxf(M, sm_m[s * GW + g]);
     const int qh = qh0 + g;
-    const float* rec0 = p.part + (int64_t(base) * p.num_q_heads + qh) * p.rec_floats;
-    if (fold) {
-      for (int q = 0; q < n_sh; ++q)
-        M = fmaxf(M, __hip_atomic_load(rec0 + q * step + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    }
     const float M_use = (M == -INFINITY) ? 0.f : M;
     float num = 0.f, den = 0.f;
 #pragma unroll
@@ -136,13 +177,8 @@ __device__ __forceinline__ void finish_item(const DecodeParams& p, const float* 
     }
     if (fold) {
       // the shared records were written by the launch before this one
-      for (int q = 0; q < n_sh; ++q) {
-        const float* rec = rec0 + q * step;
-        const float w = __builtin_amdgcn_exp2f(
-            __hip_atomic_load(rec + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M_use);
-        num = __builtin_fmaf(w, __hip_atomic_load(rec + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), num);
-        den = __builtin_fmaf(w, __hip_atomic_load(rec + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), den);
-      }
+      const float* rec0 = p.part + (int64_t(base) * p.num_q_heads + qh) * p.rec_floats;
+      merge_records<D, false>(rec0, step, n_sh, dd, M, num, den);
     }
     if (single || fold) {
       p.out[(int64_t(seq) * p.num_q_heads + qh) * D + dd] = num / den;
@@ -190,18 +226,8 @@ __device__ __forceinline__ void finish_item(const DecodeParams& p, const float* 
     const int dd = idx - g * D;
     const int qh = qh0 + g;
     const float* rec0 = p.part + (int64_t(base) * p.num_q_heads + qh) * p.rec_floats;
-    float M = -INFINITY;
-    for (int q = 0; q < n_rec; ++q)
-      M = fmaxf(M, __hip_atomic_load(rec0 + q * step + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    const float M_use = (M == -INFINITY) ? 0.f : M;
-    float num = 0.f, den = 0.f;
-    for (int q = 0; q < n_rec; ++q) {
-      const float* rec = rec0 + q * step;
-      const float w = __builtin_amdgcn_exp2f(
-          __hip_atomic_load(rec + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M_use);
-      num = __builtin_fmaf(w, __hip_atomic_load(rec + dd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), num);
-      den = __builtin_fmaf(w, __hip_atomic_load(rec + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), den);
-    }
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    merge_records<D, true>(rec0, step, n_rec, dd, M, num, den);
     p.out[(int64_t(seq) * p.num_q_heads + qh) * D + dd] = num / den;
   }
   if (threadIdx.x == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -708,26 +734,37 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
 // such sequences into nodes (a run of blocks every member holds at the same
 // table positions) and cuts each node into chunks of blocks and column sets
 // of members.  One workgroup takes one (chunk, column set, KV head): its
-// columns are the (member, query head) pairs of the set, up to 64, that read
-// this KV head, so S^T = K Q^T (16 tokens x 64 columns per block) and
-// O^T += V^T P^T are real dense products for the matrix cores even where
-// every sequence has a single query head (MHA).
+// columns are the (member, query head) pairs of the set that read this KV
+// head, up to 128, so S^T = K Q^T (16 tokens x 16 columns per product) and
+// O^T += V^T P^T are dense products for the matrix cores even where every
+// sequence has a single query head (MHA): the chunk's keys serve all those
+// queries at once, as a chunked prefill's keys serve a tile of query rows.
 //
-// The workgroup stages four blocks at a time through LDS: all 256 threads
-// load the K and V tiles (one 16-byte load each per block and pool, every
-// load instruction 1 KiB contiguous), the next stage's loads are in flight
-// while the current stage is computed from LDS, and every wave reads the
-// staged tiles it needs.  With C column tiles of 16 (C = 1, 2 or 4 after
-// rounding up), wave w serves column tile w / (4 / C) and takes every
-// (4 / C)-th block of the stage; waves of one tile merge through LDS at the
-// end.  Operand layouts are those of the grouped-query kernel above (K rows
-// as the A operand of the 16x16x32 product, V rows paired into the A operand
-// of the 16x16x16 product, the score accumulator reused as its B operand),
-// and so is the online softmax.  Each column's (o, m, l) becomes the split-K
-// record of its (member, query head) for this chunk; the decode launch that
-// follows merges them with the member's own blocks.
+// Keys stream in stages of 32 tokens (two blocks), double-buffered in LDS:
+// all 256 threads load the next stage into registers (every load
+// instruction 1 KiB contiguous; each wave's rows lie in one block) while
+// the current one is computed, then store K rows as they are and V
+// transposed (dim-major, 4-token column blocks XOR-swizzled by bits 5-6 of
+// the dim: the staging stores hit distinct banks and the operand reads stay
+// 8-byte contiguous).  Wave w holds column groups 2w and 2w + 1 (16 columns
+// each): every K operand read from LDS feeds both groups' S^T products, the
+// accumulator (tokens 4g .. 4g + 3 of column n in lane 16 g + n, for each of
+// the stage's two blocks) is the B operand of the 16x16x32 product
+// O^T += V^T P^T over the stage's 32 tokens, and every V^T operand feeds
+// both groups' products.  Online softmax per column in base 2 with the
+// scale folded into the exponent; a column's running maximum moves only
+// when a score passes it by more than 2^8 in weight, so after the first
+// keys the accumulators are almost never rescaled.  Softmax weights enter
+// the products as fp16 (fp16 inputs) or a bf16 head plus a bf16 remainder
+// (bf16 inputs); the normaliser sums the fp32 weights.
 // Every block in a node is full in every member (a sequence's last block is
-// never shared), so only table entries outside the pool are masked.
+// never shared); a stage's second block past the chunk, or a table entry
+// outside the pool, reads nothing and its keys are masked.
+// Each column's (o, m, l) becomes the split-K record of its (member, query
+// head) for this chunk; the decode launch that follows merges them with
+// the member's own blocks.
+constexpr int kNodeInts = 9;  // rep, j0, j1, first member, members, first record, first item, column sets, chunk
+
 struct SharedParams {
   const char* q;
   const char* k_cache;
@@ -735,7 +772,7 @@ struct SharedParams {
   const int32_t* block_tables;
   const int32_t* part_offset;  // [num_seqs] first record of each sequence
   const int32_t* order;        // [num_seqs] batch indices, node members contiguous
-  const int32_t* nodes;        // [n_nodes][8]
+  const int32_t* nodes;        // [n_nodes][kNodeInts]
   float* part;
   int32_t rec_floats;
   int32_t num_q_heads;
@@ -744,27 +781,39 @@ struct SharedParams {
   int32_t table_stride;
   int32_t num_blocks;
   int32_t n_nodes;
-  int32_t chunk_blocks;
-  int32_t per_set;  // members per column set: 64 / group
+  int32_t per_set;  // members per column set: kSharedCols / group
   int32_t n_partials;
   float scale_log2;
 };
 
-constexpr int kSharedStage = 4;  // blocks per LDS stage
-constexpr int kSharedRowB = 256 + 16;  // LDS bytes per staged token row (padded against bank conflicts)
+constexpr int kSharedRG = 2;                       // 16-column groups per wave
+constexpr int kSharedCols = 4 * kSharedRG * 16;    // columns per workgroup
+constexpr int kSharedStage = 32;                   // tokens per LDS stage (two blocks)
+constexpr float kSharedSlack = 8.f;                // log2 of the weight a running maximum may lag
 
-template <int DT, int CP>
-__global__ __launch_bounds__(256, 2) void paged_decode_shared_kernel(const SharedParams p) {
+// WPS: waves per SIMD the register budget is fitted to (2 or 3).
+template <int DT, int CP, int WPS>
+__global__ __launch_bounds__(256, WPS) void paged_decode_shared_kernel(const SharedParams p) {
   constexpr int D = 128;
-  constexpr int R = D * 2;
-  constexpr int TILE = kBlockTokens * R;
-  constexpr int TILE_LDS = kBlockTokens * kSharedRowB;
-  // stage: K tiles then V tiles of kSharedStage blocks; reused for the merge
-  __shared__ __attribute__((aligned(16))) char sm[2 * kSharedStage * TILE_LDS];
-  static_assert(sizeof(sm) >= 4 * 16 * (D + 2) * sizeof(float), "merge area");
+  constexpr int RG = kSharedRG;
+  constexpr int CH = D / 8;                 // 16-byte chunks per token row
+  constexpr int ROWB = D * 2;
+  constexpr int TILE = kBlockTokens * ROWB;
+  constexpr int KROW = D + 8;               // K row stride in LDS (16-bit elements)
+  constexpr int VROW = kSharedStage + 4;    // V^T row stride in LDS
+  constexpr int KL = kSharedStage * CH / 256;  // K chunks each thread stages
+  constexpr int NDT = D / 16;
+  static_assert(KL == 2 && CH * (kSharedStage / 2) == 256, "staging split");
+  // V^T column of stage token tok in LDS row r (a dim); see the comment above
+  auto vt_col = [](int r, int tok) __attribute__((always_inline)) {
+    return (((tok >> 2) ^ (2 * ((r >> 5) & 3))) << 2) | (tok & 3);
+  };
+  __shared__ __attribute__((aligned(16))) uint16_t lk[2][kSharedStage * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t lv[2][D * VROW];
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = lane >> 4;
   const int n = lane & 15;
   const int item = blockIdx.x / p.num_kv_heads;
@@ -774,35 +823,281 @@ __global__ __launch_bounds__(256, 2) void paged_decode_shared_kernel(const Share
   int lo = 0, hi = p.n_nodes - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (p.nodes[8 * mid + 6] <= item) lo = mid;
+    if (p.nodes[kNodeInts * mid + 6] <= item) lo = mid;
     else hi = mid - 1;
   }
-  const int32_t* nd = p.nodes + 8 * lo;
+  const int32_t* nd = p.nodes + kNodeInts * lo;
   const int rep = nd[0], j0 = nd[1], j1 = nd[2], first = nd[3], members = nd[4], k_base = nd[5];
   const int colsets = nd[7];
   const int local = item - nd[6];
   const int chunk = local / colsets;
   const int cset = local - chunk * colsets;
-  const int b0 = j0 + chunk * p.chunk_blocks;
-  const int b1 = min(j1, b0 + p.chunk_blocks);
+  const int b0 = j0 + chunk * nd[8];
+  const int b1 = min(j1, b0 + nd[8]);
+  const int nst = (b1 - b0 + 1) >> 1;  // stages; the last may hold one block
   const int m0 = cset * p.per_set;
   const int cols = min(p.per_set, members - m0) * p.group;
-  const int ct = (cols + 15) >> 4;
-  const int ctp = ct <= 1 ? 1 : ct <= 2 ? 2 : 4;  // column tiles, rounded up to a power of two
-  const int wpt = 4 / ctp;                        // waves per column tile
-  const int tile = wave / wpt;
-  const int sub = wave - tile * wpt;
   const float c2 = p.scale_log2;
 
-  // this lane's column: (member, query head) of the set; columns past the
-  // set repeat its first one and write nothing
-  const int col = tile * 16 + n;
-  const bool col_ok = col < cols;
-  const int cc = col_ok ? col : 0;
-  const int mem = p.order[first + m0 + cc / p.group];
-  const int qh = kvh * p.group + (cc - (cc / p.group) * p.group);
+  // this lane's columns: group j is columns (RG wave + j) * 16 + n of the
+  // set, a (member, query head) pair each; columns past the set repeat its
+  // first one and write nothing
+  auto column = [&](int j, int& mem, int& qh) __attribute__((always_inline)) -> bool {
+    const int c = (RG * wave + j) * 16 + n;
+    const int cc = c < cols ? c : 0;
+    mem = p.order[first + m0 + cc / p.group];
+    qh = kvh * p.group + (cc - (cc / p.group) * p.group);
+    return c < cols;
+  };
+  u32x4 qb[RG][4];
+#pragma unroll
+  for (int j = 0; j < RG; ++j) {
+    int mem, qh;
+    column(j, mem, qh);
+    const char* qrow = p.q + (int64_t(mem) * p.num_q_heads + qh) * ROWB;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) qb[j][kt] = *reinterpret_cast<const u32x4*>(qrow + 64 * kt + 16 * g);
+  }
+  // waves whose columns all lie past the set only stage
+  const bool active = (RG * wave) * 16 < cols;
+
+  // ---- staging: global -> registers -> LDS ----------------------------------
+  const int32_t* trow = p.block_tables + int64_t(rep) * p.table_stride;
+  const int64_t blk_stride = int64_t(p.num_kv_heads) * TILE;
+  const char* kbase = p.k_cache + int64_t(kvh) * TILE;
+  const char* vbase = p.v_cache + int64_t(kvh) * TILE;
+  // table entries b0 + 64 c .. + 63 in one register, one per lane
+  int tbl = -1, tbl_base = -kWave;
+  auto table_entry = [&](int b) __attribute__((always_inline)) -> int {
+    b = __builtin_amdgcn_readfirstlane(b);
+    const int base = b0 + ((b - b0) & ~(kWave - 1));
+    if (base != tbl_base) {  // wave-uniform; stages advance monotonically
+      tbl_base = base;
+      tbl = base + lane < b1 ? trow[base + lane] : -1;
+    }
+    return __builtin_amdgcn_readlane(tbl, b - base);
+  };
+  auto tile_rsrc = [&](const char* base, int blk) __attribute__((always_inline)) {
+    const bool ok = unsigned(blk) < unsigned(p.num_blocks);
+    return make_rsrc(base + (ok ? int64_t(blk) * blk_stride : 0), ok ? TILE : 0);
+  };
+  u32x4 kr[KL], vr0, vr1;
+  bool bad_ld[2] = {false, false}, bad_c[2] = {false, false};
+  auto load_stage = [&](int st) __attribute__((always_inline)) {
+    int ids[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int j = b0 + 2 * st + b;
+      ids[b] = j < b1 ? table_entry(j) : -1;
+      bad_ld[b] = !(unsigned(ids[b]) < unsigned(p.num_blocks));
+    }
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {  // K: thread tid, token 16 i + tid / 16, chunk tid % 16
+      const int tok = (tid + 256 * i) / CH, ch = tid % CH;
+      kr[i] = load_tile<CP>(tile_rsrc(kbase, ids[i]), (tok % kBlockTokens) * ROWB + ch * 16);
+    }
+    {  // V: thread tid, tokens 2 (tid / 16) and the next, chunk tid % 16
+      const int ch = tid % CH, tok = 2 * (tid / CH);
+      const auto rs = tile_rsrc(vbase, ids[tok / kBlockTokens]);
+      const int off = (tok % kBlockTokens) * ROWB + ch * 16;
+      vr0 = load_tile<CP>(rs, off);
+      vr1 = load_tile<CP>(rs, off + ROWB);
+    }
+  };
+  auto store_stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+      const int tok = (tid + 256 * i) / CH, ch = tid % CH;
+      *reinterpret_cast<u32x4*>(&lk[buf][tok * KROW + ch * 8]) = kr[i];
+    }
+    const int ch = tid % CH, tok = 2 * (tid / CH);
+    const uint32_t a[4] = {vr0.x, vr0.y, vr0.z, vr0.w};
+    const uint32_t b[4] = {vr1.x, vr1.y, vr1.z, vr1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t ea = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      const uint32_t eb = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      *reinterpret_cast<uint32_t*>(&lv[buf][(ch * 8 + e) * VROW + vt_col(ch * 8 + e, tok)]) = ea | (eb << 16);
+    }
+  };
+
+  // ---- compute ----------------------------------------------------------------
+  float m[RG], lsum[RG];
+  f4 o[RG][NDT];
+#pragma unroll
+  for (int j = 0; j < RG; ++j) {
+    m[j] = kNegBig;
+    lsum[j] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[j][dt] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    f4 sa[RG][2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int j = 0; j < RG; ++j) sa[j][blk] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&lk[buf][(blk * 16 + n) * KROW + 32 * kt + 8 * g]);
+#pragma unroll
+        for (int j = 0; j < RG; ++j) sa[j][blk] = mfma_k32<DT>(a, qb[j][kt], sa[j][blk]);
+      }
+    }
+    const bool bad[2] = {bad_c[0], bad_c[1]};
+    u32x4 pb[RG], pl[RG];
+    float alpha[RG];
+    bool rescale = false;
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      float s[8];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s[blk * 4 + v] = bad[blk] ? -INFINITY : sa[j][blk][v];
+      float mx = s[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+      mx = max_over_lane_groups(mx);
+      const float mxs = mx * c2;
+      const float mn = mxs > m[j] + kSharedSlack ? mxs : m[j];
+      alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
+      rescale |= mn > m[j];
+      m[j] = mn;
+      uint32_t ph[4], plo[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q2], c2, -mn));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q2 + 1], c2, -mn));
+        psum += x0 + x1;
+        const f2 xx = {x0, x1};
+        if constexpr (DT == PKV_F16) {
+          ph[q2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(xx, h2));
+        } else {
+          const b2 hi2 = __builtin_convertvector(xx, b2);
+          ph[q2] = __builtin_bit_cast(uint32_t, hi2);
+          plo[q2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(xx - __builtin_convertvector(hi2, f2), b2));
+        }
+      }
+      lsum[j] = lsum[j] * alpha[j] + psum;
+      pb[j] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+      if constexpr (DT == PKV_BF16) pl[j] = u32x4{plo[0], plo[1], plo[2], plo[3]};
+    }
+    // rescale the accumulators only when some column's maximum moved
+    if (__builtin_amdgcn_ballot_w64(rescale)) {
+#pragma unroll
+      for (int j = 0; j < RG; ++j)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[j][dt] *= alpha[j];
+    }
+    // V^T operands (dims 16 dt + n, tokens 4g .. 4g + 3 of each block),
+    // each read one d-tile ahead of its products
+    auto vt_operand = [&](int dt) __attribute__((always_inline)) -> u32x4 {
+      const uint16_t* vrow = &lv[buf][(dt * 16 + n) * VROW];
+      const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow + vt_col(dt * 16, 4 * g));
+      const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + vt_col(dt * 16, 16 + 4 * g));
+      return u32x4{a0.x, a0.y, a1.x, a1.y};
+    };
+    u32x4 a_next = vt_operand(0);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const u32x4 a = a_next;
+      if (dt + 1 < NDT) a_next = vt_operand(dt + 1);
+#pragma unroll
+      for (int j = 0; j < RG; ++j) {
+        o[j][dt] = mfma_k32<DT>(a, pb[j], o[j][dt]);
+        if constexpr (DT == PKV_BF16) o[j][dt] = mfma_k32<DT>(a, pl[j], o[j][dt]);
+      }
+    }
+  };
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    const bool more = st + 1 < nst;
+    bad_c[0] = bad_ld[0];
+    bad_c[1] = bad_ld[1];
+    if (more) load_stage(st + 1);
+    if (active) compute(buf);
+    if (more) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // records: column n of group j -> (member, query head) of the set
+  const int64_t rec_step = int64_t(p.num_q_heads) * p.rec_floats;
+#pragma unroll
+  for (int j = 0; j < RG; ++j) {
+    float lt = lsum[j] + __shfl_xor(lsum[j], 16);
+    lt += __shfl_xor(lt, 32);
+    int mem, qh;
+    if (!column(j, mem, qh)) continue;
+    const int po = p.part_offset[mem];
+    const int ridx = po + k_base + chunk;
+    if (po < 0 || ridx >= p.n_partials) continue;
+    float* rec = p.part + int64_t(ridx) * rec_step + int64_t(qh) * p.rec_floats;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f4*>(rec + dt * 16 + 4 * g) = o[j][dt];
+    if (g == 0) {
+      rec[D] = m[j];
+      rec[D + 1] = lt;
+    }
+  }
+}
+
+// Narrow shared nodes (at most 16 (member, query head) columns): one
+// workgroup per (chunk, KV head) whose four waves stream the chunk's blocks
+// as the grouped-query kernel does (register ping-pong, K through
+// wave-private LDS rows into the A operand, V rows paired into the A
+// operand of O^T += V^T P^T), with the node's columns as the 16 columns of
+// the products.  The waves' states merge in LDS and become one record per
+// column and chunk.  Blocks here are read once per launch: streaming loads.
+template <int DT, int CP>
+__global__ __launch_bounds__(256, 3) void paged_decode_narrow_kernel(const SharedParams p) {
+  constexpr int NW = 4;
+  constexpr int D = 128;
+  constexpr int R = D * 2;
+  constexpr int TILE = kBlockTokens * R;
+  constexpr int KROWB = R + 16;
+  __shared__ float sm_m[NW * 16];
+  __shared__ float sm_l[NW * 16];
+  __shared__ __attribute__((aligned(16))) float sm_o[NW * 16 * D];
+  __shared__ __attribute__((aligned(16))) char sm_k[NW * kBlockTokens * KROWB];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int item = blockIdx.x / p.num_kv_heads;
+  const int kvh = blockIdx.x - item * p.num_kv_heads;
+  int lo = 0, hi = p.n_nodes - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.nodes[kNodeInts * mid + 6] <= item) lo = mid;
+    else hi = mid - 1;
+  }
+  const int32_t* nd = p.nodes + kNodeInts * lo;
+  const int rep = nd[0], j0 = nd[1], j1 = nd[2], first = nd[3], members = nd[4], k_base = nd[5];
+  const int chunk = item - nd[6];
+  const int b0 = j0 + chunk * nd[8];
+  const int b1 = min(j1, b0 + nd[8]);
+  const int cols = min(16, members * p.group);
+  const float c2 = p.scale_log2;
+  char* const klds = sm_k + wave * kBlockTokens * KROWB;
+
+  // column n: a (member, query head) pair of the node; past the node's
+  // columns, copies of column 0 that write nothing
+  auto column = [&](int c, int& mem, int& qh) __attribute__((always_inline)) {
+    const int cc = c < cols ? c : 0;
+    mem = p.order[first + cc / p.group];
+    qh = kvh * p.group + (cc - (cc / p.group) * p.group);
+  };
   u32x4 qb[4];
   {
+    int mem, qh;
+    column(n, mem, qh);
     const char* qrow = p.q + (int64_t(mem) * p.num_q_heads + qh) * R;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) qb[kc] = *reinterpret_cast<const u32x4*>(qrow + 64 * kc + 16 * g);
@@ -814,101 +1109,94 @@ __global__ __launch_bounds__(256, 2) void paged_decode_shared_kernel(const Share
 
   const int32_t* trow = p.block_tables + int64_t(rep) * p.table_stride;
   const int64_t blk_stride = int64_t(p.num_kv_heads) * TILE;
-  const int tid = threadIdx.x;
-  // staging: thread tid moves bytes [16 tid, 16 tid + 16) of each tile, i.e.
-  // token tid / 16, dims 8 (tid % 16) .. + 7
-  const int st_off = (tid >> 4) * kSharedRowB + 16 * (tid & 15);
-  u32x4 rk[kSharedStage], rv[kSharedStage];
-  auto issue = [&](int sb) __attribute__((always_inline)) {
+  int cb = 0, ce = 0, tbl = -1;
+  const int koff = 16 * lane;
+  const int voff = 4 * g * R + 16 * n;
+  // every block of a node is full; a table entry outside the pool reads
+  // nothing and is masked
+  auto issue = [&](int j, u32x4* kk, u32x4* vv) __attribute__((always_inline)) -> bool {
+    const int blk = __builtin_amdgcn_readlane(tbl, min(j - cb, kWave - 1));
+    const bool ok = j < ce && unsigned(blk) < unsigned(p.num_blocks);
+    const int64_t tile = int64_t(ok ? blk : 0) * blk_stride + int64_t(kvh) * TILE;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_cache + tile, ok ? TILE : 0);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_cache + tile, ok ? TILE : 0);
 #pragma unroll
-    for (int i = 0; i < kSharedStage; ++i) {
-      const int j = sb + i;
-      const int blk = j < b1 ? trow[j] : -1;
-      const bool ok = unsigned(blk) < unsigned(p.num_blocks);
-      const int64_t tile_off = int64_t(ok ? blk : 0) * blk_stride + int64_t(kvh) * TILE;
-      rk[i] = load_tile<CP>(make_rsrc(p.k_cache + tile_off, ok ? TILE : 0), 16 * tid);
-      rv[i] = load_tile<CP>(make_rsrc(p.v_cache + tile_off, ok ? TILE : 0), 16 * tid);
+    for (int i = 0; i < 4; ++i) kk[i] = load_tile_s<CP>(rk, koff, 1024 * i);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) vv[t] = load_tile_s<CP>(rv, voff, t * R);
+    return ok;
+  };
+  auto process = [&](const u32x4* kk, const u32x4* vv, bool ok) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(klds + (4 * i + g) * KROWB + 16 * n) = kk[i];
+    f4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+      sacc = mfma_k32<DT>(*reinterpret_cast<const u32x4*>(klds + n * KROWB + 64 * kc + 16 * g), qb[kc], sacc);
+    float sc[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
+    if (!ok) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = -INFINITY;
+    }
+    const float mx = max_over_lane_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const float mn = fmaxf(m, mx * c2);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c2, -mn));
+    lsum = lsum * alpha + ((x[0] + x[1]) + (x[2] + x[3]));
+    const f2 x01 = {x[0], x[1]}, x23 = {x[2], x[3]};
+    u32x2 pb, pl;
+    if constexpr (DT == PKV_F16) {
+      pb = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01, h2)),
+                 __builtin_bit_cast(uint32_t, __builtin_convertvector(x23, h2))};
+    } else {
+      const b2 h01 = __builtin_convertvector(x01, b2), h23 = __builtin_convertvector(x23, b2);
+      pb = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+      pl = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01 - __builtin_convertvector(h01, f2), b2)),
+                 __builtin_bit_cast(uint32_t, __builtin_convertvector(x23 - __builtin_convertvector(h23, f2), b2))};
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) o[t] *= alpha;
+    const uint32_t v0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
+    const uint32_t v1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+    const uint32_t v2[4] = {vv[2].x, vv[2].y, vv[2].z, vv[2].w};
+    const uint32_t v3[4] = {vv[3].x, vv[3].y, vv[3].z, vv[3].w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u32x2 lo2 = {(v0[w] & 0xFFFFu) | (v1[w] << 16), (v2[w] & 0xFFFFu) | (v3[w] << 16)};
+      const u32x2 hi2 = {(v0[w] >> 16) | (v1[w] & 0xFFFF0000u), (v2[w] >> 16) | (v3[w] & 0xFFFF0000u)};
+      o[2 * w] = mfma_k16<DT>(lo2, pb, o[2 * w]);
+      o[2 * w + 1] = mfma_k16<DT>(hi2, pb, o[2 * w + 1]);
+      if constexpr (DT == PKV_BF16) {
+        o[2 * w] = mfma_k16<DT>(lo2, pl, o[2 * w]);
+        o[2 * w + 1] = mfma_k16<DT>(hi2, pl, o[2 * w + 1]);
+      }
     }
   };
 
-  issue(b0);
-  for (int sb = b0; sb < b1; sb += kSharedStage) {
-    __syncthreads();  // every wave is done with the previous stage
-#pragma unroll
-    for (int i = 0; i < kSharedStage; ++i) {
-      *reinterpret_cast<u32x4*>(sm + i * TILE_LDS + st_off) = rk[i];
-      *reinterpret_cast<u32x4*>(sm + (kSharedStage + i) * TILE_LDS + st_off) = rv[i];
-    }
-    __syncthreads();
-    issue(sb + kSharedStage);  // past b1: no records, nothing read
-    const int nb = min(kSharedStage, b1 - sb);
-    for (int i = sub; i < nb; i += wpt) {
-      const char* kl = sm + i * TILE_LDS;
-      const char* vl = sm + (kSharedStage + i) * TILE_LDS;
-      const bool blk_ok = unsigned(trow[sb + i]) < unsigned(p.num_blocks);
-      f4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        sacc = mfma_k32<DT>(*reinterpret_cast<const u32x4*>(kl + n * kSharedRowB + 64 * kc + 16 * g), qb[kc], sacc);
-      float sc[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
-      if (!blk_ok) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = -INFINITY;
-      }
-      const float mx = max_over_lane_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-      const float mn = fmaxf(m, mx * c2);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      m = mn;
-      float x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c2, -mn));
-      lsum = lsum * alpha + ((x[0] + x[1]) + (x[2] + x[3]));
-      const f2 x01 = {x[0], x[1]}, x23 = {x[2], x[3]};
-      u32x2 pb, pl;
-      if constexpr (DT == PKV_F16) {
-        pb = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01, h2)),
-                   __builtin_bit_cast(uint32_t, __builtin_convertvector(x23, h2))};
-      } else {
-        const b2 h01 = __builtin_convertvector(x01, b2), h23 = __builtin_convertvector(x23, b2);
-        pb = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
-        pl = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01 - __builtin_convertvector(h01, f2), b2)),
-                   __builtin_bit_cast(uint32_t, __builtin_convertvector(x23 - __builtin_convertvector(h23, f2), b2))};
-      }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) o[t] *= alpha;
-      // rows 4 g + j of the V tile, dims 8 n .. 8 n + 7 (the grouped-query
-      // kernel's V layout), paired into the A operand of O^T += V^T P^T
-      uint32_t vw[4][4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const u32x4 vv = *reinterpret_cast<const u32x4*>(vl + (4 * g + jj) * kSharedRowB + 16 * n);
-        vw[jj][0] = vv.x;
-        vw[jj][1] = vv.y;
-        vw[jj][2] = vv.z;
-        vw[jj][3] = vv.w;
-      }
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const u32x2 lo2 = {(vw[0][w] & 0xFFFFu) | (vw[1][w] << 16), (vw[2][w] & 0xFFFFu) | (vw[3][w] << 16)};
-        const u32x2 hi2 = {(vw[0][w] >> 16) | (vw[1][w] & 0xFFFF0000u), (vw[2][w] >> 16) | (vw[3][w] & 0xFFFF0000u)};
-        o[2 * w] = mfma_k16<DT>(lo2, pb, o[2 * w]);
-        o[2 * w + 1] = mfma_k16<DT>(hi2, pb, o[2 * w + 1]);
-        if constexpr (DT == PKV_BF16) {
-          o[2 * w] = mfma_k16<DT>(lo2, pl, o[2 * w]);
-          o[2 * w + 1] = mfma_k16<DT>(hi2, pl, o[2 * w + 1]);
-        }
-      }
+  u32x4 ka[4], va[4], kb[4], vb[4];
+  for (cb = b0; cb < b1; cb += kWave) {
+    ce = min(cb + kWave, b1);
+    tbl = (cb + lane < ce) ? trow[cb + lane] : -1;
+    int j = cb + wave;
+    if (j >= ce) break;
+    bool ok_a = issue(j, ka, va), ok_b;
+    while (true) {
+      ok_b = issue(j + NW, kb, vb);
+      process(ka, va, ok_a);
+      j += NW;
+      if (j >= ce) break;
+      ok_a = issue(j + NW, ka, va);
+      process(kb, vb, ok_b);
+      j += NW;
+      if (j >= ce) break;
     }
   }
 
-  // per wave and column: m, the sum over the four lane groups, and o with
-  // dims 32 g + 8 r + t in o[t][r]; waves of one column tile merge in LDS
   float lt = lsum + __shfl_xor(lsum, 16);
   lt += __shfl_xor(lt, 32);
-  __syncthreads();  // the stage area becomes the merge area
-  float* sm_m = reinterpret_cast<float*>(sm);
-  float* sm_l = sm_m + 4 * 16;
-  float* sm_o = sm_l + 4 * 16;
   if (g == 0) {
     sm_m[wave * 16 + n] = m;
     sm_l[wave * 16 + n] = lt;
@@ -923,25 +1211,26 @@ __global__ __launch_bounds__(256, 2) void paged_decode_shared_kernel(const Share
   }
   __syncthreads();
   const int64_t rec_step = int64_t(p.num_q_heads) * p.rec_floats;
-  for (int idx = threadIdx.x; idx < ct * 16 * D; idx += 256) {
-    const int c = idx / D;  // column of the set
+  for (int idx = threadIdx.x; idx < cols * D; idx += 256) {
+    const int c = idx / D;
     const int dd = idx - c * D;
-    if (c >= cols) continue;
-    const int t = c >> 4, cn = c & 15;
     float M = -INFINITY;
-    for (int w = t * wpt; w < (t + 1) * wpt; ++w) M = fmaxf(M, sm_m[w * 16 + cn]);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w * 16 + c]);
     const float M_use = (M == -INFINITY) ? 0.f : M;
     float num = 0.f, den = 0.f;
-    for (int w = t * wpt; w < (t + 1) * wpt; ++w) {
-      const float wt = __builtin_amdgcn_exp2f(sm_m[w * 16 + cn] - M_use);
-      num = __builtin_fmaf(wt, sm_o[(w * 16 + cn) * D + dd], num);
-      den = __builtin_fmaf(wt, sm_l[w * 16 + cn], den);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(sm_m[w * 16 + c] - M_use);
+      num = __builtin_fmaf(wt, sm_o[(w * 16 + c) * D + dd], num);
+      den = __builtin_fmaf(wt, sm_l[w * 16 + c], den);
     }
-    const int mc = p.order[first + m0 + c / p.group];
-    const int qc = kvh * p.group + (c - (c / p.group) * p.group);
-    const int ridx = p.part_offset[mc] + k_base + chunk;
-    if (p.part_offset[mc] < 0 || ridx >= p.n_partials) continue;
-    float* rec = p.part + int64_t(ridx) * rec_step + int64_t(qc) * p.rec_floats;
+    int mem, qh;
+    column(c, mem, qh);
+    const int po = p.part_offset[mem];
+    const int ridx = po + k_base + chunk;
+    if (po < 0 || ridx >= p.n_partials) continue;
+    float* rec = p.part + int64_t(ridx) * rec_step + int64_t(qh) * p.rec_floats;
     rec[dd] = num;
     if (dd == 0) {
       rec[D] = M;
@@ -981,16 +1270,8 @@ __global__ __launch_bounds__(D) void paged_decode_reduce_kernel(const ReducePara
   const int dd = threadIdx.x;
   const float* rec0 = p.part + (int64_t(base) * p.num_q_heads + h) * p.rec_floats;
   const int64_t step = int64_t(p.num_q_heads) * p.rec_floats;
-  float M = -INFINITY;
-  for (int q = 0; q < n_parts; ++q) M = fmaxf(M, rec0[q * step + D]);
-  const float M_use = (M == -INFINITY) ? 0.f : M;
-  float num = 0.f, den = 0.f;
-  for (int q = 0; q < n_parts; ++q) {
-    const float* rec = rec0 + q * step;
-    const float w = __builtin_amdgcn_exp2f(rec[D] - M_use);
-    num = __builtin_fmaf(w, rec[dd], num);
-    den = __builtin_fmaf(w, rec[D + 1], den);
-  }
+  float M = -INFINITY, num = 0.f, den = 0.f;
+  merge_records<D, false>(rec0, step, n_parts, dd, M, num, den);
   p.out[(int64_t(seq) * p.num_q_heads + h) * D + dd] = num / den;
 }
 
@@ -1086,15 +1367,20 @@ DecodeFn pick_mfma(int dt, int gw, int& nw, bool reuse) {
   }
 }
 
-// Waves per workgroup (they split a partition's blocks): 4 by default, the
-// best of {1, 2, 4, 8} on the GPT-style fp16 batch; PKV_DECODE_WAVES
-// overrides it for tuning sweeps.  The tuning variables are read at every
-// launch (a lookup in the environment, next to a launch of tens of
-// microseconds), so one process can run every variant.
-int waves_per_item() {
+// Waves per workgroup (they split a work item's blocks): 4 for items of 16
+// blocks or more on average (the best of {1, 2, 4, 8} on the GPT-style fp16
+// batch, ~28 blocks per item), 2 from 6 blocks and 1 below: a short item
+// leaves most of four waves idle, and the own parts that follow a
+// shared-block launch are a few blocks each (a prefix-shared batch of 256:
+// 0.2457 ms per decode with 4 waves, 0.2298 with 2, 0.2245 with 1).
+// PKV_DECODE_WAVES overrides the choice for tuning sweeps.  The tuning
+// variables are read at every launch (a lookup in the environment, next to
+// a launch of tens of microseconds), so one process can run every variant.
+int waves_per_item(int item_blocks) {
   const char* s = std::getenv("PKV_DECODE_WAVES");
   const int v = s ? std::atoi(s) : 0;
-  return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 4;
+  if (v == 1 || v == 2 || v == 4 || v == 8) return v;
+  return item_blocks >= 16 ? 4 : item_blocks >= 6 ? 2 : 1;
 }
 
 // Query heads of one KV head that one workgroup takes (GW): all of them,
@@ -1186,11 +1472,12 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
   if (info->n_nodes > 0) {
     if ((d.dtype != PKV_F16 && d.dtype != PKV_BF16) || d.head_dim != 128)
       return fail(PKV_E_UNSUPPORTED, "shared-block plans take fp16 / bf16 pools of head_dim 128");
-    if (info->shared_group != group || info->shared_chunk_blocks < 1 || info->n_shared_items < 1 ||
-        info->off_shared < 2 * info->n_work + num_seqs + info->n_reduce ||
-        int64_t(info->off_shared) + 3 * int64_t(num_seqs) + 8 * int64_t(info->n_nodes) > info->plan_ints)
+    if (info->shared_group != group || info->shared_chunk_blocks < 1 || info->narrow_chunk_blocks < 1 ||
+        info->n_wide_nodes < 0 || info->n_wide_nodes > info->n_nodes || info->n_shared_items < 0 ||
+        info->n_narrow_items < 0 || info->off_shared < 2 * info->n_work + num_seqs + info->n_reduce ||
+        int64_t(info->off_shared) + 3 * int64_t(num_seqs) + kNodeInts * int64_t(info->n_nodes) > info->plan_ints)
       return fail(PKV_E_BAD_ARG, "shared-block plan does not match this batch (made for another head count?)");
-    if (int64_t(info->n_shared_items) * d.num_kv_heads > INT32_MAX)
+    if (int64_t(std::max(info->n_shared_items, info->n_narrow_items)) * d.num_kv_heads > INT32_MAX)
       return fail(PKV_E_BAD_ARG, "shared launch too large");
     prm.priv_start = plan + info->off_shared;
     prm.n_shared = prm.priv_start + num_seqs;
@@ -1243,20 +1530,41 @@ pkv_status launch_shared(const pkv_pool* pool, const DecodeParams& prm, const in
   sp.group = prm.group;
   sp.table_stride = prm.table_stride;
   sp.num_blocks = prm.num_blocks;
-  sp.n_nodes = info->n_nodes;
-  sp.chunk_blocks = info->shared_chunk_blocks;
-  sp.per_set = 64 / prm.group;
+  sp.n_nodes = info->n_wide_nodes;
+  sp.per_set = kSharedCols / prm.group;
   sp.n_partials = info->n_partials;
   sp.scale_log2 = prm.scale_log2;
-  void (*fn)(const SharedParams) = pool->desc.dtype == PKV_F16
-                                       ? paged_decode_shared_kernel<PKV_F16, kCacheReuse>
-                                       : paged_decode_shared_kernel<PKV_BF16, kCacheReuse>;
-  const uint32_t grid = uint32_t(int64_t(info->n_shared_items) * prm.num_kv_heads);
-  if (ev_start)
-    hipExtLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, s, ev_start, nullptr, 0, sp);
-  else
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, s, sp);
-  return launch_status("paged_decode shared-block launch");
+  // PKV_SHARED_WAVES (2 or 3, read at every launch) picks the register
+  // budget for tuning sweeps
+  const char* e = std::getenv("PKV_SHARED_WAVES");
+  const bool three = e && e[0] == '3';
+  void (*fn)(const SharedParams) =
+      pool->desc.dtype == PKV_F16
+          ? (three ? paged_decode_shared_kernel<PKV_F16, kCacheReuse, 3> : paged_decode_shared_kernel<PKV_F16, kCacheReuse, 2>)
+          : (three ? paged_decode_shared_kernel<PKV_BF16, kCacheReuse, 3> : paged_decode_shared_kernel<PKV_BF16, kCacheReuse, 2>);
+  if (info->n_wide_nodes > 0 && info->n_shared_items > 0) {
+    const uint32_t grid = uint32_t(int64_t(info->n_shared_items) * prm.num_kv_heads);
+    if (ev_start)
+      hipExtLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, s, ev_start, nullptr, 0, sp);
+    else
+      hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, s, sp);
+    if (pkv_status st = launch_status("paged_decode wide shared-block launch")) return st;
+    ev_start = nullptr;
+  }
+  if (info->n_nodes > info->n_wide_nodes && info->n_narrow_items > 0) {
+    SharedParams np = sp;
+    np.nodes = sp.nodes + kNodeInts * int64_t(info->n_wide_nodes);
+    np.n_nodes = info->n_nodes - info->n_wide_nodes;
+    void (*nfn)(const SharedParams) = pool->desc.dtype == PKV_F16 ? paged_decode_narrow_kernel<PKV_F16, kCacheStream>
+                                                                  : paged_decode_narrow_kernel<PKV_BF16, kCacheStream>;
+    const uint32_t grid = uint32_t(int64_t(info->n_narrow_items) * prm.num_kv_heads);
+    if (ev_start)
+      hipExtLaunchKernelGGL(nfn, dim3(grid), dim3(256), 0, s, ev_start, nullptr, 0, np);
+    else
+      hipLaunchKernelGGL(nfn, dim3(grid), dim3(256), 0, s, np);
+    if (pkv_status st = launch_status("paged_decode narrow shared-block launch")) return st;
+  }
+  return PKV_OK;
 }
 
 pkv_status launch_partitions(const pkv_pool* pool, const DecodeParams& prm, int gw, bool mfma,
@@ -1268,7 +1576,7 @@ pkv_status launch_partitions(const pkv_pool* pool, const DecodeParams& prm, int 
     if (pkv_status st = launch_shared(pool, prm, prm.work, info, s, ev_start)) return st;
     ev_start = nullptr;
   }
-  int nw = waves_per_item();  // becomes the chosen instance's waves
+  int nw = waves_per_item(info->item_blocks);  // becomes the chosen instance's waves
   const bool reuse = info->shared_kv != 0;
   DecodeFn fn = mfma ? pick_mfma(pool->desc.dtype, gw, nw, reuse)
                      : pick_decode(pool->desc.dtype, pool->desc.head_dim, gw, nw, reuse);
@@ -1334,7 +1642,7 @@ extern "C" pkv_status pkv_decode_occupancy(const pkv_pool* pool, int32_t num_q_h
   bool mfma = mfma_eligible(group, d.dtype, d.head_dim);
   const int gw = heads_per_workgroup(group, mfma ? 16 : 8);
   if (gw < 2) mfma = false;
-  int nw = waves_per_item();  // becomes the chosen instance's waves
+  int nw = waves_per_item(16);  // long items, where filling the GPU matters; becomes the instance's waves
   DecodeFn fn = mfma ? pick_mfma(d.dtype, gw, nw, false) : pick_decode(d.dtype, d.head_dim, gw, nw, false);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group");
   int per_cu = 0, dev = 0, cus = 0;

@@ -285,15 +285,18 @@ static void fuzz_shared_plan(std::mt19937& rng) {
       CHECK(nsh[i] <= PKV_MAX_SHARED_RECORDS);
     }
     std::vector<std::vector<int32_t>> recs(n);
-    int64_t items = 0;
-    const int32_t cb = info.shared_chunk_blocks;
+    int64_t items[2] = {0, 0};
     for (int32_t v = 0; v < info.n_nodes; ++v) {
-      const int32_t* nd = nodes + 8 * v;
+      const int32_t* nd = nodes + 9 * v;
       const int32_t rep = nd[0], j0 = nd[1], j1 = nd[2], first = nd[3], mem = nd[4], kb = nd[5];
-      CHECK(nd[6] == items && j0 < j1 && mem >= 2 && first + mem <= n);
-      CHECK(nd[7] == (mem * group + 63) / 64);
+      const int narrow = v >= info.n_wide_nodes ? 1 : 0;
+      CHECK((mem * group <= 16) == (narrow == 1));
+      const int32_t cb = nd[8];
+      CHECK(cb >= (narrow ? info.narrow_chunk_blocks : info.shared_chunk_blocks));
+      CHECK(nd[6] == items[narrow] && j0 < j1 && mem >= 2 && first + mem <= n);
+      CHECK(nd[7] == (narrow ? 1 : (mem * group + 127) / 128));
       const int32_t nch = (j1 - j0 + cb - 1) / cb;
-      items += int64_t(nch) * nd[7];
+      items[narrow] += int64_t(nch) * nd[7];
       bool rep_in = false;
       for (int32_t t = first; t < first + mem; ++t) {
         const int32_t s = order[t];
@@ -307,7 +310,7 @@ static void fuzz_shared_plan(std::mt19937& rng) {
       }
       CHECK(rep_in);
     }
-    CHECK(items == info.n_shared_items);
+    CHECK(items[0] == info.n_shared_items && items[1] == info.n_narrow_items);
     for (int32_t i = 0; i < n; ++i) {
       std::sort(recs[i].begin(), recs[i].end());
       CHECK(int32_t(recs[i].size()) == nsh[i]);

@@ -55,11 +55,11 @@ def sections(plan, info, n):
         return work, part_offset, np.zeros(n, np.int64), np.zeros(n, np.int64), None, None
     sec = plan[info.off_shared:]
     priv, nsh, order = sec[:n], sec[n:2 * n], sec[2 * n:3 * n]
-    nodes = sec[3 * n:3 * n + 8 * info.n_nodes].reshape(info.n_nodes, 8)
+    nodes = sec[3 * n:3 * n + 9 * info.n_nodes].reshape(info.n_nodes, 9)
     return work, part_offset, priv, nsh, order, nodes
 
 
-def check_plan(pool, seqs, plan, info, P, group):
+def check_plan(pool, seqs, plan, info, P, group, chunk_fixed=False):
     n = len(seqs)
     tabs = [pool.table(s) for s in seqs]
     nblk = [len(t) for t in tabs]
@@ -68,19 +68,27 @@ def check_plan(pool, seqs, plan, info, P, group):
     recs = [[] for _ in range(n)]
     if info.n_nodes:
         assert sorted(order.tolist()) == list(range(n))
-        cb, items = info.shared_chunk_blocks, 0
-        for rep, j0, j1, first, mem, kb, fi, cs in nodes.tolist():
-            assert fi == items and j0 < j1 and mem >= 2 and cs == -(-mem * group // 64)
+        items = [0, 0]
+        for v, (rep, j0, j1, first, mem, kb, fi, cs, cb) in enumerate(nodes.tolist()):
+            narrow = v >= info.n_wide_nodes
+            assert narrow == (mem * group <= 16)  # wide nodes first
+            assert cb >= (info.narrow_chunk_blocks if narrow else info.shared_chunk_blocks)
+            if chunk_fixed:
+                assert cb == (info.narrow_chunk_blocks if narrow else info.shared_chunk_blocks)
+            else:  # long nodes in at most 8 (wide) or 4 (narrow) chunks
+                assert -(-(j1 - j0) // cb) <= (4 if narrow else 8)
+            assert fi == items[narrow] and j0 < j1 and mem >= 2
+            assert cs == (1 if narrow else -(-mem * group // 128))
             members = order[first:first + mem].tolist()
             assert rep in members
             nch = -(-(j1 - j0) // cb)
-            items += nch * cs
+            items[narrow] += nch * cs
             for s in members:
                 assert j1 <= nblk[s] - 1  # never a member's last block
                 assert tabs[s][j0:j1] == tabs[rep][j0:j1]
                 cover[s][j0:j1] += 1
                 recs[s] += [kb + c for c in range(nch)]
-        assert items == info.n_shared_items
+        assert items == [info.n_shared_items, info.n_narrow_items]
     for i in range(n):
         assert sorted(recs[i]) == list(range(int(nsh[i])))
         assert nsh[i] <= _capi.MAX_SHARED_RECORDS
@@ -114,7 +122,8 @@ def test_shared_plan_covers_every_block_once(group, chunk):
             assert info.n_nodes > 0 and info.shared_group == group and info.shared_kv == 0
             if chunk:
                 assert info.shared_chunk_blocks == chunk // BS
-            check_plan(pool, seqs, plan, info, P, group)
+                assert info.narrow_chunk_blocks == max(chunk // BS, 64)
+            check_plan(pool, seqs, plan, info, P, group, chunk_fixed=chunk > 0)
     finally:
         pool.close()
 
@@ -134,11 +143,13 @@ def test_records_per_sequence_are_capped():
         for x in chain:
             pool.append(x, 1)
         pool.take_cow()
-        plan, info = decode_plan_shared(pool, chain, 1, 256, BS)
-        assert info.n_nodes > 0
+        # 16 query heads per KV head: every node is wide and takes the
+        # one-block chunks asked for
+        plan, info = decode_plan_shared(pool, chain, 16, 256, BS)
+        assert info.n_nodes > 0 and info.n_wide_nodes == info.n_nodes
         nsh = plan[info.off_shared + len(chain):info.off_shared + 2 * len(chain)]
         assert nsh.max() == _capi.MAX_SHARED_RECORDS
-        check_plan(pool, chain, plan, info, 256, 1)
+        check_plan(pool, chain, plan, info, 256, 16, chunk_fixed=True)
     finally:
         pool.close()
 
@@ -191,8 +202,7 @@ def test_attention_from_plan_pieces_equals_whole_sequence():
         tabs = [pool.table(s) for s in seqs]
         lens = [pool.length(s) for s in seqs]
         pieces = [[] for _ in range(n)]  # (first token, last token + 1)
-        cb = info.shared_chunk_blocks
-        for rep, j0, j1, first, mem, kb, fi, cs in nodes.tolist():
+        for rep, j0, j1, first, mem, kb, fi, cs, cb in nodes.tolist():
             for s in order[first:first + mem].tolist():
                 for c in range(-(-(j1 - j0) // cb)):
                     lo = (j0 + c * cb) * BS

@@ -137,7 +137,7 @@ def test_shared_decode_matches_oracle(dtype, kv_heads, group):
     case = ForkedCase(70 + group, dtype, kv_heads, group)
     try:
         ref = np.stack(oracle_map(case.oracle_out, range(len(case.seqs))))
-        for P, chunk, kw in [(2048, 0, {}), (256, 16, {}), (512, 64, {"split": True}), (2048, 32, {"noalloc": True}),
+        for P, chunk, kw in [(2048, 0, {}), (256, 64, {}), (512, 128, {"split": True}), (2048, 256, {"noalloc": True}),
                              (128, 0, {"append": True})]:
             print(f"\n[gpu] shared {dtype} H={kv_heads} G={group} P={P} chunk={chunk} {kw}", flush=True)
             out, info = case.decode(P, chunk, **kw)
