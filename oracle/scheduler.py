@@ -121,6 +121,16 @@ class OracleScheduler:
                 and r.prefix_id not in self.holder:
             self.holder[r.prefix_id] = i
 
+    def _victim(self) -> int:
+        """Rule 2: the running request preempted first, the most recently
+        admitted one."""
+        return self.running[-1]
+
+    def _recompute_target(self, r: OracleRequest) -> int:
+        """Rule 2: tokens a (re)admitted request prefills, its prompt plus every
+        generated token but the newest, whose K/V the next decode appends."""
+        return r.prompt_len + max(r.generated - 1, 0)
+
     def _prefill_done(self, r: OracleRequest) -> None:
         if r.generated == 0:
             r.generated = 1
@@ -159,11 +169,11 @@ class OracleScheduler:
             # prefill's slice only sequences newer than it
             if dec_need <= free and (dec_need + pf_need <= free or self.running[-1] == first):
                 break
-            v = self.running[-1]
+            v = self._victim()
             r = self.reqs[v]
             self._drop_holder(v)
             self.a.free_seq(r.seq)
-            self.running.pop()
+            self.running.remove(v)
             r.seq, r.state, r.prefilled = -1, WAITING, 0
             r.preemptions += 1
             self.waiting.appendleft(v)
@@ -212,7 +222,7 @@ class OracleScheduler:
                 self.stats["rejected"] += 1
                 ev["rejected"] += 1
                 continue
-            target = r.prompt_len + max(r.generated - 1, 0)
+            target = self._recompute_target(r)
             h = self.holder.get(r.prefix_id) if r.prefix_id >= 0 and r.prefix_len > 0 else None
             start = r.prefix_len if h is not None else 0
             n = min(target - start, self.chunk, budget)
