@@ -165,6 +165,11 @@ def parse_args(argv=None):
                     help="prefix-shared loop: attach HIP timing events to every N-th iteration's decode")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--gather-probe", action="store_true",
+                    help="time the decode launch of the workload's batch beside the gather probe "
+                         "(the same tile reads without the arithmetic) in each staging mode, and the "
+                         "register-staged decode instance where the default stages through LDS; "
+                         "prints one JSON line")
     return ap.parse_args(argv)
 
 
@@ -178,6 +183,102 @@ def calib_copy():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calib_copy_bytes": n, "launches": 3}))
+
+
+def bench_gather_probe(args, cfg):
+    """The decode launch of the workload's batch (contexts as drawn, no
+    append) against the gather probe on the same tables and plan: the rate
+    of the decode's own tile reads with no arithmetic, per staging mode.
+    Each kernel runs N times back to back between two events on the launch
+    stream; its time is the span / N."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_257_amd import Pool, decode_plan, decode_workspace_bytes
+    from paged_kv_cache_257_amd.pool import fill_partition
+    from workloads import draw_decode_values
+    from workloads.configs import draw_decode_shapes
+
+    sh = draw_decode_shapes(cfg)
+    vals = draw_decode_values(cfg, sh.lens)
+    B, Hq, H, d, dt = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.dtype
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+
+    def dev(bits):
+        a = np.ascontiguousarray(bits)
+        t = torch.from_numpy(a.view(np.int16) if dt == "bf16" else a)
+        return (t.view(torch.bfloat16) if dt == "bf16" else t).to("cuda")
+
+    stride = -(-int(sh.lens.max()) // 16)
+    kc = torch.zeros((sh.num_blocks, H, 16, d), dtype=tdt, device="cuda")
+    vc = torch.zeros_like(kc)
+    pool = Pool(sh.num_blocks, H, d, dt, stride, 16, sh.free_order, kc, vc)
+    slots = np.concatenate([pool.alloc(int(L))[1] for L in sh.lens])
+    pool.write_kv(dev(vals["k"]), dev(vals["v"]), torch.from_numpy(slots).cuda())
+    tables, lens = pool.build_batch(list(range(B)), stride)
+    if args.partition == -1:
+        P = fill_partition(lens, *pool.decode_occupancy(Hq)) or 0
+    else:
+        P = args.partition
+    plan, info = decode_plan(lens, P)
+    t_d, l_d, p_d = (torch.from_numpy(a).cuda() for a in (tables, lens, plan))
+    q = dev(vals["q"])
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(max(decode_workspace_bytes(info, Hq, d) // 4, 1), dtype=torch.float32, device="cuda")
+    probe_out = torch.empty(info.n_work * H * 4, dtype=torch.int32, device="cuda")
+    per_tok = 2 * H * d * cfg.elem_bytes
+    alg = int(lens.sum()) * per_tok
+    tile_bytes = int(sum(-(-int(L) // 16) for L in lens)) * 16 * per_tok
+    n = max(args.steps, 50)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(max(args.warmup, 5)):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        return {"us": round(ms * 1e3, 2), "GBps": round(alg / ms / 1e6, 1),
+                "frac": round(alg / ms / 1e6 / HBM_PEAK_GBPS, 4)}
+
+    def decode():
+        pool.paged_decode(q, out, t_d, l_d, cfg.scale, p_d, info, ws)
+
+    res = {"mode": "gather_probe", "workload": cfg.name, "dtype": dt, "launches": n,
+           "partition_tokens": info.partition_tokens, "work_items": info.n_work,
+           "algorithmic_bytes": alg, "tile_bytes": tile_bytes, "kernels": {}}
+    res["kernels"]["decode"] = timed(decode)
+    tile = 16 * d * cfg.elem_bytes
+    if Hq == H and d == 128 and dt in ("f16", "bf16"):
+        # the default instance stages tiles through LDS; the register-staged
+        # one beside it
+        os.environ["PKV_DECODE_STAGING"] = "regs"
+        try:
+            res["kernels"]["decode_regs_staged"] = timed(decode)
+        finally:
+            del os.environ["PKV_DECODE_STAGING"]
+    # the probe in each staging mode at 4 and 2 waves per workgroup; the
+    # register modes also with 64 KiB of unused LDS per workgroup, which
+    # caps a CU at two workgroups as the LDS stages do (the register probe
+    # needs few registers and otherwise runs many more per CU)
+    for mode in ("regs", "cached", "lds"):
+        if mode == "lds" and tile > 4096:
+            continue
+        for waves in (4, 2):
+            for pad in ((0,) if mode == "lds" else (0, 65536)):
+                key = f"probe_{mode}_w{waves}" + ("_pad64k" if pad else "")
+                res["kernels"][key] = timed(
+                    lambda: pool.gather_probe(t_d, l_d, p_d, info, probe_out, mode, waves, pad))
+    best = max(v["GBps"] for k, v in res["kernels"].items() if k.startswith("probe_"))
+    res["gather_ceiling_GBps"] = best
+    res["decode_frac_of_ceiling"] = round(res["kernels"]["decode"]["GBps"] / best, 4)
+    print(json.dumps(res))
+    pool.close()
+    return 0
 
 
 def cpu_baseline(cfg, sh, vals, stride, budget_s):
@@ -669,6 +770,8 @@ def main(argv=None):
     cfg = config_by_name(args.workload)
     if isinstance(cfg, PrefixSharedConfig):
         return bench_prefix_shared(args, cfg)
+    if args.gather_probe:
+        return bench_gather_probe(args, cfg)
     sh = draw_decode_shapes(cfg)
     vals = draw_decode_values(cfg, sh.lens)
     B, Hq, H, d, dt = cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.dtype

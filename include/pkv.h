@@ -847,6 +847,34 @@ pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, float* out, in
                              const pkv_prefill_plan_info* info, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Measurement aid, not part of the decode path: reads every K/V tile that
+ * pkv_paged_decode would read for this plan (the decode gathers tiles
+ * through the block tables: "04 — Hacia PagedAttention", La idea de
+ * PagedAttention, step 5), with the decode's work items, order and wave
+ * layout, and none of its arithmetic; its duration is the gather ceiling a
+ * decode launch is compared with.  mode: PKV_PROBE_REGS (tiles into two
+ * alternating register sets, nontemporal loads, as the VALU decode),
+ * PKV_PROBE_CACHED (the same with cached loads) or PKV_PROBE_LDS (tiles
+ * loaded straight into a per-wave two-stage LDS ring, then read back; tiles
+ * of at most 4 KiB).  waves: 1, 2 or 4 per workgroup.  lds_pad: unused
+ * dynamic LDS bytes per workgroup (0 to 65536), which caps how many
+ * workgroups a compute unit holds at once (occupancy sweeps).  plan / info: a
+ * decode plan of pkv_decode_plan (no shared-block nodes), plan uploaded;
+ * block_tables / context_lens as for decode.  out: device uint32
+ * [info->n_work][num_kv_heads][waves], the XOR of every 32-bit word of the
+ * K and V tiles of blocks b0 + w, b0 + w + waves, ... of the item's
+ * partition [b0, b1) (all 16 rows of each block).  Errors: PKV_E_BAD_ARG,
+ * PKV_E_UNSUPPORTED (block size other than 16, a tile that is not a
+ * multiple of 1 KiB, or LDS mode with a tile over 4 KiB).  Asynchronous on
+ * `stream`; allocates nothing. */
+#define PKV_PROBE_REGS 0
+#define PKV_PROBE_CACHED 1
+#define PKV_PROBE_LDS 2
+pkv_status pkv_gather_probe(const pkv_pool* pool, const int32_t* block_tables, int32_t table_stride,
+                            const int32_t* context_lens, int32_t num_seqs, const int32_t* plan,
+                            const pkv_decode_plan_info* info, int32_t mode, int32_t waves,
+                            int32_t lds_pad, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,7 @@ STATUS_KIND = {E_NO_BLOCKS: "no_blocks", E_BAD_SEQ: "bad_seq", E_BAD_ARG: "bad_a
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 NOALLOC_SCRATCH_BYTES = 32 << 20  # PKV_NOALLOC_SCRATCH_BYTES of include/pkv.h
 MAX_SHARED_RECORDS = 16           # PKV_MAX_SHARED_RECORDS of include/pkv.h
+PROBE_MODES = {"regs": 0, "cached": 1, "lds": 2}  # PKV_PROBE_* of include/pkv.h
 
 
 class PoolDesc(C.Structure):
@@ -193,6 +194,7 @@ SIGNATURES = {
     "pkv_paged_decode_noalloc": [P, P, P, P, P, I32, I32, P, I32, P, C.c_float, P, C.POINTER(PlanInfo), P],
     "pkv_paged_prefill": [P, P, P, I32, I32, P, I32, P, C.c_float, P, C.POINTER(PrefillPlanInfo), P,
                           C.c_size_t, P],
+    "pkv_gather_probe": [P, P, I32, P, I32, P, C.POINTER(PlanInfo), I32, I32, I32, P, P],
     "pkv_last_error": [],
 }
 RESTYPES = {"pkv_last_error": C.c_char_p, "pkv_decode_workspace_bytes": C.c_size_t,
@@ -202,7 +204,7 @@ RESTYPES = {"pkv_last_error": C.c_char_p, "pkv_decode_workspace_bytes": C.c_size
             "pkv_prepare_decode_bytes": C.c_size_t, "pkv_stepper_slot_bytes": C.c_size_t}
 DEVICE_FUNCS = ("pkv_copy_blocks", "pkv_write_kv", "pkv_read_kv", "pkv_paged_decode", "pkv_paged_decode_partitions",
                 "pkv_decode_occupancy",
-                "pkv_paged_decode_reduce", "pkv_paged_decode_noalloc", "pkv_paged_prefill", "pkv_hybrid_copy_states",
+                "pkv_paged_decode_reduce", "pkv_paged_decode_noalloc", "pkv_paged_prefill", "pkv_hybrid_copy_states", "pkv_gather_probe",
                 "pkv_stepper_slot_bytes", "pkv_stepper_create",
                 "pkv_stepper_destroy", "pkv_stepper_step")
 

@@ -30,7 +30,7 @@ ARCH = "gfx950"
 HOST_SOURCES = ["host/pool.cpp", "host/plan.cpp", "host/plan_shared.cpp", "host/prepare.cpp", "host/prefill_plan.cpp",
                 "host/utilisation.cpp", "host/hybrid.cpp", "host/sched.cpp"]
 HIP_SOURCES = ["kernels/kv_write.hip", "kernels/paged_decode.hip", "kernels/paged_prefill.hip",
-               "kernels/stepper.cpp"]
+               "kernels/gather_probe.hip", "kernels/stepper.cpp"]
 
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -25,7 +25,9 @@
 // private to its row group, so no cross-row exchange is needed inside the
 // loop.  Scores are kept in base 2 (q . k * scale * log2 e) so that every
 // exponential is one v_exp_f32.  The next block's K and V are loaded while
-// the current one is processed.  K/V are read once per launch, so the loads
+// the current one is processed: into a second register set, or, for fp16 /
+// bf16 at head_dim 128 with one query head per workgroup, straight into a
+// second LDS stage of the wave (buffer loads with the LDS bit).  K/V are read once per launch, so the loads
 // carry the nontemporal hint: on MI355X that lifts a random 4 KiB-tile gather
 // from ~5.0 TB/s to ~6.4 TB/s.  At the end the row groups and waves of the
 // workgroup merge their (m, l, o) through LDS; a single-partition sequence
@@ -54,6 +56,8 @@
 #include <cmath>
 #include <cstdlib>
 #include <mutex>
+#include <string>
+#include <type_traits>
 
 #include "decode_launch.h"
 #include "device_common.h"
@@ -259,8 +263,10 @@ __device__ __forceinline__ u32x4 load_tile(__amdgpu_buffer_rsrc_t r, int offset)
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, CP));
 }
 
-template <int DT, int D, int GW, int NW, int CP = kCacheStream>
-__global__ __launch_bounds__(kWave* NW, (decode_waves_hint<DT, D, GW>())) void paged_decode_kernel(
+// LDS: stage K/V tiles through LDS instead of registers (see the main loop
+// and lds_staging).
+template <int DT, int D, int GW, int NW, int CP = kCacheStream, bool LDS = false>
+__global__ __launch_bounds__(kWave* NW, (LDS ? 2 : decode_waves_hint<DT, D, GW>())) void paged_decode_kernel(
     const DecodeParams p) {
   constexpr int E = ElemBytes<DT>::value;
   constexpr int R = D * E;         // bytes per token row of one head
@@ -274,6 +280,13 @@ __global__ __launch_bounds__(kWave* NW, (decode_waves_hint<DT, D, GW>())) void p
   __shared__ float sm_m[NW * RPI * GW];
   __shared__ float sm_l[NW * RPI * GW];
   __shared__ float sm_o[NW * RPI * GW * D];
+  // LDS staging ring: two stages (K and V of one block each) per wave, as
+  // two distinct arrays, so that the wait before reading one stage leaves
+  // the loads into the other in flight
+  constexpr int SW = LDS ? NW : 1;
+  constexpr int SB = LDS ? 2 * TILE : 16;
+  __shared__ __attribute__((aligned(16))) char st_a[SW][SB];
+  __shared__ __attribute__((aligned(16))) char st_b[SW][SB];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -439,21 +452,75 @@ __global__ __launch_bounds__(kWave* NW, (decode_waves_hint<DT, D, GW>())) void p
   // operations in the inner loop are the K/V loads.  Two register buffers
   // alternate: the next block loads while the current one computes.
   u32x4 ka[NI], va[NI], kb[NI], vb[NI];
-  for (cb = b0; cb < b1; cb += kWave) {
-    ce = min(cb + kWave, b1);
-    tbl = (cb + lane < ce) ? trow[cb + lane] : -1;
-    int j = cb + wave;
-    if (j >= ce) break;  // uniform: no block of this chunk (nor later ones) for this wave
-    int blk_a = issue(j, ka, va), blk_b;
-    while (true) {
-      blk_b = issue(j + NW, kb, vb);
-      consume(ka, va, j, blk_a);
-      j += NW;
+  if constexpr (!LDS) {
+    for (cb = b0; cb < b1; cb += kWave) {
+      ce = min(cb + kWave, b1);
+      tbl = (cb + lane < ce) ? trow[cb + lane] : -1;
+      int j = cb + wave;
+      if (j >= ce) break;  // uniform: no block of this chunk (nor later ones) for this wave
+      int blk_a = issue(j, ka, va), blk_b;
+      while (true) {
+        blk_b = issue(j + NW, kb, vb);
+        consume(ka, va, j, blk_a);
+        j += NW;
+        if (j >= ce) break;
+        blk_a = issue(j + NW, ka, va);
+        consume(kb, vb, j, blk_b);
+        j += NW;
+        if (j >= ce) break;
+      }
+    }
+  } else {
+    // The same walk with the tiles loaded straight into the wave's LDS ring
+    // (buffer loads with the LDS bit: lane l's 16 bytes of load i land at
+    // byte 1024 i + 16 l of the stage, the tile's own layout), then read
+    // back into the same register layout and processed as above.  No
+    // registers hold loads in flight, but a stage costs 8 KiB of LDS per
+    // wave: 72 KiB per workgroup of four waves, two workgroups per CU.
+    auto stage_in = [&](auto stage, int j) __attribute__((always_inline)) -> int {
+      const int blk = __builtin_amdgcn_readlane(tbl, min(j - cb, kWave - 1));
+      const bool ok = j < ce && unsigned(blk) < unsigned(p.num_blocks);
+      const int64_t tile = int64_t(ok ? blk : 0) * blk_stride + int64_t(kvh) * TILE;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_cache + tile, ok ? TILE : 0);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_cache + tile, ok ? TILE : 0);
+      char* base = decltype(stage)::value == 0 ? &st_a[wave][0] : &st_b[wave][0];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(base + i * 1024),
+                                                 16, lane * 16 + i * 1024, 0, 0, CP);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(base + TILE + i * 1024), 16, lane * 16 + i * 1024, 0, 0, CP);
+      return j < ce ? blk : -1;
+    };
+    auto stage_out = [&](auto stage, u32x4* kk, u32x4* vv) __attribute__((always_inline)) {
+      const char* base = decltype(stage)::value == 0 ? &st_a[wave][0] : &st_b[wave][0];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) kk[i] = *reinterpret_cast<const u32x4*>(base + i * 1024 + lane * 16);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) vv[i] = *reinterpret_cast<const u32x4*>(base + TILE + i * 1024 + lane * 16);
+    };
+    using StA = std::integral_constant<int, 0>;
+    using StB = std::integral_constant<int, 1>;
+    for (cb = b0; cb < b1; cb += kWave) {
+      ce = min(cb + kWave, b1);
+      tbl = (cb + lane < ce) ? trow[cb + lane] : -1;
+      int j = cb + wave;
       if (j >= ce) break;
-      blk_a = issue(j + NW, ka, va);
-      consume(kb, vb, j, blk_b);
-      j += NW;
-      if (j >= ce) break;
+      int blk_a = stage_in(StA{}, j), blk_b;
+      while (true) {
+        blk_b = stage_in(StB{}, j + NW);
+        stage_out(StA{}, ka, va);
+        consume(ka, va, j, blk_a);
+        j += NW;
+        if (j >= ce) break;
+        blk_a = stage_in(StA{}, j + NW);
+        stage_out(StB{}, kb, vb);
+        consume(kb, vb, j, blk_b);
+        j += NW;
+        if (j >= ce) break;
+      }
     }
   }
 
@@ -1282,11 +1349,36 @@ using DecodeFn = void (*)(const DecodeParams);
 // request): the launch's block size must be that instance's.  With `reuse`
 // (a batch that shares blocks) they return the 4-wave instance with cached
 // tile loads whatever the request.
+// PKV_DECODE_LDS_PAD=<bytes> adds that much unused dynamic LDS to every
+// workgroup of the decode launch, capping how many workgroups a CU holds:
+// a tuning variable for occupancy sweeps, read at every launch (0 to 64 KiB;
+// pkv_decode_occupancy does not see it).
+size_t lds_pad_bytes() {
+  const char* s = std::getenv("PKV_DECODE_LDS_PAD");
+  const long v = s ? std::atol(s) : 0;
+  return v > 0 && v <= 65536 ? size_t(v) : 0;
+}
+
+// The VALU kernel of fp16 / bf16, head_dim 128, one query head per
+// workgroup and four waves stages its tiles through LDS: on MI355X that
+// instance decodes the GPT-style fp16 batch (64 sequences, 32 heads) in
+// 72.4 us against 74.4 us for register staging at the same two or three
+// workgroups per CU, and the long bf16 batch in the same time.
+// PKV_DECODE_STAGING=regs selects the register-staged instance instead, for
+// comparisons; read at every launch.
+bool lds_staging() {
+  const char* s = std::getenv("PKV_DECODE_STAGING");
+  return !(s && std::string(s) == "regs");
+}
+
 template <int DT, int D, int GW>
 DecodeFn pick_waves(int& nw, bool reuse) {
   if (reuse) {
     nw = 4;
     return paged_decode_kernel<DT, D, GW, 4, kCacheReuse>;
+  }
+  if constexpr (GW == 1 && D == 128 && DT != PKV_F32) {
+    if (nw == 4 && lds_staging()) return paged_decode_kernel<DT, D, GW, 4, kCacheStream, true>;
   }
   switch (nw) {
     case 1: return paged_decode_kernel<DT, D, GW, 1>;
@@ -1582,10 +1674,11 @@ pkv_status launch_partitions(const pkv_pool* pool, const DecodeParams& prm, int 
                      : pick_decode(pool->desc.dtype, pool->desc.head_dim, gw, nw, reuse);
   if (!fn) return fail(PKV_E_UNSUPPORTED, "no kernel for this dtype / head_dim / group");
   const int64_t grid = int64_t(info->n_work) * prm.num_kv_heads * prm.hgroups_per_kv;
+  const size_t pad = lds_pad_bytes();
   if (ev_start || ev_stop)  // one start / stop pair spans both launches of a shared-block plan
-    hipExtLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kWave * nw), 0, s, ev_start, ev_stop, 0, prm);
+    hipExtLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kWave * nw), pad, s, ev_start, ev_stop, 0, prm);
   else
-    hipLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kWave * nw), 0, s, prm);
+    hipLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kWave * nw), pad, s, prm);
   return launch_status("paged_decode launch");
 }
 

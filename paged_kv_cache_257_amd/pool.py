@@ -12,7 +12,7 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 from . import _capi
-from ._capi import PlanInfo, PoolDesc, PrefillPlanInfo, Stats, check, i32p, i64p
+from ._capi import PROBE_MODES, PlanInfo, PoolDesc, PrefillPlanInfo, Stats, check, i32p, i64p
 
 
 def _stream_ptr(stream) -> Optional[int]:
@@ -220,6 +220,16 @@ class Pool:
             _dptr(block_tables), int(block_tables.shape[1]), _dptr(context_lens), float(scale),
             _dptr(plan), C.byref(info), _stream_ptr(stream)))
 
+
+    def gather_probe(self, block_tables, context_lens, plan, info: PlanInfo, out, mode: str = "regs",
+                     waves: int = 4, lds_pad: int = 0, stream=None) -> None:
+        """Read every K/V tile a decode of this plan reads, without its
+        arithmetic (a measurement aid; see pkv_gather_probe).  ``out``: device
+        uint32 tensor of at least n_work x num_kv_heads x waves entries."""
+        check(self.lib, self.lib.pkv_gather_probe(
+            self.handle, _dptr(block_tables), int(block_tables.shape[1]), _dptr(context_lens),
+            int(info.num_seqs), _dptr(plan), C.byref(info), PROBE_MODES[mode], int(waves), int(lds_pad), _dptr(out),
+            _stream_ptr(stream)))
 
     def paged_prefill(self, q, out, block_tables, context_lens, scale: float, plan,
                       info: PrefillPlanInfo, workspace=None, stream=None) -> None:

@@ -97,3 +97,10 @@ def test_noalloc_scratch_size_matches_the_header():
     m = re.search(r"#define PKV_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m, "PKV_NOALLOC_SCRATCH_BYTES not found"
     assert int(m.group(1)) << int(m.group(2)) == _capi.NOALLOC_SCRATCH_BYTES
+
+
+def test_probe_modes_match_the_header():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    for name, val in _capi.PROBE_MODES.items():
+        m = re.search(rf"#define PKV_PROBE_{name.upper()} (\d+)", text)
+        assert m and int(m.group(1)) == val, name

@@ -325,3 +325,37 @@ def test_cached_tile_loads(dtype, group, monkeypatch):
                 assert np.array_equal(outs[0], outs[1]), (mfma, P, split)
     finally:
         case.close()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_lds_staged_variant(dtype, monkeypatch):
+    """The LDS-staged instance of the VALU kernel (the default at 4 waves for
+    fp16 / bf16, head_dim 128: tiles loaded straight into a per-wave LDS
+    ring, read back into the same registers) gives bit for bit the output of
+    the register-staged one (PKV_DECODE_STAGING=regs), within the oracle's
+    tolerance, split and unsplit, with the fused append, over a NaN-filled
+    pool and tables longer than one 64-entry chunk."""
+    idx = 700 + {"f16": 1, "bf16": 2}[dtype]
+    cfg = dataclasses.replace(config_by_name("tiny_f32"), name="lds_staged", index=idx, dtype=dtype,
+                              head_dim=128, num_kv_heads=2, num_q_heads=2, num_seqs=8)
+    lens = [1, 16, 17, 40, 129, 300, 1100, 2100]
+    nb = sum(-(-L // 16) for L in lens) + 3
+    case = DecodeCase(cfg, lens=lens, num_blocks=nb, free_order=np.random.default_rng(idx).permutation(nb),
+                      fill=float("nan"))
+    try:
+        case.write_context(skip_last=True)
+        monkeypatch.setenv("PKV_DECODE_WAVES", "4")
+        for P, split in ((64, False), (64, True), (1024, True), (0, False)):
+            outs = []
+            for staging in ("regs", "lds"):
+                monkeypatch.setenv("PKV_DECODE_STAGING", staging)
+                out, _ = case.decode(P, split=split, append=True)
+                err = max_err(case, out, range(len(lens)))
+                print(f"[gpu] staging={staging} {dtype} P={P} split={split} max_err={err:.3e}", flush=True)
+                assert np.isfinite(out).all(), (staging, P, split)
+                assert err <= TOL[dtype], (staging, P, split, err)
+                assert case.last_tickets_zero
+                outs.append(out)
+            assert np.array_equal(outs[0], outs[1]), (P, split)
+    finally:
+        case.close()
