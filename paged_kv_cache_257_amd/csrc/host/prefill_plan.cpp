@@ -8,6 +8,7 @@
 // in-order workgroup dispatcher fills the tail of the launch with the
 // cheap ones.
 #include <algorithm>
+#include <cstdlib>
 #include <numeric>
 #include <vector>
 
@@ -39,7 +40,13 @@ namespace {
 constexpr int32_t kStageTokens = 32;  // keys per kernel stage
 // max_keys < 0: split only launches that would leave the GPU under-filled
 // (fewer than this many workgroups), into about this many.
+// PKV_PREFILL_SPLIT_WGS overrides it for tuning sweeps (read per plan).
 constexpr int64_t kAutoSplitWorkgroups = 512;
+int64_t auto_split_workgroups() {
+  const char* s = std::getenv("PKV_PREFILL_SPLIT_WGS");
+  const long v = s ? std::atol(s) : 0;
+  return v >= 64 && v <= 65536 ? v : kAutoSplitWorkgroups;
+}
 constexpr int32_t kAutoSplitMinKeys = 1024;
 
 // Query-head groups per KV head times KV heads: workgroups per tile.
@@ -59,8 +66,9 @@ int32_t auto_max_keys(const int32_t* q_lens, const int32_t* context_lens, int32_
       keys += int64_t(C) + std::min(t0 + tile, q_lens[i]);
     }
   }
-  if (tiles * per_tile >= kAutoSplitWorkgroups || tiles == 0) return 0;
-  const int64_t items = (kAutoSplitWorkgroups + per_tile - 1) / per_tile;
+  const int64_t target = auto_split_workgroups();
+  if (tiles * per_tile >= target || tiles == 0) return 0;
+  const int64_t items = (target + per_tile - 1) / per_tile;
   const int64_t per_item = (keys + items - 1) / items;
   return int32_t(std::max<int64_t>(kAutoSplitMinKeys, (per_item + kStageTokens - 1) / kStageTokens * kStageTokens));
 }
