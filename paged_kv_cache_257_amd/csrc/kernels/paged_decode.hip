@@ -27,9 +27,10 @@
 // exponential is one v_exp_f32.  The next block's K and V are loaded while
 // the current one is processed: into a second register set, or, for fp16 /
 // bf16 at head_dim 128 with one query head per workgroup, straight into a
-// second LDS stage of the wave (buffer loads with the LDS bit).  K/V are read once per launch, so the loads
-// carry the nontemporal hint: on MI355X that lifts a random 4 KiB-tile gather
-// from ~5.0 TB/s to ~6.4 TB/s.  At the end the row groups and waves of the
+// second LDS stage of the wave (buffer loads with the LDS bit).  K/V are
+// read once per launch, so the loads carry the nontemporal hint: on MI355X
+// that lifts the gather of the decode's 4 KiB tiles from 5.3-5.7 TB/s to
+// 6.1-6.6 TB/s (pkv_gather_probe).  At the end the row groups and waves of the
 // workgroup merge their (m, l, o) through LDS; a single-partition sequence
 // writes o / l, otherwise (m, l, o) go to the workspace and the partitions
 // are merged:  M = max m_p,
@@ -552,13 +553,14 @@ __global__ __launch_bounds__(kWave* NW, (LDS ? 2 : decode_waves_hint<DT, D, GW>(
 // on the matrix cores, and every lane then holds a real head).
 //
 // Lane (g, n) = lane (16 g + n).  Per block and wave:
-//  * K tile: load i (i = 0..3) gives lane (g, n) dims 8 n .. 8 n + 7 of
-//    token 4 i + g (1 KiB contiguous per load).  The wave writes it to its
-//    own LDS rows and reads back, for k-step kc, dims 32 kc + 8 g .. + 7 of
-//    token n: the A operand of v_mfma_f32_16x16x32 (row n, k-slice 8 g).
-//    (Loading that layout straight from HBM takes 16 rows x 64 bytes per
-//    load, measured 3.6% slower.)  Q^T is the B operand (column n, the same
-//    dims), loaded once.
+//  * K tile: four loads of 1 KiB (tokens 4 i .. 4 i + 3) straight into the
+//    wave's LDS stage (buffer loads with the LDS bit), each token row's
+//    16-byte chunks permuted (chunk c of token t at position c ^ t); the wave
+//    reads back, for k-step kc, dims 32 kc + 8 g .. + 7 of token n: the A
+//    operand of v_mfma_f32_16x16x32 (row n, k-slice 8 g).  (Loading that
+//    layout straight from HBM into registers takes 16 rows x 64 bytes per
+//    load, measured 3.6% slower than staging.)  Q^T is the B operand
+//    (column n, the same dims), loaded once.
 //  * The accumulator leaves lane (g, n) with the scores of tokens
 //    4 g .. 4 g + 3 for column n: the B-operand layout of the 16x16x16
 //    product that follows, so the weights never move between lanes.  The
@@ -602,8 +604,15 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
   __shared__ float sm_m[NW * GW];
   __shared__ float sm_l[NW * GW];
   __shared__ __attribute__((aligned(16))) float sm_o[NW * GW * D];
-  constexpr int KROWB = R + 16;  // K row stride in LDS (bytes), padded against bank conflicts
-  __shared__ __attribute__((aligned(16))) char sm_k[NW * kBlockTokens * KROWB];
+  // K tiles go straight from HBM into LDS (buffer loads with the LDS bit),
+  // into a ring of two stages per wave held in two distinct arrays, so that
+  // the compiler's wait before reading one stage leaves the other's loads in
+  // flight.  A load writes lane l's 16 bytes at byte 16 l of its 1 KiB; the
+  // lane loads the chunk that belongs there: token t's 16-byte chunk c sits
+  // at position c ^ (t mod 16) of row t, so that the operand reads below
+  // (16 lanes: 16 tokens, one chunk each) hit distinct banks.
+  __shared__ __attribute__((aligned(16))) char sk_a[NW][TILE];
+  __shared__ __attribute__((aligned(16))) char sk_b[NW][TILE];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -625,7 +634,6 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
   const int b1 = min(b0 + p.partition_blocks, nblk);
   const bool writes_new = (hg - kvh * p.hgroups_per_kv) == 0;
   const float c2 = p.scale_log2;
-  char* const klds = sm_k + wave * kBlockTokens * KROWB;
 
   // Q^T (B operand): column n = head qh0 + n mod GW, dims 32 kc + 8 g .. + 7
   u32x4 qb[4];
@@ -648,33 +656,43 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
   // the resources cover the rows that hold tokens, none past the chunk's
   // end or for a table entry outside the pool.  Returns the block id.
   int cb = 0, ce = 0, tbl = -1;
-  const int koff = 16 * lane;          // + 1024 i: token 4 i + g, dims 8 n .. 8 n + 7
+  int koff[4];  // load i: token 4 i + g, the chunk stored at position n
+#pragma unroll
+  for (int i = 0; i < 4; ++i) koff[i] = (4 * i + g) * R + 16 * (n ^ (4 * i + g));
   const int voff = 4 * g * R + 16 * n;  // + t R
-  auto issue = [&](int j, u32x4* kk, u32x4* vv) __attribute__((always_inline)) -> int {
+  auto kstage = [&](auto sc) __attribute__((always_inline)) -> char* {
+    return decltype(sc)::value == 0 ? &sk_a[wave][0] : &sk_b[wave][0];
+  };
+  auto issue = [&](auto sc, int j, u32x4* vv) __attribute__((always_inline)) -> int {
     const int blk = __builtin_amdgcn_readlane(tbl, min(j - cb, kWave - 1));
     const bool ok = j < ce && unsigned(blk) < unsigned(p.num_blocks);
     const int rows = ok ? min(kBlockTokens, L - j * kBlockTokens) : 0;
     const int64_t tile = int64_t(ok ? blk : 0) * blk_stride + int64_t(kvh) * TILE;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k_cache + tile, rows * R);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v_cache + tile, rows * R);
+    char* dst = kstage(sc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kk[i] = load_tile_s<CP>(rk, koff, 1024 * i);
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16,
+                                               koff[i], 0, 0, CP);
 #pragma unroll
     for (int t = 0; t < 4; ++t) vv[t] = load_tile_s<CP>(rv, voff, t * R);
     return j < ce ? blk : -1;
   };
 
   // One block: `valid` rows hold tokens (16 except in the last block).
-  auto process = [&](const u32x4* kk, const u32x4* vv, int valid) __attribute__((always_inline)) {
-    // K: written to this wave's LDS rows as loaded (load i: row 4 i + g,
-    // chunk n), read back as the A operand (row n, dims 32 kc + 8 g); the
-    // same wave writes and reads, and its LDS accesses complete in order
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(klds + (4 * i + g) * KROWB + 16 * n) = kk[i];
+  // K comes from the wave's LDS stage as the A operand (row n, dims
+  // 32 kc + 8 g); with `knew`, lanes of row r_new take it from kn instead
+  // (the newest token, not read from the pool).
+  auto process = [&](const char* klds, const u32x4* vv, int valid, bool knew, int r_new,
+                     const u32x4* kn) __attribute__((always_inline)) {
     f4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-      sacc = mfma_k32<DT>(*reinterpret_cast<const u32x4*>(klds + n * KROWB + 64 * kc + 16 * g), qb[kc], sacc);
+    for (int kc = 0; kc < 4; ++kc) {
+      u32x4 a = *reinterpret_cast<const u32x4*>(klds + n * R + 16 * ((4 * kc + g) ^ n));
+      if (knew) a = n == r_new ? kn[kc] : a;
+      sacc = mfma_k32<DT>(a, qb[kc], sacc);
+    }
     float s[4] = {sacc[0], sacc[1], sacc[2], sacc[3]};
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -724,20 +742,23 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
   // One block.  Rows past the sequence length (in its last block) or in a
   // table entry outside the pool are masked; every block takes the same
   // masked step (a few compares), which keeps one copy of the step per
-  // register buffer.  With k_new given, the newest row (position L - 1)
-  // replaces row r_new of the tile: K in lane group r_new mod 4 of load
-  // r_new / 4, V in lane group r_new / 4 of load r_new mod 4; the first head
-  // group stores it.
-  auto consume = [&](u32x4* kk, u32x4* vv, int j, int blk) __attribute__((always_inline)) {
+  // stage.  With k_new given, the newest row (position L - 1) replaces row
+  // r_new of the tile: K as the A operand of the lanes of row r_new (dims
+  // 32 kc + 8 g, loaded here), V in lane group r_new / 4 of load r_new mod
+  // 4; the first head group stores it.
+  auto consume = [&](auto sc, u32x4* vv, int j, int blk) __attribute__((always_inline)) {
     const bool in_pool = unsigned(blk) < unsigned(p.num_blocks);
     const int valid = in_pool ? min(kBlockTokens, L - j * kBlockTokens) : 0;
     const int r_new = L - 1 - j * kBlockTokens;
     if (p.k_new != nullptr && in_pool && r_new < kBlockTokens) {
+      // (a path of its own: the other blocks' operand reads then share no
+      // registers with these loads, and never wait for them)
       const int64_t src = (int64_t(seq) * p.num_kv_heads + kvh) * R;
       const u32x4 nv = *reinterpret_cast<const u32x4*>(p.v_new + src + 16 * n);
       const u32x4 nk = *reinterpret_cast<const u32x4*>(p.k_new + src + 16 * n);
+      u32x4 kn[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kk[i] = (g == (r_new & 3) && i == (r_new >> 2)) ? nk : kk[i];
+      for (int kc = 0; kc < 4; ++kc) kn[kc] = *reinterpret_cast<const u32x4*>(p.k_new + src + 16 * (4 * kc + g));
 #pragma unroll
       for (int t = 0; t < 4; ++t) vv[t] = (g == (r_new >> 2) && t == (r_new & 3)) ? nv : vv[t];
       if (writes_new && g == 0) {
@@ -745,27 +766,31 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
         *reinterpret_cast<u32x4*>(p.k_cache + dst) = nk;
         *reinterpret_cast<u32x4*>(p.v_cache + dst) = nv;
       }
+      process(kstage(sc), vv, valid, true, r_new, kn);
+    } else {
+      process(kstage(sc), vv, valid, false, -1, nullptr);
     }
-    process(kk, vv, valid);
   };
 
   // Wave `wave` takes blocks b0 + wave, b0 + wave + NW, ... (table entries in
   // chunks of 64, one per lane; two register buffers alternate, as in the
   // VALU kernel).
-  u32x4 ka[4], va[4], kb[4], vb[4];
+  using StA = std::integral_constant<int, 0>;
+  using StB = std::integral_constant<int, 1>;
+  u32x4 va[4], vb[4];
   for (cb = b0; cb < b1; cb += kWave) {
     ce = min(cb + kWave, b1);
     tbl = (cb + lane < ce) ? trow[cb + lane] : -1;
     int j = cb + wave;
     if (j >= ce) break;
-    int blk_a = issue(j, ka, va), blk_b;
+    int blk_a = issue(StA{}, j, va), blk_b;
     while (true) {
-      blk_b = issue(j + NW, kb, vb);
-      consume(ka, va, j, blk_a);
+      blk_b = issue(StB{}, j + NW, vb);
+      consume(StA{}, va, j, blk_a);
       j += NW;
       if (j >= ce) break;
-      blk_a = issue(j + NW, ka, va);
-      consume(kb, vb, j, blk_b);
+      blk_a = issue(StA{}, j + NW, va);
+      consume(StB{}, vb, j, blk_b);
       j += NW;
       if (j >= ce) break;
     }
