@@ -481,6 +481,10 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
     sm_last = (__hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == parts - 1);
   __syncthreads();
   if (!sm_last) return;
+  // every part's records were performed (agent-scope stores, waited for)
+  // before its ticket was taken: order this workgroup's reads of them
+  // after the ticket that counted the last part
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #pragma unroll
   for (int j = 0; j < RG; ++j) {
     float M = kNegBig;
