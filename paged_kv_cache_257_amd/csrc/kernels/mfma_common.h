@@ -50,14 +50,18 @@ __device__ __forceinline__ f4 mfma_k16(const u32x2& a, const u32x2& b, const f4&
 // Maximum over the four lanes n, n + 16, n + 32, n + 48 (one accumulator
 // column), with gfx950's lane swaps instead of LDS permutes: a swap of a
 // register with itself leaves, in the two results, each lane's own value and
-// its partner's (16 lanes away for permlane16, 32 for permlane32).
+// its partner's (16 lanes away for permlane16, 32 for permlane32).  The two
+// results are copied into scalars before they are reinterpreted as floats:
+// this compiler lowers a bit_cast of an element of the returned vector as a
+// read of element 0, so the second result would silently become the first
+// and the maximum would cover only lanes 0-15 (see device_common.h).
 __device__ __forceinline__ float max_over_lane_groups(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
-                                                  __builtin_bit_cast(uint32_t, x), false, false);
-  x = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                                  __builtin_bit_cast(uint32_t, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const uint32_t a0 = a[0], a1 = a[1];
+  x = fmaxf(__uint_as_float(a0), __uint_as_float(a1));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const uint32_t b0 = b[0], b1 = b[1];
+  return fmaxf(__uint_as_float(b0), __uint_as_float(b1));
 }
 
 }  // namespace pkv

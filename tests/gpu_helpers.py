@@ -144,3 +144,29 @@ class DecodeCase:
         self.pool.close()
         del self.k_cache, self.v_cache
         torch.cuda.empty_cache()
+
+
+# Block row of the dominant keys of peaked_qk: tokens 4..7 of a block are the
+# second group of four in the matrix-core kernels' score layout (lanes
+# 16..31), so a running maximum that missed them would show.
+PEAK_ROW = 5
+
+
+def peaked_qk(q_bits, k_bits, k_pos, dtype, seed, score=30.0):
+    """Queries and keys whose softmax is dominated by the keys at block row
+    PEAK_ROW: every query becomes one unit-variance vector g and those keys
+    score * sqrt(d) * g / |g|^2, so with the scale 1/sqrt(d) their scores are
+    about `score` (about 43 in base 2) above the others' unit-variance ones.
+    A weight taken against anything but the row's own maximum then exceeds
+    what fp16 holds.  q_bits [..][d]; k_bits [T][H][d]; k_pos [T] positions."""
+    from oracle.attention import storage_to_f64
+    from workloads import storage_from_f32
+    d = q_bits.shape[-1]
+    rng = np.random.default_rng(seed)
+    g = storage_to_f64(storage_from_f32(rng.standard_normal(d).astype(np.float32), dtype), dtype)
+    q = np.broadcast_to(g, q_bits.shape).astype(np.float32)
+    k = storage_to_f64(k_bits, dtype).astype(np.float32)
+    peak = (score * np.sqrt(d) * g / float(g @ g)).astype(np.float32)
+    rows = np.asarray(k_pos) % 16 == PEAK_ROW
+    k[rows] = peak
+    return storage_from_f32(q, dtype), storage_from_f32(k, dtype)

@@ -21,8 +21,9 @@ import pytest
 import torch
 
 from paged_kv_cache_257_amd import default_partition_tokens, fill_partition
-from tests.gpu_helpers import TOL, DecodeCase, device_bits, host_bits, sync, to_device
-from workloads import CONFIGS, config_by_name, draw_normal_storage
+from tests.gpu_helpers import TOL, DecodeCase, device_bits, host_bits, peaked_qk, sync, to_device
+from workloads import CONFIGS, config_by_name, draw_decode_values, draw_normal_storage
+from workloads.configs import DecodeConfig
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -359,3 +360,30 @@ def test_lds_staged_variant(dtype, monkeypatch):
             assert np.array_equal(outs[0], outs[1]), (P, split)
     finally:
         case.close()
+
+
+@pytest.mark.parametrize("dtype,hq,hkv", [("f16", 8, 2), ("f16", 4, 4), ("bf16", 8, 2)])
+def test_dominant_keys_outside_first_lane_group(dtype, hq, hkv):
+    """Decode rows dominated, by about 43 in base 2, by the keys at block
+    row 5 (lanes 16..31 of the matrix-core score layout): the running
+    maximum must cover every lane group or the fp16 weights overflow.  Every
+    output, unsplit and split."""
+    lens = (6, 21, 37, 100, 333, 517, 1000)
+    cfg = DecodeConfig(name=f"peak_{dtype}_{hq}_{hkv}", index=40, dtype=dtype, num_seqs=len(lens),
+                       num_q_heads=hq, num_kv_heads=hkv, head_dim=128, length_rule="fixed", fixed_lengths=lens)
+    vals = draw_decode_values(cfg, lens)
+    pos = np.concatenate([np.arange(L) for L in lens])
+    vals["q"], vals["k"] = peaked_qk(vals["q"], vals["k"], pos, dtype, seed=3)
+    case = DecodeCase(cfg, values=vals)
+    try:
+        case.write_context()
+        ref = case.oracle_all()
+        for P, split in [(0, False), (64, True), (512, False)]:
+            out, _ = case.decode(P, split=split)
+            err = float(np.max(np.abs(out - ref)))
+            print(f"\n[gpu] peaked decode {dtype} {hq}/{hkv} P={P} split={split}: max err {err:.2e}", flush=True)
+            assert np.isfinite(out).all() and err <= TOL[dtype], err
+            assert case.last_tickets_zero
+    finally:
+        case.pool.close()
+

@@ -22,7 +22,7 @@ import torch
 
 from oracle.runs import PrefillRun
 from paged_kv_cache_257_amd import PkvError, Pool, prefill_plan, prefill_workspace_bytes
-from tests.gpu_helpers import TOL, TORCH_DTYPE, sync, to_device
+from tests.gpu_helpers import TOL, TORCH_DTYPE, peaked_qk, sync, to_device
 from workloads.prefill import (PrefillConfig, draw_prefill_shapes, draw_prefill_values,
                                prefill_config_by_name, prompt_offsets)
 
@@ -89,8 +89,8 @@ class PrefillCase:
         self.pool.close()
 
 
-def run_full(cfg, fill=0.0, max_keys=0):
-    case = PrefillCase(cfg, fill=fill, max_keys=max_keys)
+def run_full(cfg, fill=0.0, max_keys=0, values=None):
+    case = PrefillCase(cfg, fill=fill, max_keys=max_keys, values=values)
     try:
         worst, splits = 0.0, 0
         for k in range(len(case.sh.steps)):
@@ -205,3 +205,23 @@ def test_unsupported_dtype_is_refused():
         assert e.value.kind == "unsupported"
     finally:
         pool.close()
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,max_keys", [("f16", 4, 4, 0), ("f16", 8, 2, 0), ("f16", 4, 4, 64),
+                                                    ("bf16", 8, 2, 0)])
+def test_dominant_keys_outside_first_lane_group(dtype, hq, hkv, max_keys):
+    """Rows whose softmax is dominated, by about 43 in base 2, by the keys at
+    block row 5 (the second group of four tokens of the score layout, held
+    by lanes 16..31): the running maximum must be each row's own over all
+    four lane groups, or the fp16 weights overflow.  Guards the lane-group
+    maximum against the compiler's lowering of a bit_cast of a vector
+    element as element 0 (which left it over lanes 0..15).  Every output."""
+    cfg = PrefillConfig(name=f"pf_peak_{dtype}_{hq}_{hkv}", index=31, dtype=dtype, num_q_heads=hq,
+                        num_kv_heads=hkv, head_dim=128, chunk_tokens=64, fixed_prompts=(150, 37))
+    sh = draw_prefill_shapes(cfg)
+    q, k, v = draw_prefill_values(cfg, sh.prompts)
+    pos = np.concatenate([np.arange(int(p)) for p in sh.prompts])
+    q, k = peaked_qk(q, k, pos, dtype, seed=5)
+    worst = run_full(cfg, max_keys=max_keys, values=(q, k, v))
+    print(f"\n[gpu] peaked prefill {dtype} {hq}/{hkv} max_keys={max_keys}: max err {worst:.2e}")
+

@@ -18,7 +18,7 @@ import torch
 from oracle.allocator import OracleAllocator
 from oracle.attention import decode_attention, storage_to_f64
 from paged_kv_cache_257_amd import Pool, decode_plan_shared, decode_workspace_bytes
-from tests.gpu_helpers import TOL, TORCH_DTYPE, oracle_map, sync, to_device
+from tests.gpu_helpers import TOL, TORCH_DTYPE, oracle_map, peaked_qk, sync, to_device
 from workloads import draw_normal_storage
 
 pytestmark = [pytest.mark.gpu,
@@ -33,7 +33,7 @@ class ForkedCase:
     appended to each; built identically on both allocators."""
 
     def __init__(self, seed, dtype="f16", kv_heads=4, group=1, prefix=1000, n_forks=48, tail_max=300,
-                 lineages=16, nan_fill=True):
+                 lineages=16, nan_fill=True, peaked=False):
         rng = np.random.default_rng(seed)
         self.dtype, self.H, self.group, self.d = dtype, kv_heads, group, 128
         self.Hq = kv_heads * group
@@ -65,6 +65,11 @@ class ForkedCase:
         shape = (nb, kv_heads, BS, 128)
         kb = draw_normal_storage((seed, 1), shape, dtype)
         vb = draw_normal_storage((seed, 2), shape, dtype)
+        q = draw_normal_storage((seed, 3), (len(seqs), self.Hq, 128), dtype)
+        if peaked:  # every block's row 5 dominates (see peaked_qk)
+            rows = np.ascontiguousarray(kb.transpose(0, 2, 1, 3)).reshape(nb * BS, kv_heads, 128)
+            q, rows = peaked_qk(q, rows, np.tile(np.arange(BS), nb), dtype, seed)
+            kb = np.ascontiguousarray(rows.reshape(nb, BS, kv_heads, 128).transpose(0, 2, 1, 3))
         if nan_fill:
             nan_bits = {"f16": np.float16(np.nan).view(np.uint16), "bf16": np.uint16(0x7FC0)}[dtype]
             for s in seqs:
@@ -75,7 +80,7 @@ class ForkedCase:
         self.kb, self.vb = kb, vb
         self.k_cache.copy_(to_device(kb, dtype))
         self.v_cache.copy_(to_device(vb, dtype))
-        self.q = draw_normal_storage((seed, 3), (len(seqs), self.Hq, 128), dtype)
+        self.q = q
         tables, lens = self.pool.build_batch(seqs, width)
         t_o, l_o = self.ora.build_batch(seqs, width)
         assert np.array_equal(tables, np.asarray(t_o, np.int32)) and np.array_equal(lens, np.asarray(l_o))
@@ -148,3 +153,25 @@ def test_shared_decode_matches_oracle(dtype, kv_heads, group):
             assert np.isfinite(out).all() and err <= TOL[dtype], err
     finally:
         case.close()
+
+
+@pytest.mark.parametrize("dtype,kv_heads,group", [("f16", 4, 1), ("f16", 2, 4), ("bf16", 2, 4)],
+                         ids=lambda x: str(x))
+def test_shared_decode_dominant_keys_outside_first_lane_group(dtype, kv_heads, group):
+    """Every block's row 5 (lanes 16..31 of the score layout) dominates by
+    about 43 in base 2 (see peaked_qk): the shared, narrow and own-block
+    kernels must each take every row's maximum over all four lane groups, or
+    the fp16 weights overflow.  Every output."""
+    case = ForkedCase(90 + group, dtype, kv_heads, group, peaked=True)
+    try:
+        ref = np.stack(oracle_map(case.oracle_out, range(len(case.seqs))))
+        for P, chunk in [(2048, 0), (256, 64)]:
+            out, info = case.decode(P, chunk)
+            assert info.n_nodes > 0
+            err = float(np.max(np.abs(out - ref)))
+            print(f"\n[gpu] peaked shared {dtype} H={kv_heads} G={group} P={P} chunk={chunk}: max err {err:.3e}",
+                  flush=True)
+            assert np.isfinite(out).all() and err <= TOL[dtype], err
+    finally:
+        case.close()
+
