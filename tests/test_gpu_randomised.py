@@ -5,8 +5,10 @@ oracle within the workload tolerances (2e-3 for fp16/bf16, 1e-5 for fp32).
 Shapes: dtype, head_dim 64/128/256 (prefill 64/128), 1-8 KV heads, query
 groups 1, 2, 3, 4, 6, 8 (prefill also 16), ragged lengths with block-edge
 values, partition sizes from 16 tokens up, split and fused-append decodes,
-prefill chunks of 1-1024 tokens with and without key splits, and pools
-pre-filled with NaN.  One case is pinned: the fp16 grouped-query prefill
+prefill chunks of 1-1024 tokens with and without key splits, pools
+pre-filled with NaN, and fork trees of random shape (prefix length, forks,
+tails, forks of forks) decoded through the shared-block plan at random
+partition and chunk sizes.  One case is pinned: the fp16 grouped-query prefill
 (4 KV heads x group 6, prompts 775/17/212/16 in 100-token chunks) whose
 error a randomised run measured at 2.08e-3 while the matrix-core kernels'
 row maximum covered lanes 0-15 only."""
@@ -17,6 +19,8 @@ import torch
 
 from tests.gpu_helpers import TOL, DecodeCase, sync
 from tests.test_gpu_prefill import PrefillCase
+from tests.test_gpu_shared_decode import ForkedCase
+from tests.gpu_helpers import oracle_map
 from workloads.configs import DecodeConfig
 from workloads.prefill import PrefillConfig
 
@@ -25,6 +29,7 @@ pytestmark = [pytest.mark.gpu,
 
 DECODE_CHUNKS, DECODE_PER_CHUNK = 8, 60
 PREFILL_CHUNKS, PREFILL_PER_CHUNK = 6, 40
+SHARED_CHUNKS, SHARED_PER_CHUNK = 3, 40
 
 
 def rand_lens(rng, n, hi):
@@ -128,3 +133,30 @@ def test_pinned_gqa6_prefill():
     err = run_prefill(cfg, 0.0, 0)
     print(f"\n[gpu] pinned fp16 group-6 prefill: max err {err:.2e}", flush=True)
     assert err <= TOL["f16"], err
+
+
+@pytest.mark.parametrize("chunk", range(SHARED_CHUNKS))
+def test_random_fork_trees(chunk):
+    rng = np.random.default_rng([2028, chunk])
+    for _ in range(SHARED_PER_CHUNK):
+        dt = str(rng.choice(["f16", "bf16"]))
+        hkv, grp = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 3, 4, 6, 8]))
+        prefix, forks = int(rng.integers(1, 2000)), int(rng.integers(1, 60))
+        tail_max, lineages = int(rng.integers(0, 300)), int(rng.integers(0, 16))
+        seed = int(rng.integers(0, 1 << 30))
+        P = int(rng.choice([0, 16, 64, 256, 512, 2048, 16 * int(rng.integers(1, 100))]))
+        chunk_tokens = int(rng.choice([0, 16, 32, 64, 128, 256, 1024]))
+        mode = str(rng.choice(["plain", "split", "append"]))
+        desc = (f"{dt} kv={hkv} grp={grp} prefix={prefix} forks={forks} tail_max={tail_max} "
+                f"lineages={lineages} seed={seed} P={P} chunk={chunk_tokens} {mode}")
+        print(f"[gpu] forks {desc}", flush=True)
+        case = ForkedCase(seed, dt, hkv, grp, prefix=prefix, n_forks=forks, tail_max=tail_max,
+                          lineages=lineages)
+        try:
+            ref = np.stack(oracle_map(case.oracle_out, range(len(case.seqs))))
+            out, _ = case.decode(P, chunk_tokens, **({} if mode == "plain" else {mode: True}))
+            err = float(np.max(np.abs(out - ref))) if np.isfinite(out).all() else float("inf")
+            assert err <= TOL[dt], (desc, err)
+        finally:
+            case.close()
+

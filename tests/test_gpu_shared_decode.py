@@ -39,7 +39,8 @@ class ForkedCase:
         self.Hq = kv_heads * group
         need = -(-prefix // BS) + (n_forks + lineages) * (-(-(tail_max + 64) // BS) + 2)
         nb = int(need * 1.25) + 8
-        width = -(-(prefix + tail_max + 80) // BS)
+        # a lineage may fork a lineage: each link appends up to 40 tokens
+        width = -(-(prefix + tail_max + 41 * (lineages + 1) + 16) // BS)
         order = rng.permutation(nb).astype(np.int32)
         self.k_cache = torch.zeros((nb, kv_heads, BS, 128), dtype=TORCH_DTYPE[dtype], device="cuda")
         self.v_cache = torch.zeros_like(self.k_cache)
