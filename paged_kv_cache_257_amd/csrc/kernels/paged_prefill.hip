@@ -301,41 +301,55 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
     const bool bad[2] = {bad_c[0], bad_c[1]};
     const bool masked = st >= mask_from || bad[0] || bad[1];
     u32x4 pb[RG], pl[RG];
-    float alpha[RG];
-    bool rescale = false;
+    float s[RG][8], mxl[RG];
+    bool moved = false;
 #pragma unroll
     for (int j = 0; j < RG; ++j) {
-      float s[8];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s[blk * 4 + v] = sa[j][blk][v];
+        for (int v = 0; v < 4; ++v) s[j][blk * 4 + v] = sa[j][blk][v];
       if (masked) {  // causal / context / pool mask (wave-uniform branch)
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int kp = st * kStage + blk * 16 + 4 * g + v;
-            if (bad[blk] || kp > qpos[j] || kp >= L) s[blk * 4 + v] = -INFINITY;
+            if (bad[blk] || kp > qpos[j] || kp >= L) s[j][blk * 4 + v] = -INFINITY;
           }
       }
-      float mx = s[0];
+      mxl[j] = s[j][0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-      mx = max_over_lane_groups(mx);
+      for (int i = 1; i < 8; ++i) mxl[j] = fmaxf(mxl[j], s[j][i]);
       // the running maximum moves only when a score exceeds it by more than
-      // kRescaleSlack (weights stay <= 2^kRescaleSlack in between)
-      const float mxs = mx * c2;
-      const float mn = mxs > m[j] + kRescaleSlack ? mxs : m[j];
-      alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
-      rescale |= mn > m[j];
-      m[j] = mn;
+      // kRescaleSlack (weights stay <= 2^kRescaleSlack in between); the
+      // lane's own 8 scores decide whether any of the row's can, so the
+      // row's maximum over its four lanes is formed only in such a stage
+      moved |= mxl[j] * c2 > m[j] + kRescaleSlack;
+    }
+    float alpha[RG] = {};
+#pragma unroll
+    for (int j = 0; j < RG; ++j) alpha[j] = 1.f;
+    bool rescale = false;
+    if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+      for (int j = 0; j < RG; ++j) {
+        const float mxs = max_over_lane_groups(mxl[j]) * c2;
+        const float mn = mxs > m[j] + kRescaleSlack ? mxs : m[j];
+        alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
+        rescale |= mn > m[j];
+        m[j] = mn;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      const float mn = m[j];
       uint32_t ph[4], plo[4];
       float psum = 0.f;
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2) {
-        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q2], c2, -mn));
-        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q2 + 1], c2, -mn));
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][2 * q2], c2, -mn));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][2 * q2 + 1], c2, -mn));
         psum += x0 + x1;
         const f2 xx = {x0, x1};
         if constexpr (DT == PKV_F16) {
