@@ -564,9 +564,10 @@ __global__ __launch_bounds__(kWave* NW, (LDS ? 2 : decode_waves_hint<DT, D, GW>(
 //  * The accumulator leaves lane (g, n) with the scores of tokens
 //    4 g .. 4 g + 3 for column n: the B-operand layout of the 16x16x16
 //    product that follows, so the weights never move between lanes.  The
-//    online softmax keeps one running maximum per column (the four lanes of
-//    a column agree after an exchange through gfx950's lane swaps) and a
-//    per-lane partial sum.
+//    online softmax keeps one running maximum per column and a per-lane
+//    partial sum; the maximum lags the column's by up to kDecodeSlack, and
+//    the four lanes of a column exchange their maxima (gfx950's lane swaps)
+//    only in a block where one lane's scores pass it by more than that.
 //  * V tile: load j (j = 0..3) gives lane (g, n) dims 8 n .. 8 n + 7 of
 //    token 4 g + j, four full 256-byte rows per load.  The lane then holds
 //    its four tokens at eight dims; pairing halves gives, for each dim
@@ -585,6 +586,13 @@ __global__ __launch_bounds__(kWave* NW, (LDS ? 2 : decode_waves_hint<DT, D, GW>(
 //    into the registers of the tile (the pool slot may still be being
 //    written by this launch), and the first head group stores it.
 // The partition's states then merge and combine as in the VALU kernel.
+// Slack of the matrix-core decode's running maxima, in base-2 units: a
+// column's maximum is raised (and its accumulators rescaled) only when a score
+// exceeds it by more than this, so after the first keys the rescale almost
+// never runs; weights stay <= 2^8, exact enough as fp16 or as a bf16 head
+// plus remainder.
+constexpr float kDecodeSlack = 8.f;
+
 // A 16-byte tile load (cache policy CP, as load_tile) whose wave-uniform part
 // of the offset sits in a scalar register, so that one vector offset serves
 // all loads of a tile.
@@ -697,13 +705,24 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (4 * g + r >= valid) s[r] = -INFINITY;
-    const float mx = max_over_lane_groups(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
-    const float mn = fmaxf(m, mx * c2);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    m = mn;
+    // the running maximum moves only when a score exceeds it by more than
+    // kDecodeSlack (weights stay <= 2^kDecodeSlack in between); the lane's
+    // own scores decide whether any of the column's can, so the column's
+    // maximum over its four lanes, the factor and the accumulators' rescale
+    // are formed only in such a block
+    const float mxl = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    float alpha = 1.f;
+    if (__builtin_amdgcn_ballot_w64(mxl * c2 > m + kDecodeSlack)) {
+      const float mxs = max_over_lane_groups(mxl) * c2;
+      const float mn = mxs > m + kDecodeSlack ? mxs : m;
+      alpha = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t] *= alpha;
+    }
     float x[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -mn));
+    for (int r = 0; r < 4; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -m));
     lsum = lsum * alpha + ((x[0] + x[1]) + (x[2] + x[3]));
     const f2 x01 = {x[0], x[1]}, x23 = {x[2], x[3]};
     u32x2 pb, pl;
@@ -716,10 +735,6 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
       pl = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01 - __builtin_convertvector(h01, f2), b2)),
                  __builtin_bit_cast(uint32_t, __builtin_convertvector(x23 - __builtin_convertvector(h23, f2), b2))};
     }
-    // every block rescales (alpha = 1 when no maximum moved): a branch on a
-    // vote makes the compiler keep a second copy of the accumulators
-#pragma unroll
-    for (int t = 0; t < 8; ++t) o[t] *= alpha;
     // vv[j] word w holds dims 8 n + 2 w (low half) and 8 n + 2 w + 1 (high
     // half) of token 4 g + j
     const uint32_t v0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
@@ -1038,30 +1053,45 @@ __global__ __launch_bounds__(256, WPS) void paged_decode_shared_kernel(const Sha
     }
     const bool bad[2] = {bad_c[0], bad_c[1]};
     u32x4 pb[RG], pl[RG];
-    float alpha[RG];
-    bool rescale = false;
+    float s[RG][8], mxl[RG];
+    bool moved = false;
 #pragma unroll
     for (int j = 0; j < RG; ++j) {
-      float s[8];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s[blk * 4 + v] = bad[blk] ? -INFINITY : sa[j][blk][v];
-      float mx = s[0];
+        for (int v = 0; v < 4; ++v) s[j][blk * 4 + v] = bad[blk] ? -INFINITY : sa[j][blk][v];
+      mxl[j] = s[j][0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-      mx = max_over_lane_groups(mx);
-      const float mxs = mx * c2;
-      const float mn = mxs > m[j] + kSharedSlack ? mxs : m[j];
-      alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
-      rescale |= mn > m[j];
-      m[j] = mn;
+      for (int i = 1; i < 8; ++i) mxl[j] = fmaxf(mxl[j], s[j][i]);
+      // the lane's own scores decide whether any of the column's can move
+      // its maximum; the column's maximum over its four lanes is formed
+      // only in such a stage
+      moved |= mxl[j] * c2 > m[j] + kSharedSlack;
+    }
+    float alpha[RG] = {};
+#pragma unroll
+    for (int j = 0; j < RG; ++j) alpha[j] = 1.f;
+    bool rescale = false;
+    if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+      for (int j = 0; j < RG; ++j) {
+        const float mxs = max_over_lane_groups(mxl[j]) * c2;
+        const float mn = mxs > m[j] + kSharedSlack ? mxs : m[j];
+        alpha[j] = __builtin_amdgcn_exp2f(m[j] - mn);
+        rescale |= mn > m[j];
+        m[j] = mn;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      const float mn = m[j];
       uint32_t ph[4], plo[4];
       float psum = 0.f;
 #pragma unroll
       for (int q2 = 0; q2 < 4; ++q2) {
-        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q2], c2, -mn));
-        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * q2 + 1], c2, -mn));
+        const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][2 * q2], c2, -mn));
+        const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][2 * q2 + 1], c2, -mn));
         psum += x0 + x1;
         const f2 xx = {x0, x1};
         if constexpr (DT == PKV_F16) {
@@ -1230,13 +1260,22 @@ __global__ __launch_bounds__(256, 3) void paged_decode_narrow_kernel(const Share
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[r] = -INFINITY;
     }
-    const float mx = max_over_lane_groups(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    const float mn = fmaxf(m, mx * c2);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    m = mn;
+    // as the matrix-core decode: the column's maximum lags by up to
+    // kDecodeSlack and is exchanged across its lanes only when one lane's
+    // scores pass it by more than that
+    const float mxl = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    float alpha = 1.f;
+    if (__builtin_amdgcn_ballot_w64(mxl * c2 > m + kDecodeSlack)) {
+      const float mxs = max_over_lane_groups(mxl) * c2;
+      const float mn = mxs > m + kDecodeSlack ? mxs : m;
+      alpha = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t] *= alpha;
+    }
     float x[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c2, -mn));
+    for (int r = 0; r < 4; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c2, -m));
     lsum = lsum * alpha + ((x[0] + x[1]) + (x[2] + x[3]));
     const f2 x01 = {x[0], x[1]}, x23 = {x[2], x[3]};
     u32x2 pb, pl;
@@ -1249,8 +1288,6 @@ __global__ __launch_bounds__(256, 3) void paged_decode_narrow_kernel(const Share
       pl = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01 - __builtin_convertvector(h01, f2), b2)),
                  __builtin_bit_cast(uint32_t, __builtin_convertvector(x23 - __builtin_convertvector(h23, f2), b2))};
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) o[t] *= alpha;
     const uint32_t v0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
     const uint32_t v1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
     const uint32_t v2[4] = {vv[2].x, vv[2].y, vv[2].z, vv[2].w};
