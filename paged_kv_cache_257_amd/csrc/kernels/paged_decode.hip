@@ -578,7 +578,8 @@ __global__ __launch_bounds__(kWave* NW, (LDS ? 2 : decode_waves_hint<DT, D, GW>(
 //  * Weights: fp16 inputs round them to fp16; bf16 inputs split them into a
 //    bf16 head and a bf16 remainder (two products), since bf16 weights
 //    alone put short contexts above the 2e-3 tolerance.  The normaliser
-//    sums the fp32 weights.
+//    sums the weights the products use: the fp16-rounded ones, or the fp32
+//    ones for bf16 (head + remainder match them to ~16 bits).
 //  * Masking: the tile's buffer resources cover only the rows that hold
 //    tokens (zeros beyond, so V rows past the length contribute 0 even if
 //    the pool holds NaN there) and scores of rows past the length are -inf.
@@ -723,13 +724,16 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
     float x[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -m));
-    lsum = lsum * alpha + ((x[0] + x[1]) + (x[2] + x[3]));
     const f2 x01 = {x[0], x[1]}, x23 = {x[2], x[3]};
     u32x2 pb, pl;
     if constexpr (DT == PKV_F16) {
-      pb = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01, h2)),
-                 __builtin_bit_cast(uint32_t, __builtin_convertvector(x23, h2))};
+      // the normaliser sums the weights as rounded (one dot product per pair)
+      const h2 h01 = __builtin_convertvector(x01, h2), h23 = __builtin_convertvector(x23, h2);
+      pb = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+      lsum = lsum * alpha + __builtin_amdgcn_fdot2(h23, h2{1.f16, 1.f16},
+                                                   __builtin_amdgcn_fdot2(h01, h2{1.f16, 1.f16}, 0.f, false), false);
     } else {
+      lsum = lsum * alpha + ((x[0] + x[1]) + (x[2] + x[3]));
       const b2 h01 = __builtin_convertvector(x01, b2), h23 = __builtin_convertvector(x23, b2);
       pb = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
       pl = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01 - __builtin_convertvector(h01, f2), b2)),
@@ -863,7 +867,8 @@ __global__ __launch_bounds__(kWave* NW, 3) void paged_decode_mfma_kernel(const D
 // when a score passes it by more than 2^8 in weight, so after the first
 // keys the accumulators are almost never rescaled.  Softmax weights enter
 // the products as fp16 (fp16 inputs) or a bf16 head plus a bf16 remainder
-// (bf16 inputs); the normaliser sums the fp32 weights.
+// (bf16 inputs); the normaliser sums the weights the products use (the
+// fp16-rounded ones; the fp32 ones for bf16).
 // Every block in a node is full in every member (a sequence's last block is
 // never shared); a stage's second block past the chunk, or a table entry
 // outside the pool, reads nothing and its keys are masked.
@@ -1092,11 +1097,14 @@ __global__ __launch_bounds__(256, WPS) void paged_decode_shared_kernel(const Sha
       for (int q2 = 0; q2 < 4; ++q2) {
         const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][2 * q2], c2, -mn));
         const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][2 * q2 + 1], c2, -mn));
-        psum += x0 + x1;
         const f2 xx = {x0, x1};
         if constexpr (DT == PKV_F16) {
-          ph[q2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(xx, h2));
+          // the normaliser sums the weights as rounded (one dot product per pair)
+          const h2 hp = __builtin_convertvector(xx, h2);
+          ph[q2] = __builtin_bit_cast(uint32_t, hp);
+          psum = __builtin_amdgcn_fdot2(hp, h2{1.f16, 1.f16}, psum, false);
         } else {
+          psum += x0 + x1;
           const b2 hi2 = __builtin_convertvector(xx, b2);
           ph[q2] = __builtin_bit_cast(uint32_t, hi2);
           plo[q2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(xx - __builtin_convertvector(hi2, f2), b2));
@@ -1276,13 +1284,16 @@ __global__ __launch_bounds__(256, 3) void paged_decode_narrow_kernel(const Share
     float x[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c2, -m));
-    lsum = lsum * alpha + ((x[0] + x[1]) + (x[2] + x[3]));
     const f2 x01 = {x[0], x[1]}, x23 = {x[2], x[3]};
     u32x2 pb, pl;
     if constexpr (DT == PKV_F16) {
-      pb = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01, h2)),
-                 __builtin_bit_cast(uint32_t, __builtin_convertvector(x23, h2))};
+      // the normaliser sums the weights as rounded (one dot product per pair)
+      const h2 h01 = __builtin_convertvector(x01, h2), h23 = __builtin_convertvector(x23, h2);
+      pb = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+      lsum = lsum * alpha + __builtin_amdgcn_fdot2(h23, h2{1.f16, 1.f16},
+                                                   __builtin_amdgcn_fdot2(h01, h2{1.f16, 1.f16}, 0.f, false), false);
     } else {
+      lsum = lsum * alpha + ((x[0] + x[1]) + (x[2] + x[3]));
       const b2 h01 = __builtin_convertvector(x01, b2), h23 = __builtin_convertvector(x23, b2);
       pb = u32x2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
       pl = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(x01 - __builtin_convertvector(h01, f2), b2)),

@@ -38,7 +38,10 @@
 // fp16 (11-bit significand); for bf16 they are split into a bf16 head and a
 // bf16 remainder (two MFMAs, ~16 bits), since bf16 weights alone put the
 // error of short contexts above 2e-3.  Both round to nearest even, two
-// weights per conversion instruction.  The normaliser sums the fp32 weights.
+// weights per conversion instruction.  The normaliser sums the weights the
+// products use: the fp16-rounded ones (which halves the worst error of
+// short rows against summing the unrounded ones), or for bf16 the fp32 ones,
+// which head + remainder match to ~16 bits.
 // A row's running maximum is raised only when a score exceeds it by more
 // than 2^8 in weight, and the accumulators are rescaled only in stages where
 // some row's maximum moved (a wave-wide vote); otherwise the factor is
@@ -350,11 +353,15 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
       for (int q2 = 0; q2 < 4; ++q2) {
         const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][2 * q2], c2, -mn));
         const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][2 * q2 + 1], c2, -mn));
-        psum += x0 + x1;
         const f2 xx = {x0, x1};
         if constexpr (DT == PKV_F16) {
-          ph[q2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(xx, h2));
+          // the normaliser sums the weights as rounded, the values the
+          // products use: one dot product with (1, 1) per pair
+          const h2 hp = __builtin_convertvector(xx, h2);
+          ph[q2] = __builtin_bit_cast(uint32_t, hp);
+          psum = __builtin_amdgcn_fdot2(hp, h2{1.f16, 1.f16}, psum, false);
         } else {
+          psum += x0 + x1;
           const b2 hi = __builtin_convertvector(xx, b2);
           ph[q2] = __builtin_bit_cast(uint32_t, hi);
           plo[q2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(xx - __builtin_convertvector(hi, f2), b2));
