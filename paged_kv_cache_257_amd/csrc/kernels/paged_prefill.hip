@@ -213,9 +213,12 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
     }
     return __builtin_amdgcn_readlane(tbl, b - base);
   };
+  // the tile's byte offset as an unsigned 32 x 32 -> 64-bit product (the
+  // launch checks that a block's stride fits 32 bits): two scalar multiplies
   auto tile_rsrc = [&](const char* base, int blk) __attribute__((always_inline)) {
     const bool ok = unsigned(blk) < unsigned(p.num_blocks);
-    return make_rsrc(base + (ok ? int64_t(blk) * blk_stride : 0), ok ? TILE : 0);
+    const uint64_t off = uint64_t(ok ? uint32_t(blk) : 0u) * uint32_t(blk_stride);
+    return make_rsrc(base + off, ok ? TILE : 0);
   };
   // a block of the stage being loaded lies outside the pool (its keys are
   // masked when the stage is computed)
@@ -590,6 +593,8 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, flo
   // the running maxima are taken over scaled scores, which equals scaling
   // the maximum only for a positive scale
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PKV_E_BAD_ARG, "scale must be finite and > 0");
+  if (int64_t(d.num_kv_heads) * kBlockTokens * d.head_dim * 2 > int64_t(UINT32_MAX))
+    return fail(PKV_E_UNSUPPORTED, "a block of the pool spans more than 4 GiB");
   if (num_q_heads < 1 || num_q_heads % d.num_kv_heads != 0)
     return fail(PKV_E_BAD_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
   const int group = num_q_heads / d.num_kv_heads;
