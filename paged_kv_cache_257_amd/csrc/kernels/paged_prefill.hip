@@ -267,11 +267,12 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
           b[i] &= z1;
         }
       }
+      // dim e of the two tokens as one word (token tok low, tok + 1 high):
+      // one byte permute per word
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t ea = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        const uint32_t eb = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        *reinterpret_cast<uint32_t*>(&lv[buf][(ch * 8 + e) * VROW + vt_col(ch * 8 + e, tok)]) = ea | (eb << 16);
+        const uint32_t w = __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+        *reinterpret_cast<uint32_t*>(&lv[buf][(ch * 8 + e) * VROW + vt_col(ch * 8 + e, tok)]) = w;
       }
     }
   };
