@@ -1027,9 +1027,9 @@ __global__ __launch_bounds__(256, WPS) void paged_decode_shared_kernel(const Sha
     const uint32_t b[4] = {vr1.x, vr1.y, vr1.z, vr1.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t ea = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      const uint32_t eb = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      *reinterpret_cast<uint32_t*>(&lv[buf][(ch * 8 + e) * VROW + vt_col(ch * 8 + e, tok)]) = ea | (eb << 16);
+      // Element e of token tok (low half) and of token tok + 1 (high half).
+      const uint32_t w = __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&lv[buf][(ch * 8 + e) * VROW + vt_col(ch * 8 + e, tok)]) = w;
     }
   };
 
