@@ -840,7 +840,16 @@ pkv_status pkv_paged_decode_noalloc(const pkv_pool* pool, const void* q, const v
  * tickets zero) of at least pkv_prefill_workspace_bytes(info, head_dim)
  * bytes, may be NULL when no tile is split.  fp16 and bf16 pools, head_dim
  * 64 or 128 (else PKV_E_UNSUPPORTED); the products run on the matrix cores
- * with fp32 accumulation.  Asynchronous on `stream`; allocates nothing. */
+ * with fp32 accumulation, the softmax weights rounded to fp16.  A bf16 pool's
+ * V is converted to fp16 as it is staged (exact below 2^16 in magnitude), and
+ * every bf16 call makes two launches: that pass, then an exact pass (V in
+ * bf16, weights as a bf16 head + remainder) whose workgroups exit at once
+ * unless the first pass met a V value of magnitude 2^16 or more.  The first
+ * pass records that in one word per device inside the library, raised to
+ * the call's number (numbers only grow), so concurrent calls can cause an
+ * exact pass that was not needed but never skip one that was.  Setting the
+ * environment variable PKV_PREFILL_BF16_EXACT=1 runs the exact pass alone.
+ * Asynchronous on `stream`; allocates nothing. */
 pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, float* out, int32_t num_seqs,
                              int32_t num_q_heads, const int32_t* block_tables, int32_t table_stride,
                              const int32_t* context_lens, float scale, const int32_t* plan,

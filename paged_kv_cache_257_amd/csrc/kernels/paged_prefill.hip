@@ -34,19 +34,28 @@
 // stale or NaN slots never reach the output.
 //
 // Precision.  Products of 16-bit inputs accumulate in fp32.  The softmax
-// weights must become 16-bit MFMA operands: for fp16 they are rounded to
-// fp16 (11-bit significand); for bf16 they are split into a bf16 head and a
-// bf16 remainder (two MFMAs, ~16 bits), since bf16 weights alone put the
-// error of short contexts above 2e-3.  Both round to nearest even, two
-// weights per conversion instruction.  The normaliser sums the weights the
+// weights must become 16-bit MFMA operands, and bf16 weights alone (8-bit
+// significand) put the error of short contexts above 2e-3.  So the weights
+// are rounded to fp16 (11 bits) and O^T += V^T P^T runs in fp16 for both
+// pool types: a bf16 pool's V is converted to fp16 while it is staged,
+// which is exact for magnitudes below 2^16 (bf16 keeps 8 significant bits,
+// fp16 11; below 2^-14 fp16 steps are 2^-24 apart).  A bf16 launch that
+// stages a V value of magnitude 2^16 or more records its launch number in a
+// device word; a second, exact pass follows every bf16 launch and runs only
+// when it finds its own number there (otherwise its workgroups exit at
+// once).  The exact pass keeps V in bf16 and splits each weight into a bf16
+// head and a bf16 remainder (two MFMAs, ~16 bits).  Weights round to nearest
+// even, two per conversion instruction.  The normaliser sums the weights the
 // products use: the fp16-rounded ones (which halves the worst error of
-// short rows against summing the unrounded ones), or for bf16 the fp32 ones,
-// which head + remainder match to ~16 bits.
+// short rows against summing the unrounded ones), or in the exact pass the
+// fp32 ones, which head + remainder match to ~16 bits.
 // A row's running maximum is raised only when a score exceeds it by more
 // than 2^8 in weight, and the accumulators are rescaled only in stages where
 // some row's maximum moved (a wave-wide vote); otherwise the factor is
 // exactly 1.
+#include <atomic>
 #include <cmath>
+#include <cstdlib>
 
 #include "mfma_common.h"
 
@@ -88,7 +97,16 @@ struct PrefillParams {
   int32_t table_stride;
   int32_t num_blocks;
   float scale_log2;
+  uint64_t overflow_launch;  // bf16 fast pass: this launch's number, recorded on overflow
+  uint64_t gate_launch;      // bf16 exact pass: run only if the device word reached it
 };
+
+// Largest launch number whose fast bf16 pass staged a V value that fp16
+// cannot hold (magnitude >= 2^16).  One word per device, raised with an
+// atomic maximum and never lowered: launch numbers only grow, so a pass
+// never misses its own record (concurrent launches can only cause an exact
+// pass that was not needed).
+__device__ unsigned long long g_v_overflow_launch = 0;
 
 // 16-byte store / load at device scope: cache policy sc1, the coherence
 // level the compiler gives relaxed agent-scope atomics (which it emits as
@@ -109,8 +127,22 @@ __device__ __forceinline__ f4 load_device(__amdgpu_buffer_rsrc_t r, int offset) 
 // SPLIT: the plan splits some tiles' keys into parts; without it the kernel
 // carries no code for partial records (the main loop then keeps its
 // registers: that code alone cost 13% on unsplit launches).
-template <int DT, int D, int GW, bool SPLIT>
+// EXACT (bf16 only): the exact pass, V staged as bf16 and the weights as a
+// bf16 head + remainder; otherwise V and the weights are fp16.
+template <int DT, int D, int GW, bool SPLIT, bool EXACT>
 __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const PrefillParams p) {
+  constexpr bool VCONV = DT == PKV_BF16 && !EXACT;  // bf16 V staged as fp16
+  constexpr bool PSPLIT = DT == PKV_BF16 && EXACT;  // weights as head + remainder
+  constexpr int PVT = PSPLIT ? PKV_BF16 : PKV_F16;  // operand type of O^T += V^T P^T
+  if constexpr (EXACT) {
+    // one read, shared through LDS: a concurrent launch may raise the word
+    // meanwhile, and the whole workgroup must take the same branch
+    __shared__ int sm_run;
+    if (threadIdx.x == 0)
+      sm_run = __hip_atomic_load(&g_v_overflow_launch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= p.gate_launch;
+    __syncthreads();
+    if (!sm_run) return;
+  }
   constexpr int RG = kPfRowGroups;         // 16-row groups per wave
   constexpr int TPW = 16 * RG / GW;        // query tokens per wave
   constexpr int TQ = kPfWaves * TPW;       // query tokens per workgroup
@@ -224,6 +256,7 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
   // masked when the stage is computed)
   bool bad_ld[2] = {false, false};
   bool bad_c[2] = {false, false};  // the same flags of the stage being computed
+  float vmax = 0.f;                // largest |v| this thread staged (VCONV)
   auto load_stage = [&](int st) __attribute__((always_inline)) {
     const int ids[2] = {table_entry(st * 2), table_entry(st * 2 + 1)};
 #pragma unroll
@@ -268,10 +301,20 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
         }
       }
       // dim e of the two tokens as one word (token tok low, tok + 1 high):
-      // one byte permute per word
+      // one byte permute per word; bf16 through fp32 to fp16 (exact below
+      // 2^16 in magnitude, the largest magnitude kept for the overflow check)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t w = __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+        uint32_t w;
+        if constexpr (VCONV) {
+          const uint32_t ua = (e & 1) ? (a[e >> 1] & 0xFFFF0000u) : (a[e >> 1] << 16);
+          const uint32_t ub = (e & 1) ? (b[e >> 1] & 0xFFFF0000u) : (b[e >> 1] << 16);
+          const f2 vv = {__uint_as_float(ua), __uint_as_float(ub)};
+          vmax = fmaxf(vmax, fmaxf(fabsf(vv.x), fabsf(vv.y)));
+          w = __builtin_bit_cast(uint32_t, __builtin_convertvector(vv, h2));
+        } else {
+          w = __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+        }
         *reinterpret_cast<uint32_t*>(&lv[buf][(ch * 8 + e) * VROW + vt_col(ch * 8 + e, tok)]) = w;
       }
     }
@@ -358,7 +401,7 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
         const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][2 * q2], c2, -mn));
         const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][2 * q2 + 1], c2, -mn));
         const f2 xx = {x0, x1};
-        if constexpr (DT == PKV_F16) {
+        if constexpr (!PSPLIT) {
           // the normaliser sums the weights as rounded, the values the
           // products use: one dot product with (1, 1) per pair
           const h2 hp = __builtin_convertvector(xx, h2);
@@ -373,7 +416,7 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
       }
       lsum[j] = lsum[j] * alpha[j] + psum;
       pb[j] = u32x4{ph[0], ph[1], ph[2], ph[3]};
-      if constexpr (DT == PKV_BF16) pl[j] = u32x4{plo[0], plo[1], plo[2], plo[3]};
+      if constexpr (PSPLIT) pl[j] = u32x4{plo[0], plo[1], plo[2], plo[3]};
     }
     // rescale the accumulators only when some row's maximum moved
     if (__builtin_amdgcn_ballot_w64(rescale)) {
@@ -389,8 +432,8 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
       const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + vt_col(dt * 16, 16 + 4 * g));
       return u32x4{a0.x, a0.y, a1.x, a1.y};
     };
-    // (two ahead where the registers allow: fp16 without split records)
-    constexpr int AHEAD = (DT == PKV_F16 && !SPLIT) ? 2 : 1;
+    // (two ahead where the registers allow: fp16 weights, no split records)
+    constexpr int AHEAD = (!PSPLIT && !SPLIT) ? 2 : 1;
     u32x4 a_q[AHEAD];
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) a_q[i] = vt_operand(i);
@@ -400,8 +443,8 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
       if (dt + AHEAD < NDT) a_q[dt % AHEAD] = vt_operand(dt + AHEAD);
 #pragma unroll
       for (int j = 0; j < RG; ++j) {
-        o[j][dt] = mfma_k32<DT>(a, pb[j], o[j][dt]);
-        if constexpr (DT == PKV_BF16) o[j][dt] = mfma_k32<DT>(a, pl[j], o[j][dt]);
+        o[j][dt] = mfma_k32<PVT>(a, pb[j], o[j][dt]);
+        if constexpr (PSPLIT) o[j][dt] = mfma_k32<PVT>(a, pl[j], o[j][dt]);
       }
     }
   };
@@ -440,6 +483,10 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
     }
   }
 
+  if constexpr (VCONV) {  // a staged V value fp16 cannot hold: the exact pass redoes this launch
+    if (__builtin_amdgcn_ballot_w64(vmax >= 65536.f) && lane == 0)
+      atomicMax(&g_v_overflow_launch, (unsigned long long)p.overflow_launch);
+  }
   float lt[RG];
 #pragma unroll
   for (int j = 0; j < RG; ++j) {
@@ -542,30 +589,32 @@ __global__ __launch_bounds__(kPfThreads, 3) void paged_prefill_kernel(const Pref
 
 typedef void (*PrefillFn)(const PrefillParams);
 
-template <int DT, int D, bool SPLIT>
+template <int DT, int D, bool SPLIT, bool EXACT>
 PrefillFn pick_gw(int gw) {
   switch (gw) {
-    case 1: return paged_prefill_kernel<DT, D, 1, SPLIT>;
-    case 2: return paged_prefill_kernel<DT, D, 2, SPLIT>;
-    case 4: return paged_prefill_kernel<DT, D, 4, SPLIT>;
-    case 8: return paged_prefill_kernel<DT, D, 8, SPLIT>;
-    case 16: return paged_prefill_kernel<DT, D, 16, SPLIT>;
+    case 1: return paged_prefill_kernel<DT, D, 1, SPLIT, EXACT>;
+    case 2: return paged_prefill_kernel<DT, D, 2, SPLIT, EXACT>;
+    case 4: return paged_prefill_kernel<DT, D, 4, SPLIT, EXACT>;
+    case 8: return paged_prefill_kernel<DT, D, 8, SPLIT, EXACT>;
+    case 16: return paged_prefill_kernel<DT, D, 16, SPLIT, EXACT>;
   }
   return nullptr;
 }
 
-template <int DT, int D>
+template <int DT, int D, bool EXACT>
 PrefillFn pick_split(int gw, bool split) {
-  return split ? pick_gw<DT, D, true>(gw) : pick_gw<DT, D, false>(gw);
+  return split ? pick_gw<DT, D, true, EXACT>(gw) : pick_gw<DT, D, false, EXACT>(gw);
 }
 
-PrefillFn pick_prefill(int32_t dtype, int32_t head_dim, int gw, bool split) {
+// exact: the bf16 exact pass (fp16 pools have one pass)
+PrefillFn pick_prefill(int32_t dtype, int32_t head_dim, int gw, bool split, bool exact) {
   if (dtype == PKV_F16) {
-    if (head_dim == 64) return pick_split<PKV_F16, 64>(gw, split);
-    if (head_dim == 128) return pick_split<PKV_F16, 128>(gw, split);
+    if (head_dim == 64) return pick_split<PKV_F16, 64, false>(gw, split);
+    if (head_dim == 128) return pick_split<PKV_F16, 128, false>(gw, split);
   } else if (dtype == PKV_BF16) {
-    if (head_dim == 64) return pick_split<PKV_BF16, 64>(gw, split);
-    if (head_dim == 128) return pick_split<PKV_BF16, 128>(gw, split);
+    if (head_dim == 64) return exact ? pick_split<PKV_BF16, 64, true>(gw, split) : pick_split<PKV_BF16, 64, false>(gw, split);
+    if (head_dim == 128)
+      return exact ? pick_split<PKV_BF16, 128, true>(gw, split) : pick_split<PKV_BF16, 128, false>(gw, split);
   }
   return nullptr;
 }
@@ -648,8 +697,34 @@ extern "C" pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, flo
   prm.scale_log2 = scale * kLog2eF;
   const int64_t grid = int64_t(info->n_work) * d.num_kv_heads * (group / gw);
   if (grid > INT32_MAX) return fail(PKV_E_BAD_ARG, "batch too large for one launch");
-  PrefillFn fn = pick_prefill(d.dtype, d.head_dim, gw, info->n_split > 0);
-  if (!fn) return fail(PKV_E_UNSUPPORTED, "no prefill kernel for this dtype / head_dim / group");
-  hipLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kPfThreads), 0, static_cast<hipStream_t>(stream), prm);
-  return launch_status("paged_prefill launch");
+  const bool split = info->n_split > 0;
+  prm.overflow_launch = 0;
+  prm.gate_launch = 0;
+  if (d.dtype == PKV_F16) {
+    PrefillFn fn = pick_prefill(d.dtype, d.head_dim, gw, split, false);
+    if (!fn) return fail(PKV_E_UNSUPPORTED, "no prefill kernel for this dtype / head_dim / group");
+    hipLaunchKernelGGL(fn, dim3(uint32_t(grid)), dim3(kPfThreads), 0, static_cast<hipStream_t>(stream), prm);
+    return launch_status("paged_prefill launch");
+  }
+  // bf16: the fast pass (V and weights in fp16), then the exact pass, which
+  // runs only if the fast one met a V value of magnitude >= 2^16.
+  // PKV_PREFILL_BF16_EXACT=1 runs the exact pass alone (read per call).
+  PrefillFn fast = pick_prefill(d.dtype, d.head_dim, gw, split, false);
+  PrefillFn exact = pick_prefill(d.dtype, d.head_dim, gw, split, true);
+  if (!fast || !exact) return fail(PKV_E_UNSUPPORTED, "no prefill kernel for this dtype / head_dim / group");
+  const char* ex = std::getenv("PKV_PREFILL_BF16_EXACT");
+  if (ex && ex[0] == '1') {
+    hipLaunchKernelGGL(exact, dim3(uint32_t(grid)), dim3(kPfThreads), 0, static_cast<hipStream_t>(stream), prm);
+    return launch_status("paged_prefill launch");
+  }
+  static std::atomic<uint64_t> launches{0};
+  const uint64_t id = launches.fetch_add(1, std::memory_order_relaxed) + 1;
+  prm.overflow_launch = id;
+  hipLaunchKernelGGL(fast, dim3(uint32_t(grid)), dim3(kPfThreads), 0, static_cast<hipStream_t>(stream), prm);
+  const pkv_status st = launch_status("paged_prefill launch");
+  if (st != PKV_OK) return st;
+  prm.overflow_launch = 0;
+  prm.gate_launch = id;
+  hipLaunchKernelGGL(exact, dim3(uint32_t(grid)), dim3(kPfThreads), 0, static_cast<hipStream_t>(stream), prm);
+  return launch_status("paged_prefill exact pass launch");
 }

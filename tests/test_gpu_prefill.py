@@ -225,3 +225,58 @@ def test_dominant_keys_outside_first_lane_group(dtype, hq, hkv, max_keys):
     worst = run_full(cfg, max_keys=max_keys, values=(q, k, v))
     print(f"\n[gpu] peaked prefill {dtype} {hq}/{hkv} max_keys={max_keys}: max err {worst:.2e}")
 
+
+
+def run_large_v(cfg, values, max_keys):
+    """run_full with a tolerance relative to each output's magnitude (the
+    large values make outputs of order 1e4 .. 1e5); returns the worst
+    relative error."""
+    case = PrefillCase(cfg, max_keys=max_keys, values=values)
+    try:
+        worst = 0.0
+        for k in range(len(case.sh.steps)):
+            items, out = case.step()
+            sync()
+            got = out.cpu().numpy().astype(np.float64)
+            assert np.isfinite(got).all(), (cfg.name, k)
+            pos = 0
+            for seq, t0, n, _ in items:
+                ref = case.ora.attend(seq, t0, n)
+                rel = float(np.max(np.abs(got[pos:pos + n] - ref) / np.maximum(1.0, np.abs(ref))))
+                worst = max(worst, rel)
+                assert rel <= TOL[cfg.dtype], (cfg.name, k, seq, t0, n, rel)
+                pos += n
+        return worst
+    finally:
+        case.close()
+
+
+@pytest.mark.parametrize("hq,hkv,max_keys", [(8, 2, 0), (8, 2, 32), (4, 4, 0)])
+def test_bf16_values_beyond_fp16_take_the_exact_pass(hq, hkv, max_keys):
+    """bf16 V is staged as fp16, which holds magnitudes below 2^16 exactly;
+    a launch that meets a larger value (here +2^17 in a few token rows of
+    every head) is redone by the exact pass (bf16 V, weights as head +
+    remainder).  Outputs stay finite and within 2e-3 of the oracle relative
+    to their magnitude, for the launches that meet the values and for the
+    later ones (whose contexts hold them)."""
+    cfg = PrefillConfig(name=f"pf_bigv_{hq}_{hkv}", index=32, dtype="bf16", num_q_heads=hq,
+                        num_kv_heads=hkv, head_dim=128, chunk_tokens=64, fixed_prompts=(150, 37))
+    sh = draw_prefill_shapes(cfg)
+    q, k, v = draw_prefill_values(cfg, sh.prompts)
+    v = v.copy()
+    big = np.array([3, 70, 149, 150 + 20], dtype=np.int64)  # rows of both prompts, several chunks
+    v[big, :, :8] = 0x4800  # bf16 storage bits of +131072 = 2^17
+    worst = run_large_v(cfg, (q, k, v), max_keys)
+    print(f"\n[gpu] bf16 prefill with V = 2^17 entries, {hq}/{hkv} max_keys={max_keys}: "
+          f"worst relative err {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name,max_keys", [("pf_tiny_gqa_bf16", 0), ("pf_tiny_gqa_bf16", 32)])
+def test_bf16_exact_pass_alone(name, max_keys, monkeypatch):
+    """PKV_PREFILL_BF16_EXACT=1 runs the bf16 exact pass by itself: every
+    output, and its error stays at the ~16-bit level of head + remainder
+    weights (the fast pass's fp16 weights give ~1e-3)."""
+    monkeypatch.setenv("PKV_PREFILL_BF16_EXACT", "1")
+    worst = run_full(prefill_config_by_name(name), max_keys=max_keys)
+    assert worst <= 1e-4, worst
+    print(f"\n[gpu] prefill {name} exact pass alone, max_keys={max_keys}: max_err={worst:.3e}", flush=True)
