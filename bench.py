@@ -416,7 +416,7 @@ def bench_prefix_shared(args, cfg):
     from paged_kv_cache_257_amd import Pool
     from paged_kv_cache_257_amd.step import DecodeIteration
     from workloads import draw_normal_storage
-    from workloads.churn import choose_churn, draw_prefix_shared_plan
+    from workloads.churn import apply_churn, draw_churn, draw_prefix_shared_plan
 
     warm = min(args.warmup, 8)
     steps = min(args.steps, cfg.iterations - warm)
@@ -457,12 +457,18 @@ def bench_prefix_shared(args, cfg):
     ev = timing_events(total)
     torch.cuda.synchronize()
 
+    # the seeded retire / fork draws are workload input, drawn before the
+    # loop like the K/V values (every iteration decodes num_seqs sequences)
+    draws = [draw_churn(cfg, it, cfg.num_seqs) for it in range(total)]
+
     def iteration(it):
-        seqs = np.asarray([x for x in pool.live() if x != root], dtype=np.int32)
+        live = np.asarray(pool.live(), dtype=np.int32)
+        seqs = live[live != root]
+        assert len(seqs) == cfg.num_seqs
         q, k, v = vals[it % 4]
         lay = step.step(seqs, q, out, k, v, cfg.scale, events=ev[it] if it % every == 0 else None)
         loads.append(lay.plan.shared_kv)
-        retire, parents = choose_churn(cfg, it, seqs.tolist())
+        retire, parents = apply_churn(seqs, *draws[it])
         for x in retire:
             pool.free(x)
         for x in parents:

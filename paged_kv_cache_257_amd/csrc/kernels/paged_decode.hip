@@ -1673,13 +1673,51 @@ pkv_status setup_decode(const pkv_pool* pool, const void* q, const void* k_new, 
   return PKV_OK;
 }
 
+// A second stream per device for the narrow shared-block launch, so that it
+// runs beside the wide one: the wide kernel is bound by its matrix-core
+// chain at two workgroups per CU and leaves registers and LDS for one
+// narrow workgroup on each CU.  Created on the first such call on the
+// device; the fork / join events are recorded and waited for under a lock,
+// so that calls from several host threads keep their own dependencies.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kSideDevices = 64;
+std::mutex side_mu;
+SideStream side_tab[kSideDevices];
+
+// *out stays null when the side stream does not exist yet and `s` is being
+// captured into a graph (nothing is created during a capture).
+pkv_status side_stream(hipStream_t s, SideStream** out) {  // caller holds side_mu
+  *out = nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices)
+    return fail(PKV_E_HIP, "no current HIP device for the shared-block side stream");
+  SideStream& ss = side_tab[dev];
+  if (!ss.stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return launch_status("stream capture query");
+    if (cs != hipStreamCaptureStatusNone) return PKV_OK;
+    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      return launch_status("shared-block side stream creation");
+  }
+  *out = &ss;
+  return PKV_OK;
+}
+
 // ev_start / ev_stop (optional) are attached to the dispatch itself
 // (hipExtLaunchKernel), so their interval is the kernel's execution, without
 // the queueing of separate marker packets.
-// The shared-block launch of a plan with nodes: one workgroup per (shared
-// item, KV head), writing the nodes' split-K records.
+// The shared-block launches of a plan with nodes: one workgroup per (shared
+// item, KV head), writing the nodes' split-K records; wide nodes on `s`,
+// narrow ones on the side stream when `concurrent` (joined back into `s`),
+// else after the wide launch on `s`.
 pkv_status launch_shared(const pkv_pool* pool, const DecodeParams& prm, const int32_t* plan,
-                         const pkv_decode_plan_info* info, hipStream_t s, hipEvent_t ev_start) {
+                         const pkv_decode_plan_info* info, hipStream_t s, hipEvent_t ev_start,
+                         bool concurrent) {
   SharedParams sp;
   sp.q = prm.q;
   sp.k_cache = prm.k_cache;
@@ -1707,38 +1745,64 @@ pkv_status launch_shared(const pkv_pool* pool, const DecodeParams& prm, const in
       pool->desc.dtype == PKV_F16
           ? (three ? paged_decode_shared_kernel<PKV_F16, kCacheReuse, 3> : paged_decode_shared_kernel<PKV_F16, kCacheReuse, 2>)
           : (three ? paged_decode_shared_kernel<PKV_BF16, kCacheReuse, 3> : paged_decode_shared_kernel<PKV_BF16, kCacheReuse, 2>);
-  if (info->n_wide_nodes > 0 && info->n_shared_items > 0) {
-    const uint32_t grid = uint32_t(int64_t(info->n_shared_items) * prm.num_kv_heads);
+  const bool wide = info->n_wide_nodes > 0 && info->n_shared_items > 0;
+  const bool narrow = info->n_nodes > info->n_wide_nodes && info->n_narrow_items > 0;
+  SharedParams np = sp;
+  np.nodes = sp.nodes + kNodeInts * int64_t(info->n_wide_nodes);
+  np.n_nodes = info->n_nodes - info->n_wide_nodes;
+  void (*nfn)(const SharedParams) = pool->desc.dtype == PKV_F16 ? paged_decode_narrow_kernel<PKV_F16, kCacheStream>
+                                                                : paged_decode_narrow_kernel<PKV_BF16, kCacheStream>;
+  const uint32_t wgrid = uint32_t(int64_t(info->n_shared_items) * prm.num_kv_heads);
+  const uint32_t ngrid = uint32_t(int64_t(info->n_narrow_items) * prm.num_kv_heads);
+  // PKV_SHARED_CONCURRENT=0 (read at every launch) keeps both on `s`
+  const char* ce = std::getenv("PKV_SHARED_CONCURRENT");
+  std::unique_lock<std::mutex> lock(side_mu, std::defer_lock);
+  SideStream* ss = nullptr;
+  if (wide && narrow && concurrent && !(ce && ce[0] == '0')) {
+    lock.lock();
+    if (pkv_status st = side_stream(s, &ss)) return st;
+  }
+  if (ss) {
+    // a start event brackets both launches from here
+    if (ev_start && hipEventRecord(ev_start, s) != hipSuccess) return launch_status("decode start event");
+    if (hipEventRecord(ss->fork, s) != hipSuccess || hipStreamWaitEvent(ss->stream, ss->fork, 0) != hipSuccess)
+      return launch_status("shared-block fork");
+    hipLaunchKernelGGL(nfn, dim3(ngrid), dim3(256), 0, ss->stream, np);
+    if (pkv_status st = launch_status("paged_decode narrow shared-block launch")) return st;
+    if (hipEventRecord(ss->join, ss->stream) != hipSuccess) return launch_status("shared-block join record");
+    hipLaunchKernelGGL(fn, dim3(wgrid), dim3(256), 0, s, sp);
+    if (pkv_status st = launch_status("paged_decode wide shared-block launch")) return st;
+    if (hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return launch_status("shared-block join");
+    return PKV_OK;
+  }
+  if (wide) {
     if (ev_start)
-      hipExtLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, s, ev_start, nullptr, 0, sp);
+      hipExtLaunchKernelGGL(fn, dim3(wgrid), dim3(256), 0, s, ev_start, nullptr, 0, sp);
     else
-      hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, s, sp);
+      hipLaunchKernelGGL(fn, dim3(wgrid), dim3(256), 0, s, sp);
     if (pkv_status st = launch_status("paged_decode wide shared-block launch")) return st;
     ev_start = nullptr;
   }
-  if (info->n_nodes > info->n_wide_nodes && info->n_narrow_items > 0) {
-    SharedParams np = sp;
-    np.nodes = sp.nodes + kNodeInts * int64_t(info->n_wide_nodes);
-    np.n_nodes = info->n_nodes - info->n_wide_nodes;
-    void (*nfn)(const SharedParams) = pool->desc.dtype == PKV_F16 ? paged_decode_narrow_kernel<PKV_F16, kCacheStream>
-                                                                  : paged_decode_narrow_kernel<PKV_BF16, kCacheStream>;
-    const uint32_t grid = uint32_t(int64_t(info->n_narrow_items) * prm.num_kv_heads);
+  if (narrow) {
     if (ev_start)
-      hipExtLaunchKernelGGL(nfn, dim3(grid), dim3(256), 0, s, ev_start, nullptr, 0, np);
+      hipExtLaunchKernelGGL(nfn, dim3(ngrid), dim3(256), 0, s, ev_start, nullptr, 0, np);
     else
-      hipLaunchKernelGGL(nfn, dim3(grid), dim3(256), 0, s, np);
+      hipLaunchKernelGGL(nfn, dim3(ngrid), dim3(256), 0, s, np);
     if (pkv_status st = launch_status("paged_decode narrow shared-block launch")) return st;
   }
   return PKV_OK;
 }
 
+// concurrent: the narrow shared-block launch may run on the side stream
+// (not for the no-allocation entry point, which creates nothing)
 pkv_status launch_partitions(const pkv_pool* pool, const DecodeParams& prm, int gw, bool mfma,
                              const pkv_decode_plan_info* info, hipStream_t s,
-                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr) {
+                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                             bool concurrent = true) {
   if (info->n_nodes > 0) {
     // blocks held in common first: their records must exist before the
-    // decode launch below combines them (stream order)
-    if (pkv_status st = launch_shared(pool, prm, prm.work, info, s, ev_start)) return st;
+    // decode launch below combines them (stream order, or the join)
+    if (pkv_status st = launch_shared(pool, prm, prm.work, info, s, ev_start, concurrent)) return st;
     ev_start = nullptr;
   }
   int nw = waves_per_item(info->item_blocks);  // becomes the chosen instance's waves
@@ -1915,5 +1979,5 @@ extern "C" pkv_status pkv_paged_decode_noalloc(const pkv_pool* pool, const void*
     hipLaunchKernelGGL(clear_tickets_kernel, dim3(uint32_t((n + 255) / 256)), dim3(256), 0, s, prm.counters, n);
     if (pkv_status st = launch_status("decode scratch ticket clear")) return st;
   }
-  return launch_partitions(pool, prm, gw, mfma, info, s);
+  return launch_partitions(pool, prm, gw, mfma, info, s, nullptr, nullptr, false);
 }

@@ -61,16 +61,27 @@ def draw_prefix_shared_plan(cfg: PrefixSharedConfig) -> PrefixSharedPlan:
     return PrefixSharedPlan(tails=tails, num_blocks=nb, free_order=order)
 
 
+def draw_churn(cfg: PrefixSharedConfig, iteration: int, n_live: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Iteration's seeded draws for ``n_live`` decoding sequences: positions
+    (in ascending id order) of the ``churn`` that retire, then positions
+    among the survivors of the ``churn`` fork parents."""
+    k = cfg.churn
+    rng = np.random.default_rng((cfg.seed, STREAM_CHURN_BASE + int(iteration)))
+    ridx = rng.choice(n_live, size=k, replace=False)
+    pidx = rng.choice(n_live - k, size=k, replace=False)
+    return ridx, pidx
+
+
+def apply_churn(live_ids: Sequence[int], ridx: np.ndarray, pidx: np.ndarray) -> Tuple[List[int], List[int]]:
+    """(retire ids ascending, fork parents in admission order) for the draws."""
+    live = np.sort(np.asarray(live_ids, dtype=np.int64))
+    retire = np.sort(live[ridx])
+    survivors = np.delete(live, ridx)  # ids are distinct: ascending order kept
+    return retire.tolist(), survivors[pidx].tolist()
+
+
 def choose_churn(cfg: PrefixSharedConfig, iteration: int,
                  live_ids: Sequence[int]) -> Tuple[List[int], List[int]]:
     """Seeded (retire ids ascending, fork parents in admission order)."""
-    live = sorted(int(i) for i in live_ids)
-    k = cfg.churn
-    rng = np.random.default_rng((cfg.seed, STREAM_CHURN_BASE + int(iteration)))
-    ridx = rng.choice(len(live), size=k, replace=False)
-    retire = sorted(live[i] for i in ridx)
-    rset = set(retire)
-    survivors = [s for s in live if s not in rset]
-    pidx = rng.choice(len(survivors), size=k, replace=False)
-    parents = [survivors[i] for i in pidx]
-    return retire, parents
+    ridx, pidx = draw_churn(cfg, iteration, len(live_ids))
+    return apply_churn(live_ids, ridx, pidx)
