@@ -475,7 +475,7 @@ pkv_status pkv_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_
  * chunk's blocks for its columns.  Both write one split-K record per
  * member, query head and chunk.  A chunk is chunk_tokens / block_size
  * blocks (at least 64 for a narrow node), or, for chunk_tokens = 0, at
- * least 32 blocks (wide) or 64 (narrow), long nodes being cut into at most
+ * least 64 blocks, long nodes being cut into at most
  * 8 chunks (wide) or 4 (narrow); shared_chunk_blocks / narrow_chunk_blocks
  * give the smallest size of each kind and every node stores its own.  Every
  * sequence then attends over the rest of its blocks (from private_start) as

@@ -27,11 +27,13 @@ constexpr int32_t kNarrowColumns = 16;    // a node of at most this many columns
 // Chunk sizes without an explicit chunk_tokens: at least kWideChunkBlocks
 // (wide) or kNarrowChunkBlocks (narrow), and long nodes cut into at most
 // kWideChunks or kNarrowChunks chunks, which keeps the records a sequence
-// owns per node few.  A narrow workgroup streams its chunk with four waves;
-// a wide one computes up to 128 columns per staged block, so its chunks are
-// shorter (a 256-sequence batch over a 4096-token prefix: 32-block chunks
-// 0.2275 ms per decode, 64-block 0.2356, 128-block 0.2701).
-constexpr int32_t kWideChunkBlocks = 32, kNarrowChunkBlocks = 64;
+// owns per node few.  The wide launch runs beside the narrow one, which
+// hides its length; fewer, longer wide chunks leave fewer records to merge
+// and more room on the CUs for narrow workgroups (a 256-sequence batch over
+// a 4096-token prefix: 32-block chunks 0.2241-0.2249 ms per decode, 48-block
+// 0.2204-0.2208, 64-block 0.2181-0.2187, 128-block 0.2186-0.2201; before
+// the two launches overlapped, 32-block chunks were the fastest).
+constexpr int32_t kWideChunkBlocks = 64, kNarrowChunkBlocks = 64;
 constexpr int32_t kWideChunks = 8, kNarrowChunks = 4;
 
 struct Node {
