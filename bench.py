@@ -469,10 +469,8 @@ def bench_prefix_shared(args, cfg):
         lay = step.step(seqs, q, out, k, v, cfg.scale, events=ev[it] if it % every == 0 else None)
         loads.append(lay.plan.shared_kv)
         retire, parents = apply_churn(seqs, *draws[it])
-        for x in retire:
-            pool.free(x)
-        for x in parents:
-            pool.fork(x)
+        pool.free_batch(retire)
+        pool.fork_batch(parents)
         return len(seqs)
 
     loads = []  # the plan's load-policy hint of every iteration

@@ -156,6 +156,15 @@ pkv_status pkv_seq_fork_prefix(pkv_pool* pool, int32_t parent, int32_t n_tokens,
  * or already freed id (nothing changes). */
 pkv_status pkv_seq_free(pkv_pool* pool, int32_t seq);
 
+/* Batched retire / admit for a scheduler iteration (the same passages as
+ * pkv_seq_free and pkv_seq_fork): pkv_seq_free on seqs[0 .. n_seqs) in
+ * order, and pkv_seq_fork on parents[0 .. n) in order with the new ids in
+ * children[0 .. n) (host arrays).  All or nothing: an unknown id
+ * (PKV_E_BAD_SEQ) or an id given twice to the free (PKV_E_BAD_ARG) is found
+ * before anything changes.  A parent may appear more than once. */
+pkv_status pkv_seq_free_batch(pkv_pool* pool, const int32_t* seqs, int32_t n_seqs);
+pkv_status pkv_seq_fork_batch(pkv_pool* pool, const int32_t* parents, int32_t n, int32_t* children);
+
 pkv_status pkv_seq_length(const pkv_pool* pool, int32_t seq, int32_t* length);
 /* Copy the sequence's block table to table[0..cap); *n = its length. */
 pkv_status pkv_seq_table(const pkv_pool* pool, int32_t seq, int32_t* table, int32_t cap,

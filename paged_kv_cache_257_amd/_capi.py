@@ -145,6 +145,8 @@ SIGNATURES = {
     "pkv_sched_request": [P, I32, C.POINTER(RequestState)],
     "pkv_sched_stats": [P, C.POINTER(SchedStats)],
     "pkv_seq_free": [P, I32],
+    "pkv_seq_free_batch": [P, PI32, I32],
+    "pkv_seq_fork_batch": [P, PI32, I32, PI32],
     "pkv_seq_length": [P, I32, PI32],
     "pkv_seq_table": [P, I32, PI32, I32, PI32],
     "pkv_seq_slots": [P, I32, I32, I32, PI64],

@@ -332,6 +332,33 @@ pkv_status pkv_seq_free(pkv_pool* p, int32_t seq) {
   return PKV_OK;
 }
 
+pkv_status pkv_seq_free_batch(pkv_pool* p, const int32_t* seqs, int32_t n_seqs) {
+  if (pkv_status st = check_pool(p)) return st;
+  if (n_seqs < 0 || (n_seqs > 0 && !seqs)) return fail(PKV_E_BAD_ARG, "bad batch arguments");
+  // all or nothing: every id live and none twice, checked before any is freed
+  const uint64_t epoch = ++p->epoch;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    pkv_seq_state* s = find_seq(p, seqs[i]);
+    if (!s) return fail(PKV_E_BAD_SEQ, unknown(seqs[i]));
+    if (s->mark == epoch) return fail(PKV_E_BAD_ARG, "duplicate sequence in batch");
+    s->mark = epoch;
+  }
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (pkv_status st = pkv_seq_free(p, seqs[i])) return st;
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_fork_batch(pkv_pool* p, const int32_t* parents, int32_t n, int32_t* children) {
+  if (pkv_status st = check_pool(p)) return st;
+  if (n < 0 || (n > 0 && (!parents || !children))) return fail(PKV_E_BAD_ARG, "bad batch arguments");
+  // all or nothing: every parent live before any child is made
+  for (int32_t i = 0; i < n; ++i)
+    if (!find_seq(p, parents[i])) return fail(PKV_E_BAD_SEQ, unknown(parents[i]));
+  for (int32_t i = 0; i < n; ++i)
+    if (pkv_status st = pkv_seq_fork(p, parents[i], children + i)) return st;
+  return PKV_OK;
+}
+
 pkv_status pkv_seq_length(const pkv_pool* p, int32_t seq, int32_t* length) {
   if (pkv_status st = check_pool(p)) return st;
   if (!length) return fail(PKV_E_BAD_ARG, "null length");

@@ -97,6 +97,16 @@ class Pool:
     def free(self, seq: int) -> None:
         check(self.lib, self.lib.pkv_seq_free(self.handle, seq))
 
+    def free_batch(self, seqs: Sequence[int]) -> None:
+        arr = np.ascontiguousarray(seqs, dtype=np.int32)
+        check(self.lib, self.lib.pkv_seq_free_batch(self.handle, i32p(arr), len(arr)))
+
+    def fork_batch(self, parents: Sequence[int]) -> np.ndarray:
+        arr = np.ascontiguousarray(parents, dtype=np.int32)
+        kids = np.empty(len(arr), dtype=np.int32)
+        check(self.lib, self.lib.pkv_seq_fork_batch(self.handle, i32p(arr), len(arr), i32p(kids)))
+        return kids
+
     def length(self, seq: int) -> int:
         n = C.c_int32()
         check(self.lib, self.lib.pkv_seq_length(self.handle, seq, C.byref(n)))

@@ -176,9 +176,13 @@ def test_prefix_shared_schedule_matches_oracle():
         assert np.array_equal(l1, np.asarray(l2, dtype=np.int32)), it
         shared_seen = max(shared_seen, pool.stats()["shared_blocks"])
         retire, parents = choose_churn(cfg, it, seqs_c)
-        for s in retire:
-            pool.free(s)
-        kids = [pool.fork(p) for p in parents]
+        if it % 2:  # the batched retire / admit calls on odd iterations
+            pool.free_batch(retire)
+            kids = pool.fork_batch(parents).tolist()
+        else:
+            for s in retire:
+                pool.free(s)
+            kids = [pool.fork(p) for p in parents]
         _, _, kids_o = ora.churn_step(it)
         assert kids == kids_o
         assert pool.stats() == ora.alloc.stats()
@@ -348,3 +352,38 @@ def test_seq_slots_read_back_each_sequences_dense_history():
     with pytest.raises(PkvError) as e:
         pool.slots(10_000, 0, 0)
     assert e.value.kind == "bad_seq"
+
+
+def test_batched_free_and_fork_are_all_or_nothing():
+    """pkv_seq_free_batch / pkv_seq_fork_batch: an unknown id, or an id
+    freed twice in one call, is refused before anything changes; otherwise
+    they equal the single calls in order (the oracle's free / fork)."""
+    order = np.arange(64, dtype=np.int32)[::-1].copy()
+    pool = host_pool(64, 4, 16, order)
+    ora = OracleAllocator(64, 4, 16, order.tolist())
+    try:
+        ids = [pool.alloc(n)[0] for n in (5, 9, 3, 12)]
+        ids_o = [ora.alloc(n)[0] for n in (5, 9, 3, 12)]
+        assert ids == ids_o
+        before = (pool.live(), pool.free_list(), pool.refcounts(), pool.stats())
+        for bad, kind in (([ids[0], 999], "bad_seq"), ([ids[1], ids[1]], "bad_arg")):
+            with pytest.raises(PkvError) as e:
+                pool.free_batch(bad)
+            assert e.value.kind == kind
+        with pytest.raises(PkvError) as e:
+            pool.fork_batch([ids[2], 999])
+        assert e.value.kind == "bad_seq"
+        assert (pool.live(), pool.free_list(), pool.refcounts(), pool.stats()) == before
+        kids = pool.fork_batch([ids[1], ids[1], ids[3]]).tolist()
+        kids_o = [ora.fork(p) for p in (ids[1], ids[1], ids[3])]
+        assert kids == kids_o
+        pool.free_batch([ids[1], kids[0], ids[0]])
+        for x in (ids[1], kids[0], ids[0]):
+            ora.free_seq(x)
+        assert pool.free_list() == ora.free_handout_order()
+        assert pool.refcounts() == [int(x) for x in ora.rc]
+        assert pool.stats() == ora.stats()
+        assert pool.fork_batch([]).tolist() == []
+        pool.free_batch([])
+    finally:
+        pool.close()
