@@ -573,7 +573,11 @@ int32_t pkv_decode_fill_partition(const int32_t* context_lens, int32_t num_seqs,
  * than 512 workgroups, with a limit that brings it to about 512 (at least
  * 1024 keys per part).  Each part is a work item, and the parts' partial softmax states are merged in the same
  * launch (workspace: pkv_prefill_workspace_bytes).  The kernel runs every
- * item for every KV head.  Items are ordered by decreasing number of keys.
+ * item for every KV head.  Items are ordered by decreasing number of keys,
+ * except that a launch of at most 512 workgroups (items x KV heads x head
+ * groups: two per CU of MI355X, one round) takes its second half in
+ * increasing order, so that workgroups j and j + 256, which the dispatcher
+ * puts on one CU, hold a long and a short item.
  *
  * plan (host int32, cap >= pkv_prefill_plan_ints(...)) receives
  *   [0, 6*n_work)                      items (sequence, tile, first stage,

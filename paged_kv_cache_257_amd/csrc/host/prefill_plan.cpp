@@ -6,7 +6,8 @@
 // consecutive query tokens; a tile's cost is the number of keys its last
 // token attends, so items are sorted by that, largest first, and the
 // in-order workgroup dispatcher fills the tail of the launch with the
-// cheap ones.
+// cheap ones (a launch that runs in one round instead pairs long and short
+// items on each CU).
 #include <algorithm>
 #include <cstdlib>
 #include <numeric>
@@ -42,6 +43,9 @@ constexpr int32_t kStageTokens = 32;  // keys per kernel stage
 // (fewer than this many workgroups), into about this many.
 // PKV_PREFILL_SPLIT_WGS overrides it for tuning sweeps (read per plan).
 constexpr int64_t kAutoSplitWorkgroups = 512;
+// Two workgroups on each of MI355X's 256 CUs: a launch of at most this many
+// runs in one round.
+constexpr int64_t kOneRoundWorkgroups = 512;
 int64_t auto_split_workgroups() {
   const char* s = std::getenv("PKV_PREFILL_SPLIT_WGS");
   const long v = s ? std::atol(s) : 0;
@@ -189,6 +193,14 @@ pkv_status pkv_prefill_plan(const int32_t* q_lens, const int32_t* context_lens, 
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(),
                    [](int32_t a, int32_t b) { return items[a].keys > items[b].keys; });
+  // A launch of at most two workgroups per CU runs in one round: the
+  // dispatcher gives each CU workgroup j and j + 256 (the XCDs take
+  // workgroups in turn and fill their CUs breadth first), so the second
+  // half of the items goes in ascending order and every CU holds a long and
+  // a short tile of about the same total (the causal tiles of one chunk
+  // differ in length by the chunk).
+  if (int64_t(order.size()) * workgroups_per_tile(num_q_heads, num_kv_heads, tile) <= kOneRoundWorkgroups)
+    std::reverse(order.begin() + order.size() / 2, order.end());
   for (size_t w = 0; w < order.size(); ++w) {
     const Item& it = items[order[w]];
     int32_t* e = plan + 6 * w;

@@ -3,7 +3,8 @@
 Every (sequence, tile) appears; a tile's stages (32 keys each, up to the
 keys its last query attends) are covered exactly once by its parts; a split
 tile's parts are balanced and at most max_keys keys each; items are sorted
-by the keys they attend, largest first; q_start are the prefix sums of the
+by the keys they attend, largest first (a launch of at most 512 workgroups:
+the second half in increasing order); q_start are the prefix sums of the
 chunk lengths; the split table points at disjoint, consecutive partials.
 """
 
@@ -60,7 +61,13 @@ def check(q_lens, ctx, Hq, Hkv, max_keys=0):
     assert info.n_partials == pos
     cost = [min(s1 * 32, int(ctx[seq]) - int(q_lens[seq]) + min((t + 1) * tile, int(q_lens[seq])))
             if sp < 0 else (s1 - s0) * 32 for seq, t, s0, s1, sp, _ in items.tolist()]
-    assert cost == sorted(cost, reverse=True)
+    wgs = nw * Hkv * (Hq // Hkv // gw)
+    if wgs <= 512:  # one round: the second half ascending, paired with the first on the CUs
+        h = nw // 2
+        assert cost[:h] == sorted(cost[:h], reverse=True) and cost[h:] == sorted(cost[h:])
+        assert sorted(cost, reverse=True) == cost[:h] + cost[h:][::-1]
+    else:
+        assert cost == sorted(cost, reverse=True)
     assert info.total_q == int(np.sum(q_lens)) and info.max_context_len == int(max(ctx))
     assert info.plan_ints == len(plan)
     return info
