@@ -1691,18 +1691,32 @@ SideStream side_tab[kSideDevices];
 // captured into a graph (nothing is created during a capture).
 pkv_status side_stream(hipStream_t s, SideStream** out) {  // caller holds side_mu
   *out = nullptr;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices)
-    return fail(PKV_E_HIP, "no current HIP device for the shared-block side stream");
+  // the device of the caller's stream (the current one for the null stream)
+  int cur = -1, dev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return launch_status("current device query");
+  if (s == nullptr) dev = cur;
+  else if (hipStreamGetDevice(s, &dev) != hipSuccess) return launch_status("stream device query");
+  if (dev < 0 || dev >= kSideDevices) return fail(PKV_E_HIP, "device out of range for the shared-block side stream");
   SideStream& ss = side_tab[dev];
   if (!ss.stream) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) return launch_status("stream capture query");
     if (cs != hipStreamCaptureStatusNone) return PKV_OK;
-    if (hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
-      return launch_status("shared-block side stream creation");
+    // created on the stream's device, the current device restored after
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return launch_status("side stream device");
+    SideStream n;
+    const bool ok = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking) == hipSuccess &&
+                    hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) == hipSuccess &&
+                    hipEventCreateWithFlags(&n.join, hipEventDisableTiming) == hipSuccess;
+    if (!ok) {  // nothing half made is kept
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.stream) (void)hipStreamDestroy(n.stream);
+    } else {
+      ss = n;
+    }
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return launch_status("current device restore");
+    if (!ok) return launch_status("shared-block side stream creation");
   }
   *out = &ss;
   return PKV_OK;
