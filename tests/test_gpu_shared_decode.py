@@ -176,3 +176,42 @@ def test_shared_decode_dominant_keys_outside_first_lane_group(dtype, kv_heads, g
     finally:
         case.close()
 
+
+
+def test_shared_decode_replays_in_a_captured_graph():
+    """The shared-block decode with its narrow launch on the library's side
+    stream (forked from and joined back into the caller's stream by events),
+    captured in a HIP graph after an eager call: each replay, with eager
+    decodes between them, equals the eager output bit for bit."""
+    case = ForkedCase(77, "f16", 4, 1, nan_fill=False)
+    try:
+        plan, info = decode_plan_shared(case.pool, case.seqs, case.Hq, 2048, 0)
+        assert info.n_nodes > info.n_wide_nodes > 0  # wide and narrow launches both run
+        q = to_device(case.q, "f16")
+        args = (torch.from_numpy(case.tables).cuda(), torch.from_numpy(case.lens).cuda(), 1 / np.sqrt(128),
+                torch.from_numpy(plan).cuda(), info)
+        ws = decode_workspace_bytes(info, case.Hq, 128)
+        workspace = torch.zeros(max(ws // 4, 1), dtype=torch.float32, device="cuda")
+        shape = (len(case.seqs), case.Hq, 128)
+        eager = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+        case.pool.paged_decode(q, eager, *args, workspace)  # creates the side stream
+        sync()
+        ref = eager.clone()
+        err = float(np.max(np.abs(ref.cpu().numpy() - np.stack(oracle_map(case.oracle_out, range(len(case.seqs)))))))
+        assert err <= TOL["f16"], err
+        out = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            case.pool.paged_decode(q, out, *args, workspace)
+        for rep in range(3):
+            out.fill_(float("nan"))
+            g.replay()
+            sync()
+            assert torch.equal(out, ref), rep
+            eager.fill_(float("nan"))
+            case.pool.paged_decode(q, eager, *args, workspace)
+            sync()
+            assert torch.equal(eager, ref), rep
+        print(f"\n[gpu] shared decode in a graph: 3 replays equal the eager call (oracle err {err:.2e})", flush=True)
+    finally:
+        case.close()
