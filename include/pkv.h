@@ -860,8 +860,11 @@ pkv_status pkv_paged_decode_noalloc(const pkv_pool* pool, const void* q, const v
  * unless the first pass met a V value of magnitude 2^16 or more.  The first
  * pass records that in one word per device inside the library, raised to
  * the call's number (numbers only grow), so concurrent calls can cause an
- * exact pass that was not needed but never skip one that was.  Setting the
- * environment variable PKV_PREFILL_BF16_EXACT=1 runs the exact pass alone.
+ * exact pass that was not needed but never skip one that was.  A captured
+ * graph keeps the number the call had at capture: once one replay meets such
+ * a value, every later replay of that graph also runs the exact pass (its
+ * results stay exact).  Setting the environment variable
+ * PKV_PREFILL_BF16_EXACT=1 runs the exact pass alone.
  * Asynchronous on `stream`; allocates nothing. */
 pkv_status pkv_paged_prefill(const pkv_pool* pool, const void* q, float* out, int32_t num_seqs,
                              int32_t num_q_heads, const int32_t* block_tables, int32_t table_stride,
