@@ -1535,16 +1535,20 @@ DecodeFn pick_mfma(int dt, int gw, int& nw, bool reuse) {
 // Waves per workgroup (they split a work item's blocks): 4 for items of 16
 // blocks or more on average (the best of {1, 2, 4, 8} on the GPT-style fp16
 // batch, ~28 blocks per item), 2 from 6 blocks and 1 below: a short item
-// leaves most of four waves idle, and the own parts that follow a
-// shared-block launch are a few blocks each (a prefix-shared batch of 256:
-// 0.2457 ms per decode with 4 waves, 0.2298 with 2, 0.2245 with 1).
+// leaves most of four waves idle.  The own parts that follow shared-block
+// launches take one wave whatever their length: each also merges its
+// sequence's shared records, and more, smaller workgroups finish sooner (a
+// prefix-shared batch of 256 over its 56 timed iterations, own parts of 3 to
+// ~17 blocks on average: 0.2134-0.2140 ms per decode with one wave against
+// 0.2160-0.2175 with the length rule).
 // PKV_DECODE_WAVES overrides the choice for tuning sweeps.  The tuning
 // variables are read at every launch (a lookup in the environment, next to
 // a launch of tens of microseconds), so one process can run every variant.
-int waves_per_item(int item_blocks) {
+int waves_per_item(int item_blocks, bool after_shared = false) {
   const char* s = std::getenv("PKV_DECODE_WAVES");
   const int v = s ? std::atoi(s) : 0;
   if (v == 1 || v == 2 || v == 4 || v == 8) return v;
+  if (after_shared) return 1;
   return item_blocks >= 16 ? 4 : item_blocks >= 6 ? 2 : 1;
 }
 
@@ -1819,7 +1823,7 @@ pkv_status launch_partitions(const pkv_pool* pool, const DecodeParams& prm, int 
     if (pkv_status st = launch_shared(pool, prm, prm.work, info, s, ev_start, concurrent)) return st;
     ev_start = nullptr;
   }
-  int nw = waves_per_item(info->item_blocks);  // becomes the chosen instance's waves
+  int nw = waves_per_item(info->item_blocks, info->n_nodes > 0);  // becomes the chosen instance's waves
   const bool reuse = info->shared_kv != 0;
   DecodeFn fn = mfma ? pick_mfma(pool->desc.dtype, gw, nw, reuse)
                      : pick_decode(pool->desc.dtype, pool->desc.head_dim, gw, nw, reuse);
